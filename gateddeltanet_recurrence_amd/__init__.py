@@ -1,0 +1,16 @@
+"""MI355X (gfx950) GatedDeltaNet operator: Python binding of libgdn.so.
+
+The binding only marshals arguments: it checks that tensors are contiguous,
+on the GPU and shaped consistently with each other, fills the C structs of
+include/gdn.h and calls the library. Every step of the operator runs in the
+HIP kernels of libgdn.so; there is no Python or CPU fallback, and a missing
+library raises an error.
+"""
+from .binding import (  # noqa: F401
+    GDNError, LibraryNotBuilt, PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK,
+    GDN_F32, GDN_F16, GDN_BF16, RULE_GATED_DELTA,
+    GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIAS, GDN_ERR_CAPACITY,
+    GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP, GdnParams, GdnTensors,
+    lib, library_path, gdn_abi_version, gdn_strerror, gdn_forward, gdn_forward_workspace_bytes,
+    gdn_resolve_plan, gdn_replay, capsule_width, make_params,
+)

@@ -1,0 +1,259 @@
+"""ctypes binding of the C ABI in include/gdn.h (same entry-point names).
+
+Tensors are torch tensors on the current HIP device; torch only provides the
+device memory and the stream. Shapes are read from the tensors, checked for
+consistency (the C ABI sees bare pointers and cannot), and passed as sizes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgdn.so"
+
+GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIAS = 0, 1, 2, 3, 4
+GDN_ERR_CAPACITY, GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP = 5, 6, 7, 8, 9
+GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
+PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
+RULE_GATED_DELTA = 0
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({gdn_strerror(status)})")
+
+
+class GdnParams(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("num_reqs", ctypes.c_int32),
+        ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+        ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("chunk", ctypes.c_int32),
+        ("state_update_capacity", ctypes.c_int32), ("plan", ctypes.c_int32),
+        ("update_rule", ctypes.c_int32),
+    ]
+
+
+class GdnTensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens", "cu_seqlens_host",
+        "initial_state", "final_state", "output", "state_update", "capture_count")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(PKG, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so; raises LibraryNotBuilt when it has not been built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise LibraryNotBuilt(f"{path} is missing: build it with "
+                                  "`python -m gateddeltanet_recurrence_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.gdn_forward.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), vp,
+                                  ctypes.c_size_t, vp]
+        L.gdn_forward.restype = ctypes.c_int
+        L.gdn_forward_workspace_bytes.argtypes = [ctypes.POINTER(GdnParams), vp,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_forward_workspace_bytes.restype = ctypes.c_int
+        L.gdn_resolve_plan.argtypes = [ctypes.POINTER(GdnParams), vp, ctypes.POINTER(i32)]
+        L.gdn_resolve_plan.restype = ctypes.c_int
+        L.gdn_replay.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.gdn_replay.restype = ctypes.c_int
+        L.gdn_strerror.argtypes = [ctypes.c_int]
+        L.gdn_strerror.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def gdn_abi_version() -> int:
+    return int(lib().gdn_abi_version())
+
+
+def gdn_strerror(status: int) -> str:
+    return lib().gdn_strerror(int(status)).decode()
+
+
+def capsule_width(Hk: int, Hv: int, Dk: int, Dv: int) -> int:
+    """Floats per capsule row: Hv decays, Hk*Dk unit keys, Hv*Dv deltas."""
+    return Hv + Hk * Dk + Hv * Dv
+
+
+def make_params(N, R, Hk, Hv, Dk, Dv, io_dtype, *, scale=0.0, chunk=0, capacity=0,
+                plan=PLAN_AUTO, update_rule=RULE_GATED_DELTA) -> GdnParams:
+    return GdnParams(int(N), int(R), int(Hk), int(Hv), int(Dk), int(Dv), int(io_dtype),
+                     float(scale), int(chunk), int(capacity), int(plan), int(update_rule))
+
+
+# ------------------------------------------------------------------ helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return GDN_F32
+    if dtype == torch.float16:
+        return GDN_F16
+    if dtype == torch.bfloat16:
+        return GDN_BF16                      # passed through so the library rejects it
+    raise ValueError(f"unsupported io dtype {dtype}")
+
+
+def _ptr(x) -> Optional[int]:
+    return None if x is None else int(x.data_ptr())
+
+
+def _need(x, name, shape, dtype=None):
+    if x is None:
+        return
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(x.shape)} != expected {tuple(shape)}")
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError(f"{name}: dtype {x.dtype} != expected {dtype}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        return int(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _host_i32(arr):
+    """Keep-alive int32 host buffer and its address, from a sequence / numpy / CPU tensor."""
+    import numpy as np
+    if arr is None:
+        return None, None
+    if hasattr(arr, "numpy") and hasattr(arr, "is_cuda"):
+        if arr.is_cuda:
+            raise ValueError("host mirrors must be CPU data")
+        arr = arr.numpy()
+    a = np.ascontiguousarray(np.asarray(arr, dtype=np.int32))
+    return a, a.ctypes.data
+
+
+# ------------------------------------------------------------- entry points
+def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state=None,
+                final_state=None, state_update=None, capture_count=None, cu_seqlens_host=None,
+                scale: float = 0.0, chunk: int = 0, state_update_capacity: int = 0,
+                plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA, workspace=None,
+                stream=None, check: bool = True) -> int:
+    """gdn_forward of include/gdn.h on torch tensors; returns the status code.
+
+    q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32; a, b
+    [N, Hv] float32; A_log, dt_bias [Hv] float32; cu_seqlens [R+1] int32;
+    states [R, Hv, Dv, Dk] float32; state_update [R, capacity, W] float32;
+    capture_count [R] int32; workspace a uint8 GPU tensor (CHUNK plan).
+    """
+    torch = _torch()
+    N, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    R = cu_seqlens.shape[0] - 1
+    io = q.dtype
+    _need(q, "q", (N, Hk, Dk))
+    _need(k, "k", (N, Hk, Dk), io)
+    _need(v, "v", (N, Hv, Dv), io)
+    _need(output, "output", (N, Hv, Dv), io)
+    _need(a, "a", (N, Hv), torch.float32)
+    _need(b, "b", (N, Hv), torch.float32)
+    _need(A_log, "A_log", (Hv,), torch.float32)
+    _need(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _need(cu_seqlens, "cu_seqlens", (R + 1,), torch.int32)
+    _need(initial_state, "initial_state", (R, Hv, Dv, Dk), torch.float32)
+    _need(final_state, "final_state", (R, Hv, Dv, Dk), torch.float32)
+    if state_update is not None:
+        _need(state_update, "state_update",
+              (R, state_update_capacity, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
+    _need(capture_count, "capture_count", (R,), torch.int32)
+    host_cu, host_cu_ptr = _host_i32(cu_seqlens_host)
+    if host_cu is not None and host_cu.shape != (R + 1,):
+        raise ValueError("cu_seqlens_host must have R + 1 entries")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = int(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    params = make_params(N, R, Hk, Hv, Dk, Dv, _io_code(io), scale=scale, chunk=chunk,
+                         capacity=state_update_capacity, plan=plan, update_rule=update_rule)
+    tens = GdnTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                      _ptr(cu_seqlens), host_cu_ptr, _ptr(initial_state), _ptr(final_state),
+                      _ptr(output), _ptr(state_update), _ptr(capture_count))
+    st = lib().gdn_forward(ctypes.byref(params), ctypes.byref(tens), ws_ptr,
+                           ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    del host_cu
+    if check and st != GDN_OK:
+        raise GDNError(st, "gdn_forward")
+    return st
+
+
+def gdn_forward_workspace_bytes(N, R, Hk, Hv, Dk, Dv, io_dtype=GDN_F16, *, capacity=0,
+                                plan=PLAN_AUTO, cu_seqlens_host=None, chunk=0) -> int:
+    """Workspace bytes gdn_forward needs (0 for the recurrent plan)."""
+    params = make_params(N, R, Hk, Hv, Dk, Dv, io_dtype, chunk=chunk, capacity=capacity, plan=plan)
+    host_cu, host_ptr = _host_i32(cu_seqlens_host)
+    out = ctypes.c_size_t(0)
+    st = lib().gdn_forward_workspace_bytes(ctypes.byref(params), host_ptr, ctypes.byref(out))
+    del host_cu
+    if st != GDN_OK:
+        raise GDNError(st, "gdn_forward_workspace_bytes")
+    return int(out.value)
+
+
+def gdn_resolve_plan(N, R, Hk, Hv, Dk, Dv, io_dtype=GDN_F16, *, capacity=0, plan=PLAN_AUTO,
+                     cu_seqlens_host=None) -> int:
+    params = make_params(N, R, Hk, Hv, Dk, Dv, io_dtype, capacity=capacity, plan=plan)
+    host_cu, host_ptr = _host_i32(cu_seqlens_host)
+    out = ctypes.c_int32(0)
+    st = lib().gdn_resolve_plan(ctypes.byref(params), host_ptr, ctypes.byref(out))
+    del host_cu
+    if st != GDN_OK:
+        raise GDNError(st, "gdn_resolve_plan")
+    return int(out.value)
+
+
+def gdn_replay(src_state, state_update, accepted, dst_state, *, num_k_heads: int,
+               state_update_capacity: int, accepted_host=None, stream=None,
+               check: bool = True) -> int:
+    """gdn_replay of include/gdn.h: dst = src advanced by the accepted capsule prefix."""
+    torch = _torch()
+    R, Hv, Dv, Dk = src_state.shape
+    Hk = int(num_k_heads)
+    cap = int(state_update_capacity)
+    _need(src_state, "src_state", (R, Hv, Dv, Dk), torch.float32)
+    _need(dst_state, "dst_state", (R, Hv, Dv, Dk), torch.float32)
+    _need(accepted, "accepted", (R,), torch.int32)
+    if cap > 0:
+        _need(state_update, "state_update", (R, cap, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
+    host_acc, host_ptr = _host_i32(accepted_host)
+    if host_acc is not None and host_acc.shape != (R,):
+        raise ValueError("accepted_host must have R entries")
+    st = lib().gdn_replay(R, Hk, Hv, Dk, Dv, cap, _ptr(src_state), _ptr(state_update),
+                          _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
+    del host_acc
+    if check and st != GDN_OK:
+        raise GDNError(st, "gdn_replay")
+    return st

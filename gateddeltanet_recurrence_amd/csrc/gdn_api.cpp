@@ -1,0 +1,270 @@
+// C ABI of libgdn.so: argument validation, plan resolution and dispatch.
+//
+// Every check runs on the host before any launch, so an error status other
+// than GDN_ERR_HIP leaves device memory untouched (validation and preparation
+// before the publication boundary: "Replay compact fixed state for hybrid
+// decoding", Key Changes). The library allocates nothing and keeps no state.
+#include "../../include/gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "gdn_kernels.h"
+
+namespace {
+
+constexpr int kRecurrentMaxLenForAuto = 32;
+constexpr bool kChunkPathBuilt = false;
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t io_bytes(int dtype) { return dtype == GDN_F16 ? 2 : 4; }
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+  Span() = default;
+  Span(const void* p, size_t bytes) : lo(reinterpret_cast<uintptr_t>(p)), hi(lo + (p ? bytes : 0)) {}
+  bool empty() const { return lo == hi; }
+  bool overlaps(const Span& o) const { return !empty() && !o.empty() && lo < o.hi && o.lo < hi; }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every forward entry point; fills the resolved values.
+struct Resolved {
+  int64_t N, R, Hk, Hv, Dk, Dv;
+  int cap;
+  float scale;
+  int plan;
+  int64_t chunk_slots;  // chunk slots the CHUNK workspace holds
+};
+
+int check_params(const gdn_params* p, Resolved* out) {
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (p->update_rule != GDN_RULE_GATED_DELTA) return GDN_ERR_RULE;
+  if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_F16) return GDN_ERR_DTYPE;
+  if (p->num_tokens < 0 || p->num_reqs < 0 || p->num_k_heads <= 0 || p->num_v_heads <= 0)
+    return GDN_ERR_SHAPE;
+  if (p->num_v_heads % p->num_k_heads != 0) return GDN_ERR_SHAPE;
+  if (!supported_dim(p->head_k_dim) || !supported_dim(p->head_v_dim)) return GDN_ERR_SHAPE;
+  if (std::isnan(p->scale) || std::isinf(p->scale)) return GDN_ERR_SHAPE;
+  if (p->state_update_capacity < 0) return GDN_ERR_CAPACITY;
+  if (p->chunk != 0 && p->chunk != gdn::kChunk) return GDN_ERR_SHAPE;
+  if (p->plan != GDN_PLAN_AUTO && p->plan != GDN_PLAN_RECURRENT && p->plan != GDN_PLAN_CHUNK)
+    return GDN_ERR_PLAN;
+  out->N = p->num_tokens;
+  out->R = p->num_reqs;
+  out->Hk = p->num_k_heads;
+  out->Hv = p->num_v_heads;
+  out->Dk = p->head_k_dim;
+  out->Dv = p->head_v_dim;
+  out->cap = p->state_update_capacity;
+  out->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt(static_cast<float>(p->head_k_dim));
+  // capsule rows of one request must be addressable with 32-bit row offsets in-kernel
+  const int64_t W = out->Hv + out->Hk * out->Dk + out->Hv * out->Dv;
+  if (W > std::numeric_limits<int32_t>::max()) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+int check_cu_host(const int32_t* cu, int64_t R, int64_t N, int64_t* max_len, int64_t* slots) {
+  if (cu[0] != 0) return GDN_ERR_SHAPE;
+  int64_t mx = 0, nch = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t len = static_cast<int64_t>(cu[r + 1]) - cu[r];
+    if (len < 0) return GDN_ERR_SHAPE;
+    if (len > mx) mx = len;
+    nch += (len + gdn::kChunk - 1) / gdn::kChunk;
+  }
+  if (cu[R] != N) return GDN_ERR_SHAPE;
+  *max_len = mx;
+  *slots = nch;
+  return GDN_OK;
+}
+
+// Resolves the plan and the chunk-slot count. `capsule` says a capsule is written.
+int resolve_plan(const gdn_params* p, const int32_t* cu_host, bool capsule, Resolved* rv) {
+  int64_t max_len = 0, slots = 0;
+  if (cu_host != nullptr) {
+    int st = check_cu_host(cu_host, rv->R, rv->N, &max_len, &slots);
+    if (st != GDN_OK) return st;
+  } else {
+    // upper bound valid for any split of N tokens into R requests
+    max_len = rv->R > 0 ? (rv->N + rv->R - 1) / rv->R : 0;  // mean, for planning only
+    slots = rv->R > 0 ? (rv->N + rv->R * (gdn::kChunk - 1)) / gdn::kChunk : 0;
+  }
+  const bool chunk_shape = kChunkPathBuilt && rv->Dk == 128 && rv->Dv == 128;
+  int plan = p->plan;
+  if (plan == GDN_PLAN_CHUNK) {
+    if (capsule || !chunk_shape) return GDN_ERR_PLAN;
+  } else if (plan == GDN_PLAN_AUTO) {
+    plan = (capsule || !chunk_shape || max_len <= kRecurrentMaxLenForAuto) ? GDN_PLAN_RECURRENT
+                                                                            : GDN_PLAN_CHUNK;
+  }
+  rv->plan = plan;
+  rv->chunk_slots = slots;
+  return GDN_OK;
+}
+
+size_t workspace_for(const Resolved& rv) {
+  if (rv.plan != GDN_PLAN_CHUNK) return 0;
+  return gdn::chunk_workspace_bytes(rv.chunk_slots, (int)rv.R, (int)rv.Hk, (int)rv.Hv);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_strerror(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "unsupported size, malformed cu_seqlens or misaligned pointer";
+    case GDN_ERR_DTYPE: return "io dtype must be FP16 or FP32 (BF16 is not supported)";
+    case GDN_ERR_ALIAS: return "buffers overlap in a way the call does not allow";
+    case GDN_ERR_CAPACITY: return "capacity is negative or an accepted/captured count exceeds it";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_PLAN: return "the forced plan cannot run these arguments";
+    case GDN_ERR_RULE: return "only the gated delta update rule is implemented";
+    case GDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int gdn_resolve_plan(const gdn_params* p, const int32_t* cu_host, int32_t* plan) {
+  Resolved rv;
+  int st = check_params(p, &rv);
+  if (st != GDN_OK) return st;
+  if (plan == nullptr) return GDN_ERR_NULL;
+  st = resolve_plan(p, cu_host, rv.cap > 0, &rv);
+  if (st != GDN_OK) return st;
+  *plan = rv.plan;
+  return GDN_OK;
+}
+
+int gdn_forward_workspace_bytes(const gdn_params* p, const int32_t* cu_host, size_t* bytes) {
+  Resolved rv;
+  int st = check_params(p, &rv);
+  if (st != GDN_OK) return st;
+  if (bytes == nullptr) return GDN_ERR_NULL;
+  st = resolve_plan(p, cu_host, rv.cap > 0, &rv);
+  if (st != GDN_OK) return st;
+  *bytes = workspace_for(rv);
+  return GDN_OK;
+}
+
+int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Resolved rv;
+  int st = check_params(p, &rv);
+  if (st != GDN_OK) return st;
+  if (t == nullptr) return GDN_ERR_NULL;
+  const bool capsule = t->state_update != nullptr;
+  if (capsule && rv.cap == 0) return GDN_ERR_CAPACITY;   // a capsule needs rows
+  if (rv.R == 0) return rv.N == 0 ? GDN_OK : GDN_ERR_SHAPE;
+
+  // required pointers
+  if (t->cu_seqlens == nullptr || t->A_log == nullptr || t->dt_bias == nullptr) return GDN_ERR_NULL;
+  if (rv.N > 0 && (t->q == nullptr || t->k == nullptr || t->v == nullptr || t->a == nullptr ||
+                   t->b == nullptr || t->output == nullptr))
+    return GDN_ERR_NULL;
+
+  // alignment of vector-accessed buffers
+  const void* vec_ptrs[] = {t->q, t->k, t->initial_state, t->final_state};
+  for (const void* ptr : vec_ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDN_ERR_SHAPE;
+
+  st = resolve_plan(p, t->cu_seqlens_host, capsule, &rv);
+  if (st != GDN_OK) return st;
+
+  // overlap rules
+  const size_t io = io_bytes(p->io_dtype);
+  const size_t N = (size_t)rv.N, R = (size_t)rv.R, Hk = (size_t)rv.Hk, Hv = (size_t)rv.Hv;
+  const size_t Dk = (size_t)rv.Dk, Dv = (size_t)rv.Dv;
+  const size_t W = Hv + Hk * Dk + Hv * Dv;
+  const size_t state_bytes = R * Hv * Dv * Dk * 4;
+  const Span inputs[] = {
+      Span(t->q, N * Hk * Dk * io), Span(t->k, N * Hk * Dk * io), Span(t->v, N * Hv * Dv * io),
+      Span(t->a, N * Hv * 4),       Span(t->b, N * Hv * 4),       Span(t->A_log, Hv * 4),
+      Span(t->dt_bias, Hv * 4),     Span(t->cu_seqlens, (R + 1) * 4),
+      Span(t->capture_count, capsule ? R * 4 : 0)};
+  const Span init(t->initial_state, state_bytes);
+  const Span fin(t->final_state, state_bytes);
+  const Span out(t->output, N * Hv * Dv * io);
+  const Span cap(t->state_update, capsule ? R * (size_t)rv.cap * W * 4 : 0);
+  const size_t need_ws = workspace_for(rv);
+  const Span ws(workspace, need_ws);
+  const Span outputs[] = {out, fin, cap, ws};
+  for (const Span& o : outputs) {
+    for (const Span& i : inputs)
+      if (o.overlaps(i)) return GDN_ERR_ALIAS;
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (outputs[i].overlaps(outputs[j])) return GDN_ERR_ALIAS;
+  if (out.overlaps(init) || cap.overlaps(init) || ws.overlaps(init)) return GDN_ERR_ALIAS;
+  // final_state may be the very same buffer as initial_state (in-place update)
+  if (fin.overlaps(init) && t->final_state != t->initial_state) return GDN_ERR_ALIAS;
+
+  if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
+  if (need_ws > 0 && !aligned16(workspace)) return GDN_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (rv.plan == GDN_PLAN_RECURRENT) {
+    gdn::RecurrentArgs a{};
+    a.q = t->q; a.k = t->k; a.v = t->v; a.a = t->a; a.b = t->b;
+    a.A_log = t->A_log; a.dt_bias = t->dt_bias; a.cu_seqlens = t->cu_seqlens;
+    a.initial_state = t->initial_state; a.final_state = t->final_state; a.output = t->output;
+    a.state_update = t->state_update; a.capture_count = t->capture_count;
+    a.N = (int32_t)rv.N; a.R = (int32_t)rv.R; a.Hk = (int32_t)rv.Hk; a.Hv = (int32_t)rv.Hv;
+    a.Dk = (int32_t)rv.Dk; a.Dv = (int32_t)rv.Dv; a.group = (int32_t)(rv.Hv / rv.Hk);
+    a.capacity = rv.cap; a.capsule_width = (int32_t)W; a.scale = rv.scale;
+    err = gdn::launch_recurrent(a, p->io_dtype, s);
+  } else {
+    gdn::ChunkArgs a{};
+    a.q = t->q; a.k = t->k; a.v = t->v; a.a = t->a; a.b = t->b;
+    a.A_log = t->A_log; a.dt_bias = t->dt_bias; a.cu_seqlens = t->cu_seqlens;
+    a.initial_state = t->initial_state; a.final_state = t->final_state; a.output = t->output;
+    a.workspace = workspace;
+    a.N = (int32_t)rv.N; a.R = (int32_t)rv.R; a.Hk = (int32_t)rv.Hk; a.Hv = (int32_t)rv.Hv;
+    a.group = (int32_t)(rv.Hv / rv.Hk); a.max_chunks = (int32_t)rv.chunk_slots; a.scale = rv.scale;
+    err = gdn::launch_chunk(a, p->io_dtype, s);
+  }
+  return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
+               const float* src, const float* capsule, const int32_t* accepted,
+               const int32_t* accepted_host, float* dst, void* stream) {
+  if (R < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return GDN_ERR_SHAPE;
+  if (!supported_dim(Dk) || !supported_dim(Dv)) return GDN_ERR_SHAPE;
+  if (capacity < 0) return GDN_ERR_CAPACITY;
+  if (R == 0) return GDN_OK;
+  if (src == nullptr || dst == nullptr || accepted == nullptr) return GDN_ERR_NULL;
+  if (capacity > 0 && capsule == nullptr) return GDN_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return GDN_ERR_SHAPE;
+  const int64_t W64 = (int64_t)Hv + (int64_t)Hk * Dk + (int64_t)Hv * Dv;
+  if (W64 > std::numeric_limits<int32_t>::max()) return GDN_ERR_SHAPE;
+  if (accepted_host != nullptr) {
+    for (int32_t r = 0; r < R; ++r)
+      if (accepted_host[r] < 0 || accepted_host[r] > capacity) return GDN_ERR_CAPACITY;
+  }
+  const size_t state_bytes = (size_t)R * Hv * Dv * Dk * 4;
+  const Span d(dst, state_bytes);
+  if (d.overlaps(Span(src, state_bytes)) || d.overlaps(Span(capsule, (size_t)R * capacity * W64 * 4)) ||
+      d.overlaps(Span(accepted, (size_t)R * 4)))
+    return GDN_ERR_ALIAS;
+  gdn::ReplayArgs a{};
+  a.src = src; a.capsule = capsule; a.accepted = accepted; a.dst = dst;
+  a.R = R; a.Hk = Hk; a.Hv = Hv; a.Dk = Dk; a.Dv = Dv; a.group = Hv / Hk;
+  a.capacity = capacity; a.capsule_width = (int32_t)W64;
+  hipError_t err = gdn::launch_replay(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

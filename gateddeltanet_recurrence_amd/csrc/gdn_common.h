@@ -1,0 +1,71 @@
+// Device helpers shared by the GatedDeltaNet HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kNormEps = 1e-6f;
+
+// DPP lane permutations within a row of 16 lanes (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i <- lane 7-i of its 8
+constexpr int kDppRowMirror = 0x140;    // row_mirror: lane i <- lane 15-i of its 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of LANES (4 or 8) adjacent lanes; every lane of
+// the group gets the total. All 64 lanes must be active.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group of 4, 8 or 16 lanes");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  if constexpr (LANES >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (LANES >= 16) x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+// io element access: 4 consecutive elements widened to float, one narrowed store.
+template <typename IO> struct IoOps;
+
+template <> struct IoOps<float> {
+  static __device__ __forceinline__ float4_t load4(const float* p) {
+    return *reinterpret_cast<const float4_t*>(p);
+  }
+  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+};
+
+template <> struct IoOps<_Float16> {
+  static __device__ __forceinline__ float4_t load4(const _Float16* p) {
+    half4_t h = *reinterpret_cast<const half4_t*>(p);
+    return float4_t{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+  }
+  static __device__ __forceinline__ float load1(const _Float16* p) { return (float)*p; }
+  // float -> half conversion rounds to nearest even
+  static __device__ __forceinline__ void store1(_Float16* p, float x) { *p = (_Float16)x; }
+};
+
+// log(1 + e^x); above 20 the correction log1p(e^-x) < 2.1e-9 is below fp32 resolution of x.
+__device__ __forceinline__ float softplus_f(float x) {
+  return x > 20.0f ? x : log1pf(expf(x));
+}
+
+// Gate arithmetic from the raw inputs: alpha = exp(-exp(A_log) softplus(a + dt_bias)).
+__device__ __forceinline__ float decay_from_raw(float a, float expA, float dt_bias) {
+  return expf(-expA * softplus_f(a + dt_bias));
+}
+
+__device__ __forceinline__ float sigmoid_f(float b) { return 1.0f / (1.0f + expf(-b)); }
+
+}  // namespace gdn

@@ -1,0 +1,83 @@
+// gdn_replay: advance the committed state by an accepted capsule prefix and
+// write the result into an inactive state bank ("Replay compact fixed state
+// for hybrid decoding", Summary and Key Changes: compact prefix replay into
+// double-buffered banks).
+//
+//   dst[r,h] = src[r,h];  for j < m_r:  dst[r,h] = alpha_j * dst[r,h] + u_j k^_j^T
+//
+// A pure stream: every state element is read once from the committed bank and
+// written once to the inactive bank; the m_r rank-1 updates run in registers.
+// A workgroup owns one (request, value head) slice of Dv x Dk floats; thread t
+// owns the 16-byte column group t % (Dk/4) of rows t / (Dk/4) + (256/(Dk/4)) i,
+// so it needs one key vector and a few delta scalars per capsule row, read
+// through the cache (the capsule is small and shared by a head's threads).
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+template <int DK>
+__global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
+  constexpr int C4 = DK / 4;          // 16-byte column groups per row
+  constexpr int RPP = 256 / C4;       // rows per pass of the block
+  constexpr int ITERS = 128 / RPP;    // passes: the block covers 128 rows
+  const int tid = threadIdx.x;
+  const int c4 = tid % C4;
+  const int rsub = tid / C4;
+
+  const int h = blockIdx.x % p.Hv;
+  const int r = blockIdx.x / p.Hv;
+  const int g = h / p.group;
+  const int Dv = p.Dv;
+  const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
+
+  float4_t S[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int row = rsub + RPP * it;
+    S[it] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (row < Dv)
+      S[it] = *reinterpret_cast<const float4_t*>(p.src + head_off + (size_t)row * DK + 4 * c4);
+  }
+
+  const int m = min(max(p.accepted[r], 0), p.capacity);
+  const float* caprow = p.capsule + (size_t)r * p.capacity * p.capsule_width;
+  const int key_off = p.Hv + g * DK + 4 * c4;
+  const int delta_off = p.Hv + p.Hk * DK + h * Dv;
+  for (int j = 0; j < m; ++j, caprow += p.capsule_width) {
+    const float alpha = caprow[h];
+    const float4_t kk = {caprow[key_off], caprow[key_off + 1], caprow[key_off + 2], caprow[key_off + 3]};
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int row = rsub + RPP * it;
+      const float u = row < Dv ? caprow[delta_off + row] : 0.f;
+      S[it].x = fmaf(alpha, S[it].x, u * kk.x);
+      S[it].y = fmaf(alpha, S[it].y, u * kk.y);
+      S[it].z = fmaf(alpha, S[it].z, u * kk.z);
+      S[it].w = fmaf(alpha, S[it].w, u * kk.w);
+    }
+  }
+
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int row = rsub + RPP * it;
+    if (row < Dv)
+      *reinterpret_cast<float4_t*>(p.dst + head_off + (size_t)row * DK + 4 * c4) = S[it];
+  }
+}
+
+hipError_t launch_replay(const ReplayArgs& p, hipStream_t stream) {
+  if (p.R == 0) return hipSuccess;
+  const dim3 grid((unsigned)((size_t)p.R * p.Hv));
+  const dim3 block(256);
+  switch (p.Dk) {
+    case 16: hipLaunchKernelGGL(gdn_replay<16>, grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(gdn_replay<32>, grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(gdn_replay<64>, grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(gdn_replay<128>, grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

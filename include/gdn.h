@@ -1,0 +1,177 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) GatedDeltaNet operator library, libgdn.so.
+ *
+ * The operator runs the gated delta rule on packed ragged inputs and keeps an
+ * FP32 V-major recurrent state per request and value head:
+ *
+ *   alpha_t = exp(-exp(A_log[h]) * softplus(a[t,h] + dt_bias[h]))
+ *   beta_t  = sigmoid(b[t,h])
+ *   k^_t    = k[t,g] / sqrt(|k[t,g]|^2 + 1e-6)          g = h / (Hv / Hk)
+ *   q^_t    = q[t,g] / sqrt(|q[t,g]|^2 + 1e-6) * scale
+ *   u_t     = beta_t * (v[t,h] - alpha_t * S k^_t)
+ *   S       = alpha_t * S + u_t k^_t^T                    S is [Dv, Dk]
+ *   out[t,h] = S q^_t
+ *
+ * Sources, by page and section:
+ *  - "Add GatedDeltaNet evaluation export for Qwen hybrid models", What changed:
+ *    packed THD q/k/v with cumulative sequence lengths, FP32 V-major state,
+ *    the gated_delta update rule, an FP32 gate ABI, FP16/FP32 I/O only (BF16
+ *    rejected); Dependency: dt_bias is one scalar per head, a forced plan,
+ *    update-rule validation and an initial/final state alias.
+ *  - "[CUDA] Add compact GatedDeltaNet operator", Description: recurrent decode
+ *    and chunked prefill paths, ragged inputs, gate arithmetic fused from raw
+ *    A_log, and the three outputs [output, final_state, state_update] where the
+ *    FP32 state_update capsule packs decay, shared key and delta per token.
+ *  - The same page's embedded VarlenCausalConv commit, Description: a bounded
+ *    state_update_capacity and an optional per-request capture_count, the
+ *    capture shaped [batch, capacity, channels].
+ *  - "Replay compact fixed state for hybrid decoding", Summary and Key Changes:
+ *    replay of only an accepted prefix into an inactive state bank, and a
+ *    replay ABI with a version number.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; "_host" pointers point to host memory.
+ *  - The caller owns every buffer. The library keeps no pointer after a call
+ *    returns, allocates no memory and holds no global mutable state: calls on
+ *    different streams may run concurrently as long as their buffers do not
+ *    overlap.
+ *  - All device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and runs asynchronously; no call blocks on the device.
+ *  - Every argument check runs on the host before anything is enqueued. A
+ *    nonzero status other than GDN_ERR_HIP means nothing was enqueued and no
+ *    device memory was written. GDN_ERR_HIP means a kernel launch failed.
+ *  - Sizes are element counts unless named _bytes.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Version of this ABI: structs, entry points and the capsule layout. */
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,       /* a required pointer is NULL                          */
+  GDN_ERR_SHAPE = 2,      /* a size is out of range or cu_seqlens is malformed   */
+  GDN_ERR_DTYPE = 3,      /* io dtype other than FP16 / FP32 (BF16 is rejected)  */
+  GDN_ERR_ALIAS = 4,      /* buffers overlap in a way the call does not allow    */
+  GDN_ERR_CAPACITY = 5,   /* capacity < 0, or capture/accepted beyond capacity   */
+  GDN_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required          */
+  GDN_ERR_PLAN = 7,       /* forced plan not possible for these arguments        */
+  GDN_ERR_RULE = 8,       /* update rule other than the gated delta rule         */
+  GDN_ERR_HIP = 9         /* the HIP runtime rejected a launch                   */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
+
+/* Kernel path. AUTO takes RECURRENT when a capsule is requested, when Dk or Dv
+ * is not 128, or when the longest request (from cu_seqlens_host, else the mean
+ * N / R) is at most 32 tokens; otherwise CHUNK. A forced plan overrides this
+ * ("forced-plan behavior", first page, Dependency). */
+typedef enum gdn_plan { GDN_PLAN_AUTO = 0, GDN_PLAN_RECURRENT = 1, GDN_PLAN_CHUNK = 2 } gdn_plan;
+
+/* Only the gated delta rule is implemented ("update-rule input validation",
+ * first page, Dependency). */
+typedef enum gdn_rule { GDN_RULE_GATED_DELTA = 0 } gdn_rule;
+
+typedef struct gdn_params {
+  int32_t num_tokens;            /* N: packed tokens over all requests, >= 0      */
+  int32_t num_reqs;              /* R: requests (state batch), >= 0               */
+  int32_t num_k_heads;           /* Hk >= 1, divides Hv                            */
+  int32_t num_v_heads;           /* Hv >= 1                                        */
+  int32_t head_k_dim;            /* Dk in {16, 32, 64, 128}                        */
+  int32_t head_v_dim;            /* Dv in {16, 32, 64, 128}                        */
+  int32_t io_dtype;              /* gdn_dtype of q, k, v and output                */
+  float scale;                   /* query scale; <= 0 selects Dk^-1/2              */
+  int32_t chunk;                 /* chunk length of the CHUNK plan; 0 selects 64;
+                                    only 64 is supported                           */
+  int32_t state_update_capacity; /* capsule rows per request; 0: no capsule        */
+  int32_t plan;                  /* gdn_plan                                       */
+  int32_t update_rule;           /* gdn_rule; must be GDN_RULE_GATED_DELTA         */
+} gdn_params;
+
+/* Tensors of one forward call. Layouts are dense row-major with the last
+ * index fastest; "io" is the element type named by io_dtype. */
+typedef struct gdn_tensors {
+  const void* q;                 /* device, io  [N, Hk, Dk]                        */
+  const void* k;                 /* device, io  [N, Hk, Dk]                        */
+  const void* v;                 /* device, io  [N, Hv, Dv]                        */
+  const float* a;                /* device, f32 [N, Hv]  raw decay input           */
+  const float* b;                /* device, f32 [N, Hv]  raw beta input            */
+  const float* A_log;            /* device, f32 [Hv]                               */
+  const float* dt_bias;          /* device, f32 [Hv]  one scalar per value head    */
+  const int32_t* cu_seqlens;     /* device, i32 [R + 1]: 0 = cu[0] <= ... <= cu[R] = N;
+                                    request r owns tokens cu[r] .. cu[r+1]-1       */
+  const int32_t* cu_seqlens_host;/* host mirror of cu_seqlens, or NULL. When given
+                                    it is validated and used for planning.         */
+  const float* initial_state;    /* device, f32 [R, Hv, Dv, Dk], or NULL for zeros */
+  float* final_state;            /* device, f32 [R, Hv, Dv, Dk], or NULL (not
+                                    written). May equal initial_state exactly
+                                    (in-place update); any other overlap is an error */
+  void* output;                  /* device, io  [N, Hv, Dv]                        */
+  float* state_update;           /* device, f32 [R, capacity, W] with
+                                    W = Hv + Hk*Dk + Hv*Dv, or NULL (no capsule).
+                                    Row j of request r holds token cu[r]+j as
+                                    [alpha for Hv heads | k^ for Hk heads (Dk each)
+                                     | u for Hv heads (Dv each)]. Rows j >= n_r are
+                                    not written.                                   */
+  const int32_t* capture_count;  /* device, i32 [R] or NULL. Request r captures its
+                                    leading n_r = min(len_r, c_r) tokens, c_r being
+                                    capture_count[r] clamped to [0, capacity], or
+                                    capacity when NULL.                            */
+} gdn_tensors;
+
+/* Runs one forward call: output, final_state (if non-NULL) and the capsule
+ * (if state_update is non-NULL). The CHUNK plan needs a device workspace of
+ * gdn_forward_workspace_bytes() bytes, disjoint from every tensor; RECURRENT
+ * needs none (workspace may be NULL). */
+int gdn_forward(const gdn_params* params, const gdn_tensors* tensors,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_forward needs for these params, written to *bytes.
+ * cu_seqlens_host may be NULL; the result then is an upper bound that is valid
+ * for every cu_seqlens with the same N and R. Resolves the plan exactly as
+ * gdn_forward does (state_update_capacity > 0 is taken to mean a capsule). */
+int gdn_forward_workspace_bytes(const gdn_params* params, const int32_t* cu_seqlens_host,
+                                size_t* bytes);
+
+/* The plan gdn_forward would run for these params (GDN_PLAN_RECURRENT or
+ * GDN_PLAN_CHUNK), written to *plan; capsule as for the workspace query. */
+int gdn_resolve_plan(const gdn_params* params, const int32_t* cu_seqlens_host, int32_t* plan);
+
+/* Replays the leading accepted[r] capsule rows of every request r onto the
+ * committed state and writes the result to an inactive bank ("Replay compact
+ * fixed state for hybrid decoding", Summary):
+ *   dst[r,h] = src[r,h];  for j < m_r:  dst[r,h] = alpha_j * dst[r,h] + u_j k^_j^T
+ * with alpha_j, k^_j (key head h / (Hv/Hk)) and u_j read from capsule row j.
+ *   src_state     device, f32 [R, Hv, Dv, Dk]  committed bank, read only
+ *   state_update  device, f32 [R, capacity, W] as written by gdn_forward
+ *   accepted      device, i32 [R]; m_r = accepted[r] clamped to [0, capacity]
+ *   accepted_host host mirror of accepted or NULL; when given every value must
+ *                 lie in [0, capacity] (else GDN_ERR_CAPACITY)
+ *   dst_state     device, f32 [R, Hv, Dv, Dk]; must not overlap src_state,
+ *                 state_update or accepted. m_r = 0 copies the committed state.
+ * The caller guarantees m_r <= n_r (rows beyond n_r hold no capture). */
+int gdn_replay(int32_t num_reqs, int32_t num_k_heads, int32_t num_v_heads,
+               int32_t head_k_dim, int32_t head_v_dim, int32_t state_update_capacity,
+               const float* src_state, const float* state_update, const int32_t* accepted,
+               const int32_t* accepted_host, float* dst_state, void* stream);
+
+/* Static text for a status code. */
+const char* gdn_strerror(int status);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,211 @@
+"""Host-side checks of libgdn.so: it loads, exports what include/gdn.h declares,
+and rejects bad arguments on the host before anything reaches the GPU.
+
+No call here launches a kernel: every forward/replay call is built to fail a
+host-side check (fake device addresses are never dereferenced), and the
+workspace / plan queries are host-only by contract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gateddeltanet_recurrence_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0        # counts devices without initialising HIP
+    except Exception:
+        return False
+
+
+# Fake device addresses must never reach a real GPU: these host checks run only
+# where no GPU is visible (a call that passed validation would launch a kernel).
+pytestmark = [
+    pytest.mark.skipif(not os.path.exists(gdn.library_path()),
+                       reason="libgdn.so not built (run the build first)"),
+    pytest.mark.skipif(_gpu_visible(), reason="fake-pointer host checks run only without a GPU"),
+]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_forward", "gdn_replay", "gdn_forward_workspace_bytes", "gdn_resolve_plan",
+              "gdn_strerror", "gdn_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_strerror():
+    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
+    assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
+    assert gdn.gdn_strerror(12345) == "unknown status"
+
+
+# -------------------------------------------------------- raw ABI helpers
+FAKE = 1 << 40          # a 16-byte aligned address that is never dereferenced
+
+
+def _tensors(N, R, Hk, Hv, Dk, Dv, io=2, **override):
+    """Disjoint fake device ranges for every tensor of a forward call."""
+    sizes = {"q": N * Hk * Dk * io, "k": N * Hk * Dk * io, "v": N * Hv * Dv * io,
+             "a": N * Hv * 4, "b": N * Hv * 4, "A_log": Hv * 4, "dt_bias": Hv * 4,
+             "cu_seqlens": (R + 1) * 4, "initial_state": R * Hv * Dv * Dk * 4,
+             "final_state": R * Hv * Dv * Dk * 4, "output": N * Hv * Dv * io}
+    t = gdn.GdnTensors()
+    addr = FAKE
+    for name, size in sizes.items():
+        setattr(t, name, addr)
+        addr += (size + 4095) // 4096 * 4096 + 4096
+    for name, val in override.items():
+        setattr(t, name, val)
+    return t, addr
+
+
+def _forward(params, tensors, ws=None, ws_bytes=0):
+    return gdn.lib().gdn_forward(ctypes.byref(params), ctypes.byref(tensors), ws,
+                                 ctypes.c_size_t(ws_bytes), None)
+
+
+def _p(N=8, R=2, Hk=2, Hv=4, Dk=16, Dv=16, io=gdn.GDN_F16, **kw):
+    return gdn.make_params(N, R, Hk, Hv, Dk, Dv, io, **kw)
+
+
+def test_null_structs():
+    t, _ = _tensors(8, 2, 2, 4, 16, 16)
+    assert gdn.lib().gdn_forward(None, ctypes.byref(t), None, 0, None) == gdn.GDN_ERR_NULL
+    p = _p()
+    assert gdn.lib().gdn_forward(ctypes.byref(p), None, None, 0, None) == gdn.GDN_ERR_NULL
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("io_dtype", gdn.GDN_BF16, gdn.GDN_ERR_DTYPE),
+    ("io_dtype", 7, gdn.GDN_ERR_DTYPE),
+    ("update_rule", 1, gdn.GDN_ERR_RULE),
+    ("num_v_heads", 3, gdn.GDN_ERR_SHAPE),          # Hk = 2 does not divide 3
+    ("head_k_dim", 48, gdn.GDN_ERR_SHAPE),
+    ("head_v_dim", 256, gdn.GDN_ERR_SHAPE),
+    ("num_tokens", -1, gdn.GDN_ERR_SHAPE),
+    ("num_k_heads", 0, gdn.GDN_ERR_SHAPE),
+    ("state_update_capacity", -1, gdn.GDN_ERR_CAPACITY),
+    ("chunk", 32, gdn.GDN_ERR_SHAPE),
+    ("plan", 9, gdn.GDN_ERR_PLAN),
+    ("scale", float("nan"), gdn.GDN_ERR_SHAPE),
+])
+def test_param_validation(field, value, code):
+    p = _p()
+    setattr(p, field, value)
+    t, _ = _tensors(8, 2, 2, 4, 16, 16)
+    assert _forward(p, t) == code
+    out = ctypes.c_size_t(0)
+    assert gdn.lib().gdn_forward_workspace_bytes(ctypes.byref(p), None, ctypes.byref(out)) == code
+
+
+def test_missing_required_pointers():
+    for name in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens", "output"):
+        t, _ = _tensors(8, 2, 2, 4, 16, 16, **{name: None})
+        assert _forward(_p(), t) == gdn.GDN_ERR_NULL, name
+
+
+def test_tokens_without_requests_is_a_shape_error():
+    t, _ = _tensors(8, 0, 2, 4, 16, 16)
+    assert _forward(_p(N=8, R=0), t) == gdn.GDN_ERR_SHAPE
+    assert _forward(_p(N=0, R=0), t) == gdn.GDN_OK           # nothing to do, nothing launched
+
+
+def test_misaligned_state_is_rejected():
+    t, _ = _tensors(8, 2, 2, 4, 16, 16)
+    t.initial_state = t.initial_state + 4
+    assert _forward(_p(), t) == gdn.GDN_ERR_SHAPE
+
+
+@pytest.mark.parametrize("cu,code", [
+    ([1, 4, 8], gdn.GDN_ERR_SHAPE),      # must start at 0
+    ([0, 5, 4], gdn.GDN_ERR_SHAPE),      # decreasing
+    ([0, 4, 7], gdn.GDN_ERR_SHAPE),      # does not end at N = 8
+])
+def test_host_cu_seqlens_validation(cu, code):
+    t, _ = _tensors(8, 2, 2, 4, 16, 16)
+    host = np.asarray(cu, np.int32)
+    t.cu_seqlens_host = host.ctypes.data
+    assert _forward(_p(), t) == code
+
+
+def test_alias_rules():
+    N, R, Hk, Hv, Dk, Dv = 8, 2, 2, 4, 16, 16
+    # output overlapping v
+    t, _ = _tensors(N, R, Hk, Hv, Dk, Dv)
+    t.output = t.v + 64
+    assert _forward(_p(), t) == gdn.GDN_ERR_ALIAS
+    # final_state partially overlapping initial_state
+    t, _ = _tensors(N, R, Hk, Hv, Dk, Dv)
+    t.final_state = t.initial_state + 1024
+    assert _forward(_p(), t) == gdn.GDN_ERR_ALIAS
+    # final_state over q
+    t, _ = _tensors(N, R, Hk, Hv, Dk, Dv)
+    t.final_state = t.q
+    assert _forward(_p(), t) == gdn.GDN_ERR_ALIAS
+
+
+def test_capsule_rules():
+    N, R, Hk, Hv, Dk, Dv = 8, 2, 2, 4, 16, 16
+    t, end = _tensors(N, R, Hk, Hv, Dk, Dv)
+    t.state_update = end
+    # a capsule with zero capacity has no rows to write
+    assert _forward(_p(capacity=0), t) == gdn.GDN_ERR_CAPACITY
+    # a capsule forces the recurrent path: a forced CHUNK plan is refused
+    assert _forward(_p(Dk=128, Dv=128, capacity=4, plan=gdn.PLAN_CHUNK),
+                    _tensors(N, R, Hk, Hv, 128, 128, state_update=end * 4)[0]) == gdn.GDN_ERR_PLAN
+    # the capsule may not overlap the output
+    t2, _ = _tensors(N, R, Hk, Hv, Dk, Dv)
+    t2.state_update = t2.output
+    assert _forward(_p(capacity=2), t2) == gdn.GDN_ERR_ALIAS
+
+
+def test_plan_resolution_is_host_only():
+    # capsule -> recurrent; small dims -> recurrent; forced recurrent honoured
+    assert gdn.gdn_resolve_plan(64, 16, 16, 48, 128, 128, capacity=4) == gdn.PLAN_RECURRENT
+    assert gdn.gdn_resolve_plan(4096, 1, 2, 2, 16, 16) == gdn.PLAN_RECURRENT
+    assert gdn.gdn_resolve_plan(4096, 1, 16, 32, 128, 128, plan=gdn.PLAN_RECURRENT) == gdn.PLAN_RECURRENT
+    assert gdn.gdn_resolve_plan(64, 64, 16, 32, 128, 128) == gdn.PLAN_RECURRENT
+    assert gdn.gdn_forward_workspace_bytes(64, 64, 16, 32, 128, 128) == 0
+
+
+def test_replay_validation():
+    L = gdn.lib()
+    src, cap, acc, dst = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    R, Hk, Hv, D = 2, 1, 2, 16
+    assert L.gdn_replay(R, 2, 3, D, D, 4, src, cap, acc, None, dst, None) == gdn.GDN_ERR_SHAPE
+    assert L.gdn_replay(R, Hk, Hv, 48, D, 4, src, cap, acc, None, dst, None) == gdn.GDN_ERR_SHAPE
+    assert L.gdn_replay(R, Hk, Hv, D, D, -1, src, cap, acc, None, dst, None) == gdn.GDN_ERR_CAPACITY
+    assert L.gdn_replay(R, Hk, Hv, D, D, 4, None, cap, acc, None, dst, None) == gdn.GDN_ERR_NULL
+    assert L.gdn_replay(R, Hk, Hv, D, D, 4, src, None, acc, None, dst, None) == gdn.GDN_ERR_NULL
+    assert L.gdn_replay(R, Hk, Hv, D, D, 4, src, cap, acc, None, src + 64, None) == gdn.GDN_ERR_ALIAS
+    assert L.gdn_replay(R, Hk, Hv, D, D, 4, src, cap, acc, None, cap, None) == gdn.GDN_ERR_ALIAS
+    bad = np.asarray([1, 5], np.int32)                       # 5 > capacity 4
+    assert L.gdn_replay(R, Hk, Hv, D, D, 4, src, cap, acc, bad.ctypes.data, dst, None) == gdn.GDN_ERR_CAPACITY
+    neg = np.asarray([-1, 0], np.int32)
+    assert L.gdn_replay(R, Hk, Hv, D, D, 4, src, cap, acc, neg.ctypes.data, dst, None) == gdn.GDN_ERR_CAPACITY
+    assert L.gdn_replay(0, Hk, Hv, D, D, 4, None, None, None, None, None, None) == gdn.GDN_OK

@@ -1,0 +1,240 @@
+"""GPU parity of the recurrent kernels (gdn_decode, gdn_capsule) and gdn_replay
+against the float64 oracle, called through the C ABI.
+
+Tolerances (written here, applied by gpu_helpers.assert_parity):
+  FP32 I/O  max|x-y| / max|y| <= 1e-4 for output and final state
+  FP16 I/O  output max-abs <= 2e-2, final-state relative L2 <= 1e-3
+  replay vs the GPU's own recurrence on the same prefix: rel-max <= 1e-5
+  capsule / accepted-prefix indexing: bit-exact (untouched rows keep their poison)
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+from gdn_workloads import cu_from_lengths, make_inputs, workload_inputs
+from gpu_helpers import (TOL_F32_REL, TOL_REPLAY_REL, assert_parity, dev, oracle_forward,
+                         rel_max, run_forward)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gateddeltanet_recurrence_amd as gdn          # noqa: E402
+from oracle import gdn_oracle as O                   # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.lib()                                         # fails loudly if libgdn.so is missing
+
+
+def _case(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+def test_tiny_recurrent_fp32():
+    inp = workload_inputs("tiny_recurrent")
+    _case("tiny_recurrent fp32 T=16 Hk=Hv=2 D=16")
+    res = run_forward(inp, torch, gdn)
+    ref_o, ref_s, _ = oracle_forward(inp, O)
+    assert_parity("f32", res["output"], ref_o, res["final_state"], ref_s, "tiny")
+
+
+def test_batched_decode_in_place_fp16():
+    inp = workload_inputs("batched_decode")
+    _case("batched_decode fp16 R=64 Hv=32 D=128 in place")
+    res = run_forward(inp, torch, gdn, in_place=True)
+    ref_o, ref_s, _ = oracle_forward(inp, O)
+    assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "decode")
+
+
+@pytest.mark.parametrize("io", ["f32", "f16"])
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)])
+def test_ragged_recurrent_shapes(io, Dk, Dv):
+    lengths = [1, 7, 0, 33, 5, 64, 2]
+    inp = make_inputs(lengths, 2, 6, Dk, Dv, io, seed=100 + Dk + Dv)
+    _case(f"ragged recurrent io={io} Dk={Dk} Dv={Dv} lengths={lengths}")
+    res = run_forward(inp, torch, gdn, plan=gdn.PLAN_RECURRENT)
+    ref_o, ref_s, _ = oracle_forward(inp, O)
+    assert_parity(io, res["output"], ref_o, res["final_state"], ref_s, f"{io} {Dk}x{Dv}")
+
+
+def test_explicit_scale_and_zero_initial_state():
+    inp = make_inputs([9, 4], 1, 2, 32, 32, "f32", seed=7, initial="zero")
+    _case("explicit scale 0.3, zero initial state")
+    res = run_forward(inp, torch, gdn, scale=0.3)
+    ref_o, ref_s, _ = oracle_forward(inp, O, scale=0.3)
+    assert rel_max(res["output"], ref_o) <= TOL_F32_REL
+    assert rel_max(res["final_state"], ref_s) <= TOL_F32_REL
+
+
+def test_in_place_matches_out_of_place_bitwise():
+    inp = make_inputs([3, 1, 6], 2, 4, 128, 128, "f16", seed=8)
+    _case("in place vs out of place")
+    a = run_forward(inp, torch, gdn)
+    b = run_forward(inp, torch, gdn, in_place=True)
+    assert np.array_equal(a["output"], b["output"])
+    assert np.array_equal(a["final_state"], b["final_state"])
+
+
+def test_packing_invariance_bitwise():
+    lengths = [17, 5, 40]                              # a small ragged mix
+    inp = make_inputs(lengths, 2, 4, 64, 64, "f16", seed=9)
+    _case(f"packing invariance lengths={lengths}")
+    packed = run_forward(inp, torch, gdn, plan=gdn.PLAN_RECURRENT)
+    cu = inp["cu_seqlens"]
+    for r, L in enumerate(lengths):
+        sub = dict(inp)
+        for n in ("q", "k", "v", "a", "b"):
+            sub[n] = inp[n][cu[r]:cu[r + 1]]
+        sub["cu_seqlens"] = cu_from_lengths([L])
+        sub["initial_state"] = inp["initial_state"][r:r + 1]
+        alone = run_forward(sub, torch, gdn, plan=gdn.PLAN_RECURRENT)
+        assert np.array_equal(alone["output"], packed["output"][cu[r]:cu[r + 1]])
+        assert np.array_equal(alone["final_state"][0], packed["final_state"][r])
+
+
+def test_no_final_state_leaves_initial_untouched():
+    inp = make_inputs([4, 4], 1, 2, 128, 128, "f16", seed=10)
+    _case("final_state NULL")
+    res = run_forward(inp, torch, gdn, write_final=False)
+    assert np.array_equal(res["initial_after"], inp["initial_state"])
+    ref_o, _, _ = oracle_forward(inp, O)
+    assert_parity("f16", res["output"], ref_o, what="no-final")
+
+
+def test_empty_segments_copy_state():
+    inp = make_inputs([0, 3, 0, 0], 1, 1, 32, 16, "f32", seed=11)
+    _case("empty segments")
+    res = run_forward(inp, torch, gdn)
+    for r in (0, 2, 3):
+        assert np.array_equal(res["final_state"][r], inp["initial_state"][r])
+
+
+def test_bf16_rejected_without_writes():
+    inp = make_inputs([2], 1, 1, 16, 16, "f32", seed=12)
+    _case("bf16 rejected")
+    d = {n: dev(inp[n], torch) for n in ("a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    q = dev(inp["q"], torch, torch.bfloat16)
+    k = dev(inp["k"], torch, torch.bfloat16)
+    v = dev(inp["v"], torch, torch.bfloat16)
+    out = torch.full(v.shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    st = gdn.gdn_forward(q, k, v, d["a"], d["b"], d["A_log"], d["dt_bias"], d["cu_seqlens"], out,
+                         check=False)
+    torch.cuda.synchronize()
+    assert st == gdn.GDN_ERR_DTYPE
+    assert bool(torch.all(out == 3.0))
+
+
+# ---------------------------------------------------------------- capsule
+def _capsule_sections(Hk, Hv, Dk, Dv):
+    return O.capsule_sections(Hk, Hv, Dk, Dv)
+
+
+def test_spec_verify_capsule():
+    inp = workload_inputs("spec_verify_replay")
+    cap = inp["capacity"]
+    _case("spec_verify capsule R=16 T=4 Hv=48 cap=4")
+    res = run_forward(inp, torch, gdn, capacity=cap, write_final=False, poison=-7.0)
+    ref_o, _, ref_cap = oracle_forward(inp, O, capacity=cap, poison=-7.0)
+    assert_parity("f16", res["output"], ref_o, what="verify")
+    assert np.array_equal(res["initial_after"], inp["initial_state"])   # committed bank untouched
+    got = res["state_update"]
+    sa, sk, sd = _capsule_sections(inp["Hk"], inp["Hv"], inp["Dk"], inp["Dv"])
+    assert rel_max(got[..., sa], ref_cap[..., sa]) <= 1e-5
+    assert rel_max(got[..., sk], ref_cap[..., sk]) <= 1e-5
+    # deltas depend on the state the way outputs do: FP16-input tolerance on their scale
+    assert rel_max(got[..., sd], ref_cap[..., sd]) <= 1e-3
+
+
+def test_capture_count_and_untouched_rows():
+    lengths = [4, 2, 5, 0, 3]
+    cap = 4
+    inp = make_inputs(lengths, 2, 4, 64, 32, "f32", seed=13, capacity=cap)
+    cc = np.array([4, 4, 2, 3, 0], np.int32)
+    _case(f"capture_count {cc.tolist()} lengths={lengths}")
+    res = run_forward(inp, torch, gdn, capacity=cap, capture_count=cc, poison=-7.0)
+    ref_o, ref_s, ref_cap = oracle_forward(inp, O, capacity=cap, capture_count=cc, poison=-7.0)
+    assert_parity("f32", res["output"], ref_o, res["final_state"], ref_s, "capture")
+    got = res["state_update"]
+    for r, L in enumerate(lengths):
+        n = min(L, cc[r], cap)
+        assert np.all(got[r, n:] == -7.0), r                    # bit-exact: untouched
+        assert np.all(got[r, :n] != -7.0), r
+        if n:
+            assert rel_max(got[r, :n], ref_cap[r, :n]) <= TOL_F32_REL
+
+
+def test_capture_count_clamped_to_capacity():
+    inp = make_inputs([6, 6], 1, 1, 16, 16, "f32", seed=14, capacity=3)
+    cc = np.array([99, -5], np.int32)
+    _case("capture_count clamped")
+    res = run_forward(inp, torch, gdn, capacity=3, capture_count=cc, poison=-7.0)
+    assert np.all(res["state_update"][0] != -7.0)
+    assert np.all(res["state_update"][1] == -7.0)
+
+
+# ----------------------------------------------------------------- replay
+def _replay(src, capsule, accepted, Hk, cap, accepted_host=True):
+    s = torch.from_numpy(np.ascontiguousarray(src)).cuda()
+    c = torch.from_numpy(np.ascontiguousarray(capsule)).cuda()
+    a = torch.from_numpy(np.ascontiguousarray(accepted)).cuda()
+    dst = torch.full_like(s, float("nan"))
+    gdn.gdn_replay(s, c, a, dst, num_k_heads=Hk, state_update_capacity=cap,
+                   accepted_host=accepted if accepted_host else None)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy()
+
+
+def test_replay_matches_own_recurrence_and_oracle():
+    inp = workload_inputs("spec_verify_replay")
+    cap, Hk, Hv, Dk, Dv = inp["capacity"], inp["Hk"], inp["Hv"], inp["Dk"], inp["Dv"]
+    acc = inp["accepted"]
+    _case(f"replay accepted={acc.tolist()}")
+    verify = run_forward(inp, torch, gdn, capacity=cap, write_final=False)
+    dst = _replay(inp["initial_state"], verify["state_update"], acc, Hk, cap)
+    # the GPU's own sequential state after the accepted prefix of every request
+    cu = inp["cu_seqlens"]
+    sub = dict(inp)
+    idx = np.concatenate([np.arange(cu[r], cu[r] + acc[r]) for r in range(len(acc))]).astype(int)
+    for n in ("q", "k", "v", "a", "b"):
+        sub[n] = inp[n][idx]
+    sub["cu_seqlens"] = cu_from_lengths(acc)
+    own = run_forward(sub, torch, gdn, plan=gdn.PLAN_RECURRENT)
+    assert rel_max(dst, own["final_state"]) <= TOL_REPLAY_REL
+    # and the float64 oracle replay of the GPU capsule
+    ref = O.gdn_replay(inp["initial_state"], verify["state_update"], acc, Hk, Hv, Dk, Dv)
+    assert rel_max(dst, ref) <= TOL_REPLAY_REL
+    for r in np.nonzero(acc == 0)[0]:
+        assert np.array_equal(dst[r], inp["initial_state"][r])      # m = 0 copies exactly
+
+
+@pytest.mark.parametrize("m", [0, 1, 2, 3, 4])
+def test_replay_every_prefix_length(m):
+    lengths = [4, 4, 4]
+    inp = make_inputs(lengths, 2, 4, 128, 64, "f16", seed=15, capacity=4)
+    _case(f"replay prefix m={m}")
+    verify = run_forward(inp, torch, gdn, capacity=4, write_final=False)
+    acc = np.full(3, m, np.int32)
+    dst = _replay(inp["initial_state"], verify["state_update"], acc, 2, 4, accepted_host=False)
+    ref = O.gdn_replay(inp["initial_state"], verify["state_update"], acc, 2, 4, 128, 64)
+    assert rel_max(dst, ref) <= TOL_REPLAY_REL
+    if m == 0:
+        assert np.array_equal(dst, inp["initial_state"])
+
+
+def test_replay_rejects_accepted_beyond_capacity():
+    src = np.zeros((2, 2, 16, 16), np.float32)
+    capsule = np.zeros((2, 4, gdn.capsule_width(1, 2, 16, 16)), np.float32)
+    s = torch.from_numpy(src).cuda()
+    c = torch.from_numpy(capsule).cuda()
+    a = torch.tensor([1, 5], dtype=torch.int32, device="cuda")
+    dst = torch.full_like(s, 9.0)
+    st = gdn.gdn_replay(s, c, a, dst, num_k_heads=1, state_update_capacity=4,
+                        accepted_host=[1, 5], check=False)
+    torch.cuda.synchronize()
+    assert st == gdn.GDN_ERR_CAPACITY and bool(torch.all(dst == 9.0))
