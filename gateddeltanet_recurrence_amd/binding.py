@@ -51,7 +51,8 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(PKG, _LIB_NAME)
+    """libgdn.so next to this file, or the file named by GDN_LIBRARY."""
+    return os.environ.get("GDN_LIBRARY") or os.path.join(PKG, _LIB_NAME)
 
 
 def lib() -> ctypes.CDLL:

@@ -23,7 +23,35 @@
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
+// Launch shape of the Dk = 128 instantiation: state rows per lane group (NI) and
+// waves per workgroup; state streams may use nontemporal loads/stores.
+#ifndef GDN_REC_NI128
+#define GDN_REC_NI128 2
+#endif
+#ifndef GDN_REC_WAVES
+#define GDN_REC_WAVES 4
+#endif
+#ifndef GDN_STATE_NT
+#define GDN_STATE_NT 1
+#endif
+
 namespace gdn {
+
+__device__ __forceinline__ float4_t load_state4(const float* p) {
+#if GDN_STATE_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(p));
+#else
+  return *reinterpret_cast<const float4_t*>(p);
+#endif
+}
+
+__device__ __forceinline__ void store_state4(float* p, float4_t x) {
+#if GDN_STATE_NT
+  __builtin_nontemporal_store(x, reinterpret_cast<float4_t*>(p));
+#else
+  *reinterpret_cast<float4_t*>(p) = x;
+#endif
+}
 
 template <int DK>
 struct RecLayout {
@@ -71,7 +99,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     for (int j = 0; j < V4; ++j) {
       float4_t x = {0.f, 0.f, 0.f, 0.f};
       if (p.initial_state != nullptr && valid[i])
-        x = *reinterpret_cast<const float4_t*>(p.initial_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j);
+        x = load_state4(p.initial_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j);
       S[i][4 * j + 0] = x.x;
       S[i][4 * j + 1] = x.y;
       S[i][4 * j + 2] = x.z;
@@ -191,7 +219,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
 #pragma unroll
       for (int j = 0; j < V4; ++j) {
         float4_t x = {S[i][4 * j + 0], S[i][4 * j + 1], S[i][4 * j + 2], S[i][4 * j + 3]};
-        *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j) = x;
+        store_state4(p.final_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
       }
     }
   }
@@ -199,11 +227,11 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
 
 // Distinct kernel names for the profiler: gdn_decode (no capture) and gdn_capsule.
 template <typename IO, int DK, int NI>
-__global__ void __launch_bounds__(256) gdn_decode(RecurrentArgs p, int wpb, int bph) {
+__global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_decode(RecurrentArgs p, int wpb, int bph) {
   recurrent_body<IO, DK, NI, false>(p, wpb, bph);
 }
 template <typename IO, int DK, int NI>
-__global__ void __launch_bounds__(256) gdn_capsule(RecurrentArgs p, int wpb, int bph) {
+__global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_capsule(RecurrentArgs p, int wpb, int bph) {
   recurrent_body<IO, DK, NI, true>(p, wpb, bph);
 }
 
@@ -211,7 +239,7 @@ template <typename IO, int DK, int NI>
 static hipError_t launch_dk(const RecurrentArgs& p, hipStream_t stream) {
   constexpr int RW = RecLayout<DK>::RI * NI;
   const int waves_needed = (p.Dv + RW - 1) / RW;
-  const int wpb = waves_needed < 4 ? waves_needed : 4;
+  const int wpb = waves_needed < GDN_REC_WAVES ? waves_needed : GDN_REC_WAVES;
   const int bph = (p.Dv + wpb * RW - 1) / (wpb * RW);
   const dim3 grid((unsigned)((size_t)p.R * p.Hv * bph));
   const dim3 block((unsigned)(64 * wpb));
@@ -228,7 +256,7 @@ static hipError_t launch_io(const RecurrentArgs& p, hipStream_t stream) {
     case 16: return launch_dk<IO, 16, 1>(p, stream);
     case 32: return launch_dk<IO, 32, 2>(p, stream);
     case 64: return launch_dk<IO, 64, 2>(p, stream);
-    case 128: return launch_dk<IO, 128, 2>(p, stream);
+    case 128: return launch_dk<IO, 128, GDN_REC_NI128>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,7 +6,8 @@
 //   dst[r,h] = src[r,h];  for j < m_r:  dst[r,h] = alpha_j * dst[r,h] + u_j k^_j^T
 //
 // A pure stream: every state element is read once from the committed bank and
-// written once to the inactive bank; the m_r rank-1 updates run in registers.
+// written once to the inactive bank (nontemporal, so the streams do not evict
+// cached data); the m_r rank-1 updates run in registers.
 // A workgroup owns one (request, value head) slice of Dv x Dk floats; thread t
 // owns the 16-byte column group t % (Dk/4) of rows t / (Dk/4) + (256/(Dk/4)) i,
 // so it needs one key vector and a few delta scalars per capsule row, read
@@ -37,7 +38,7 @@ __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
     const int row = rsub + RPP * it;
     S[it] = float4_t{0.f, 0.f, 0.f, 0.f};
     if (row < Dv)
-      S[it] = *reinterpret_cast<const float4_t*>(p.src + head_off + (size_t)row * DK + 4 * c4);
+      S[it] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(p.src + head_off + (size_t)row * DK + 4 * c4));
   }
 
   const int m = min(max(p.accepted[r], 0), p.capacity);
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
   for (int it = 0; it < ITERS; ++it) {
     const int row = rsub + RPP * it;
     if (row < Dv)
-      *reinterpret_cast<float4_t*>(p.dst + head_off + (size_t)row * DK + 4 * c4) = S[it];
+      __builtin_nontemporal_store(S[it], reinterpret_cast<float4_t*>(p.dst + head_off + (size_t)row * DK + 4 * c4));
   }
 }
 
