@@ -17,7 +17,6 @@
 namespace {
 
 constexpr int kRecurrentMaxLenForAuto = 32;
-constexpr bool kChunkPathBuilt = false;
 
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
@@ -95,7 +94,8 @@ int resolve_plan(const gdn_params* p, const int32_t* cu_host, bool capsule, Reso
     max_len = rv->R > 0 ? (rv->N + rv->R - 1) / rv->R : 0;  // mean, for planning only
     slots = rv->R > 0 ? (rv->N + rv->R * (gdn::kChunk - 1)) / gdn::kChunk : 0;
   }
-  const bool chunk_shape = kChunkPathBuilt && rv->Dk == 128 && rv->Dv == 128;
+  // the MFMA chunk path takes fp16 operands: it serves fp16 I/O at Dk = Dv = 128
+  const bool chunk_shape = rv->Dk == 128 && rv->Dv == 128 && p->io_dtype == GDN_F16;
   int plan = p->plan;
   if (plan == GDN_PLAN_CHUNK) {
     if (capsule || !chunk_shape) return GDN_ERR_PLAN;

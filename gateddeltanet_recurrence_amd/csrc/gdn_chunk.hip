@@ -1,10 +1,608 @@
-// Chunked prefill: not built yet; the plan resolver never selects it.
+// Chunked prefill of the gated delta rule on fp16 MFMA (gfx950): gdn_chunk_prefill.
+//
+// The tensor-core chunked prefill path of "[CUDA] Add compact GatedDeltaNet
+// operator" (Description), rebuilt for CDNA4: chunk C = 64, an intra-chunk
+// UT/WY transform and the state passing on v_mfma_f32_16x16x32_f16 with FP32
+// accumulation; the inter-chunk state is carried in FP32.
+//
+// Per sequence, chunks start at the sequence's first token (the last one may be
+// short, length L <= 64). For one chunk and value head h (key head g = h / G),
+// with k^ = rk k, q^ = rq q (rq includes the query scale), g_t the in-chunk
+// cumulative log decay and S0 the state entering the chunk:
+//   A[r,i] = beta_r e^{g_r - g_i} k^_r.k^_i  (i < r),   T = (I + A)^-1
+//   P[r,i] = e^{g_r - g_i} q^_r.k^_i         (i <= r)
+//   X = K S0^T,  Y = Q S0^T                              (raw fp16 k, q)
+//   Z = diag(beta) (V - diag(e^g rk) X),   U = T Z       (U rows: the deltas u_t)
+//   O = diag(e^g rq) Y + P U
+//   S = e^{g_L} S0 + (diag(e^{g_L - g} rk) U)^T K
+// Everything that does not depend on S0 (Gram matrices, T, P, gates, norms) is
+// chunk-parallel and done first by gdn_chunk_prep; gdn_chunk_scan then walks
+// the chunks of each sequence in order. The rows of S evolve independently,
+// so the scan splits every head's state into Dv tiles of TV rows, one
+// workgroup each: the serial chain is spread over heads x tiles workgroups.
+//
+// Kernels: gdn_chunk_index (chunk offsets per sequence), gdn_chunk_prep,
+// gdn_chunk_scan. Dk = Dv = 128, fp16 I/O only.
+#include "gdn_common.h"
 #include "gdn_kernels.h"
 
 namespace gdn {
 
-size_t chunk_workspace_bytes(int64_t, int, int, int) { return 0; }
+namespace {
 
-hipError_t launch_chunk(const ChunkArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+constexpr int C = kChunk;     // 64 tokens per chunk
+constexpr int D = 128;        // Dk = Dv
+constexpr int KS = D + 8;     // LDS row stride (halves) of 128-wide fp16 tiles
+constexpr int TS = C + 8;     // LDS row stride (halves) of 64-wide fp16 tiles
+constexpr int AS = C + 4;     // LDS row stride (floats) of the fp32 A matrix
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float4_t mfma_f16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8_t lds8(const _Float16* p) {
+  return *reinterpret_cast<const half8_t*>(p);
+}
+
+// Workspace layout: chunk offsets, then per (slot, value head) T and P (fp16
+// 64x64 row-major), per (slot, value head) [g; beta] and per (slot, key head)
+// [rk; rq] (fp32, 64 each).
+struct Ws {
+  int32_t* chunk_start;
+  _Float16* T;
+  _Float16* P;
+  float* gb;
+  float* nrm;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline Ws ws_layout(void* base, int64_t slots, int R, int Hk, int Hv) {
+  char* p = static_cast<char*>(base);
+  Ws w;
+  size_t off = 0;
+  w.chunk_start = reinterpret_cast<int32_t*>(p + off);
+  off += align256((size_t)(R + 1) * 4);
+  w.T = reinterpret_cast<_Float16*>(p + off);
+  off += align256((size_t)slots * Hv * C * C * 2);
+  w.P = reinterpret_cast<_Float16*>(p + off);
+  off += align256((size_t)slots * Hv * C * C * 2);
+  w.gb = reinterpret_cast<float*>(p + off);
+  off += align256((size_t)slots * Hv * 2 * C * 4);
+  w.nrm = reinterpret_cast<float*>(p + off);
+  return w;
+}
+
+__host__ inline size_t ws_bytes(int64_t slots, int R, int Hk, int Hv) {
+  return align256((size_t)(R + 1) * 4) + 2 * align256((size_t)slots * Hv * C * C * 2) +
+         align256((size_t)slots * Hv * 2 * C * 4) + align256((size_t)slots * Hk * 2 * C * 4);
+}
+
+__device__ __forceinline__ int clamp_cu(const int32_t* cu, int i, int N) {
+  return min(max(cu[i], 0), N);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// chunk offsets: chunk_start[r] = sum_{i<r} ceil(len_i / 64), chunk_start[R] = total
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) gdn_chunk_index(ChunkArgs p, Ws w) {
+  __shared__ int part[kThreads];
+  const int tid = threadIdx.x;
+  const int per = (p.R + kThreads - 1) / kThreads;
+  const int r0 = min(tid * per, p.R), r1 = min(r0 + per, p.R);
+  int prev = clamp_cu(p.cu_seqlens, r0, p.N);
+  int sum = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int nxt = max(clamp_cu(p.cu_seqlens, r + 1, p.N), prev);
+    sum += (nxt - prev + C - 1) / C;
+    prev = nxt;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  // inclusive scan of the 256 partial sums (Hillis-Steele)
+  for (int d = 1; d < kThreads; d <<= 1) {
+    const int v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid > 0 ? part[tid - 1] : 0;
+  prev = clamp_cu(p.cu_seqlens, r0, p.N);
+  for (int r = r0; r < r1; ++r) {
+    w.chunk_start[r] = run;
+    const int nxt = max(clamp_cu(p.cu_seqlens, r + 1, p.N), prev);
+    run += (nxt - prev + C - 1) / C;
+    prev = nxt;
+  }
+  if (tid == kThreads - 1) w.chunk_start[p.R] = part[kThreads - 1];
+}
+
+// Locates (request, first token, length) of a chunk slot; false past the end.
+__device__ __forceinline__ bool locate_chunk(const ChunkArgs& p, const Ws& w, int slot, int* req,
+                                             int* t0, int* len) {
+  const int total = min(w.chunk_start[p.R], p.max_chunks);
+  if (slot >= total) return false;
+  int lo = 0, hi = p.R - 1;                 // last r with chunk_start[r] <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (w.chunk_start[mid] <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int beg = clamp_cu(p.cu_seqlens, lo, p.N);
+  const int end = max(clamp_cu(p.cu_seqlens, lo + 1, p.N), beg);
+  *req = lo;
+  *t0 = beg + C * (slot - w.chunk_start[lo]);
+  *len = min(C, end - *t0);
+  return *len > 0;
+}
+
+// ----------------------------------------------------------------------------
+// gdn_chunk_prep: one workgroup per (chunk slot, key head)
+// ----------------------------------------------------------------------------
+struct PrepSmem {
+  union {
+    struct {
+      _Float16 K[C * KS];
+      _Float16 Q[C * KS];
+    } in;
+    float A[4][C * AS];        // A of up to four value heads (after the Gram step)
+  } u;
+  float rk[C], rq[C];
+  float g[4][C], beta[4][C];
+};
+
+__global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
+  __shared__ PrepSmem sm;
+  const int slot = blockIdx.x;
+  const int g = blockIdx.y;
+  int req, t0, L;
+  if (!locate_chunk(p, w, slot, &req, &t0, &L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const _Float16* kp = static_cast<const _Float16*>(p.k);
+  const _Float16* qp = static_cast<const _Float16*>(p.q);
+
+  // ---- K, Q chunk tiles into LDS (rows >= L zero)
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + kThreads * it;    // 1024 16-byte pieces per tile
+    const int row = idx >> 4, c8 = (idx & 15) * 8;
+    half8_t kv = {}, qv = {};
+    if (row < L) {
+      const size_t off = ((size_t)(t0 + row) * p.Hk + g) * D + c8;
+      kv = *reinterpret_cast<const half8_t*>(kp + off);
+      qv = *reinterpret_cast<const half8_t*>(qp + off);
+    }
+    *reinterpret_cast<half8_t*>(&sm.u.in.K[row * KS + c8]) = kv;
+    *reinterpret_cast<half8_t*>(&sm.u.in.Q[row * KS + c8]) = qv;
+  }
+  __syncthreads();
+
+  // ---- per-token inverse norms: 4 threads per row, 32 elements each
+  {
+    const int row = tid >> 2, part = tid & 3;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float kx = (float)sm.u.in.K[row * KS + part * 32 + j];
+      const float qx = (float)sm.u.in.Q[row * KS + part * 32 + j];
+      sk = fmaf(kx, kx, sk);
+      sq = fmaf(qx, qx, sq);
+    }
+    sk = group_sum<4>(sk);
+    sq = group_sum<4>(sq);
+    if (part == 0) {
+      const float rk = rsqrtf(sk + kNormEps);
+      const float rq = rsqrtf(sq + kNormEps) * p.scale;
+      sm.rk[row] = rk;
+      sm.rq[row] = rq;
+      float* nrm = w.nrm + ((size_t)slot * p.Hk + g) * 2 * C;
+      nrm[row] = rk;
+      nrm[C + row] = rq;
+    }
+  }
+
+  // ---- Gram matrices K K^T and Q K^T, rows 16*wave .. +15, column blocks <= wave
+  float4_t kk[4], qk[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    kk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    qk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (nb <= wave) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int col = 32 * ks + 8 * (lane >> 4);
+        const half8_t ak = lds8(&sm.u.in.K[(16 * wave + (lane & 15)) * KS + col]);
+        const half8_t aq = lds8(&sm.u.in.Q[(16 * wave + (lane & 15)) * KS + col]);
+        const half8_t bk = lds8(&sm.u.in.K[(16 * nb + (lane & 15)) * KS + col]);
+        kk[nb] = mfma_f16(ak, bk, kk[nb]);
+        qk[nb] = mfma_f16(aq, bk, qk[nb]);
+      }
+    }
+  }
+  __syncthreads();   // K, Q tiles are dead from here; their LDS becomes A
+
+  const float* a_in = p.a;
+  const float* b_in = p.b;
+  for (int base = 0; base < p.group; base += 4) {
+    const int nb_heads = min(4, p.group - base);
+    // ---- gates and in-chunk cumulative log decay: wave hv handles head base + hv
+    if (wave < nb_heads) {
+      const int h = g * p.group + base + wave;
+      const int t = lane;
+      float la = 0.f, be = 0.f;
+      if (t < L) {
+        const float x = a_in[(size_t)(t0 + t) * p.Hv + h] + p.dt_bias[h];
+        la = -expf(p.A_log[h]) * softplus_f(x);
+        be = sigmoid_f(b_in[(size_t)(t0 + t) * p.Hv + h]);
+      }
+      // inclusive prefix sum over the 64 lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(la, d, 64);
+        if (t >= d) la += y;
+      }
+      sm.g[wave][t] = la;
+      sm.beta[wave][t] = be;
+      float* gb = w.gb + ((size_t)slot * p.Hv + h) * 2 * C;
+      gb[t] = la;
+      gb[C + t] = be;
+    }
+    __syncthreads();
+
+    // ---- A (fp32, LDS) and P (fp16, workspace) from the Gram accumulators
+    for (int hv = 0; hv < nb_heads; ++hv) {
+      const int h = g * p.group + base + hv;
+      _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int i = 16 * nb + (lane & 15);            // column (key token)
+        const float gi = sm.g[hv][i], rki = sm.rk[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * wave + 4 * (lane >> 4) + e;  // row (query / later token)
+          const float gr = sm.g[hv][r];
+          float av = 0.f, pv = 0.f;
+          if (nb <= wave) {
+            const float dec = expf(fminf(gr - gi, 0.f));
+            if (i < r) av = sm.beta[hv][r] * dec * sm.rk[r] * rki * kk[nb][e];
+            if (i <= r) pv = dec * sm.rq[r] * rki * qk[nb][e];
+          }
+          sm.u.A[hv][r * AS + i] = av;
+          Pw[r * C + i] = (_Float16)pv;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- T = (I + A)^-1 by forward substitution, one column per lane; wave hv = head
+    if (wave < nb_heads) {
+      const int h = g * p.group + base + wave;
+      const float* A = sm.u.A[wave];
+      const int j = lane;
+      float x[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) x[r] = 0.f;
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int i = 0; i < r; i += 4) {
+          const float4_t a4 = *reinterpret_cast<const float4_t*>(&A[r * AS + i]);
+          s0 = fmaf(a4.x, x[i], s0);
+          s1 = fmaf(a4.y, x[i + 1], s1);
+          s2 = fmaf(a4.z, x[i + 2], s2);
+          s3 = fmaf(a4.w, x[i + 3], s3);
+        }
+        x[r] = (r == j ? 1.f : 0.f) - ((s0 + s1) + (s2 + s3));
+      }
+      _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * C * C;
+#pragma unroll
+      for (int r = 0; r < C; ++r) Tw[r * C + j] = (_Float16)x[r];
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------
+// gdn_chunk_scan: one workgroup per (request, value head, Dv tile of TV rows)
+// ----------------------------------------------------------------------------
+template <int TV>
+struct ScanSmem {
+  _Float16 K[C * KS];      // raw k of the chunk, token-major
+  _Float16 Q[C * KS];      // raw q of the chunk
+  _Float16 T[C * TS];
+  _Float16 P[C * TS];
+  _Float16 V[C * (TV + 8)];
+  _Float16 S16[TV * KS];   // fp16 copy of the state tile, [dv][dk]
+  _Float16 Zt[TV * TS];    // Z^T  [dv][token]
+  _Float16 Ut[TV * TS];    // U^T  [dv][token]
+  _Float16 Uk[TV * TS];    // (diag(e^{gL-g} rk) U)^T
+  float g[C], beta[C], rk[C], rq[C];
+};
+
+// Registers holding the next chunk's inputs while the current one computes.
+template <int TV>
+struct Prefetch {
+  half8_t k[4], q[4], t[2], pm[2];
+  half8_t v;
+  float vec;
+};
+
+template <int TV>
+__device__ __forceinline__ void prefetch_chunk(const ChunkArgs& p, const Ws& w, int slot, int t0,
+                                               int L, int h, int g, int d0, Prefetch<TV>& f) {
+  const int tid = threadIdx.x;
+  const _Float16* kp = static_cast<const _Float16*>(p.k);
+  const _Float16* qp = static_cast<const _Float16*>(p.q);
+  const _Float16* vp = static_cast<const _Float16*>(p.v);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + kThreads * it;
+    const int row = idx >> 4, c8 = (idx & 15) * 8;
+    f.k[it] = half8_t{};
+    f.q[it] = half8_t{};
+    if (row < L) {
+      const size_t off = ((size_t)(t0 + row) * p.Hk + g) * D + c8;
+      f.k[it] = *reinterpret_cast<const half8_t*>(kp + off);
+      f.q[it] = *reinterpret_cast<const half8_t*>(qp + off);
+    }
+  }
+  const _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * C * C;
+  const _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + kThreads * it;       // 512 pieces of 8 halves
+    f.t[it] = *reinterpret_cast<const half8_t*>(Tw + idx * 8);
+    f.pm[it] = *reinterpret_cast<const half8_t*>(Pw + idx * 8);
+  }
+  {
+    constexpr int PER_ROW = TV / 8;
+    f.v = half8_t{};
+    if (tid < C * PER_ROW) {
+      const int row = tid / PER_ROW, c8 = (tid % PER_ROW) * 8;
+      if (row < L) f.v = *reinterpret_cast<const half8_t*>(vp + ((size_t)(t0 + row) * p.Hv + h) * D + d0 + c8);
+    }
+  }
+  {
+    const int which = tid >> 6, t = tid & 63;  // 0: g, 1: beta, 2: rk, 3: rq
+    const float* src = which < 2 ? w.gb + ((size_t)slot * p.Hv + h) * 2 * C + which * C
+                                 : w.nrm + ((size_t)slot * p.Hk + g) * 2 * C + (which - 2) * C;
+    f.vec = src[t];
+  }
+}
+
+template <int TV>
+__device__ __forceinline__ void stage_chunk(ScanSmem<TV>& sm, const Prefetch<TV>& f) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + kThreads * it;
+    const int row = idx >> 4, c8 = (idx & 15) * 8;
+    *reinterpret_cast<half8_t*>(&sm.K[row * KS + c8]) = f.k[it];
+    *reinterpret_cast<half8_t*>(&sm.Q[row * KS + c8]) = f.q[it];
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + kThreads * it;
+    const int row = idx >> 3, c8 = (idx & 7) * 8;
+    *reinterpret_cast<half8_t*>(&sm.T[row * TS + c8]) = f.t[it];
+    *reinterpret_cast<half8_t*>(&sm.P[row * TS + c8]) = f.pm[it];
+  }
+  {
+    constexpr int PER_ROW = TV / 8;
+    if (tid < C * PER_ROW) {
+      const int row = tid / PER_ROW, c8 = (tid % PER_ROW) * 8;
+      *reinterpret_cast<half8_t*>(&sm.V[row * (TV + 8) + c8]) = f.v;
+    }
+  }
+  {
+    const int which = tid >> 6, t = tid & 63;
+    float* dst = which == 0 ? sm.g : which == 1 ? sm.beta : which == 2 ? sm.rk : sm.rq;
+    dst[t] = f.vec;
+  }
+}
+
+template <int TV>
+__global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_items) {
+  constexpr int NT = D / TV;        // Dv tiles per head
+  constexpr int MB = TV / 16;       // 16-row blocks of the tile
+  __shared__ ScanSmem<TV> sm;
+
+  // XCD-aware order: consecutive items (same request and key head) share an XCD's L2
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int tile = item % NT;
+  int rest = item / NT;
+  const int hv = rest % p.group;
+  rest /= p.group;
+  const int g = rest % p.Hk;
+  const int req = rest / p.Hk;
+  const int h = g * p.group + hv;
+  const int d0 = tile * TV;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, q4 = lane >> 4;
+
+  const int beg = clamp_cu(p.cu_seqlens, req, p.N);
+  const int end = max(clamp_cu(p.cu_seqlens, req + 1, p.N), beg);
+  const int slot0 = w.chunk_start[req];
+  int nch = (end - beg + C - 1) / C;
+  nch = max(0, min(nch, p.max_chunks - slot0));
+
+  // ---- state tile: wave owns dk columns 32*wave .. +31; S[mb][nb] is a 16x16 block
+  float4_t S[MB][2];
+  const size_t head_off = ((size_t)req * p.Hv + h) * D * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dv = d0 + 16 * mb + 4 * q4 + e, dk = 32 * wave + 16 * nb + l16;
+        S[mb][nb][e] = p.initial_state != nullptr ? p.initial_state[head_off + (size_t)dv * D + dk] : 0.f;
+      }
+
+  Prefetch<TV> f;
+  if (nch > 0) prefetch_chunk<TV>(p, w, slot0, beg, min(C, end - beg), h, g, d0, f);
+
+  _Float16* op = static_cast<_Float16*>(p.output);
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = beg + C * c;
+    const int L = min(C, end - t0);
+    // ---- chunk inputs and the fp16 state copy into LDS
+    stage_chunk<TV>(sm, f);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sm.S16[(16 * mb + 4 * q4 + e) * KS + 32 * wave + 16 * nb + l16] = (_Float16)S[mb][nb][e];
+    __syncthreads();
+    if (c + 1 < nch) {
+      const int tn = t0 + C;
+      prefetch_chunk<TV>(p, w, slot0 + c + 1, tn, min(C, end - tn), h, g, d0, f);
+    }
+
+    // ---- X = K S0^T and Y = Q S0^T for tokens 16*wave .. +15
+    float4_t X[MB], Y[MB];
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
+      X[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      Y[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int col = 32 * ks + 8 * q4;
+        const half8_t ak = lds8(&sm.K[(16 * wave + l16) * KS + col]);
+        const half8_t aq = lds8(&sm.Q[(16 * wave + l16) * KS + col]);
+        const half8_t bs = lds8(&sm.S16[(16 * nb + l16) * KS + col]);
+        X[nb] = mfma_f16(ak, bs, X[nb]);
+        Y[nb] = mfma_f16(aq, bs, Y[nb]);
+      }
+    }
+    // ---- Z = beta (V - e^g rk X) -> Zt[dv][token]
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
+      half4_t z4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * wave + 4 * q4 + e;
+        const int dv = 16 * nb + l16;
+        const float vv = (float)sm.V[t * (TV + 8) + dv];
+        z4[e] = (_Float16)(sm.beta[t] * (vv - expf(sm.g[t]) * sm.rk[t] * X[nb][e]));
+      }
+      *reinterpret_cast<half4_t*>(&sm.Zt[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = z4;
+    }
+    __syncthreads();
+
+    // ---- U = T Z (T is lower triangular: tokens beyond this row block add nothing)
+    const float gL = sm.g[C - 1];
+    float4_t U[MB];
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
+      U[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (32 * ks <= 16 * wave + 15) {
+          const int col = 32 * ks + 8 * q4;
+          const half8_t at = lds8(&sm.T[(16 * wave + l16) * TS + col]);
+          const half8_t bz = lds8(&sm.Zt[(16 * nb + l16) * TS + col]);
+          U[nb] = mfma_f16(at, bz, U[nb]);
+        }
+      }
+      half4_t u4, w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * wave + 4 * q4 + e;
+        u4[e] = (_Float16)U[nb][e];
+        w4[e] = (_Float16)(expf(gL - sm.g[t]) * sm.rk[t] * U[nb][e]);
+      }
+      *reinterpret_cast<half4_t*>(&sm.Ut[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = u4;
+      *reinterpret_cast<half4_t*>(&sm.Uk[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = w4;
+    }
+    __syncthreads();
+
+    // ---- O = diag(e^g rq) Y + P U  -> output rows < L
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
+      float4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * wave + 4 * q4 + e;
+        o[e] = expf(sm.g[t]) * sm.rq[t] * Y[nb][e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (32 * ks <= 16 * wave + 15) {
+          const int col = 32 * ks + 8 * q4;
+          const half8_t ap = lds8(&sm.P[(16 * wave + l16) * TS + col]);
+          const half8_t bu = lds8(&sm.Ut[(16 * nb + l16) * TS + col]);
+          o = mfma_f16(ap, bu, o);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * wave + 4 * q4 + e;
+        if (t < L) op[((size_t)(t0 + t) * p.Hv + h) * D + d0 + 16 * nb + l16] = (_Float16)o[e];
+      }
+    }
+
+    // ---- S = e^{gL} S + Uk^T K  (wave: dk columns 32*wave .. +31)
+    const float decay_L = expf(gL);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        S[mb][nb] *= decay_L;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int tk = 32 * ks + 8 * q4;
+          const half8_t au = lds8(&sm.Uk[(16 * mb + l16) * TS + tk]);
+          const int dk = 32 * wave + 16 * nb + l16;
+          half8_t bk;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bk[j] = sm.K[(tk + j) * KS + dk];
+          S[mb][nb] = mfma_f16(au, bk, S[mb][nb]);
+        }
+      }
+    __syncthreads();   // all LDS reads of this chunk are done before the next stage
+  }
+
+  if (p.final_state != nullptr) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dv = d0 + 16 * mb + 4 * q4 + e, dk = 32 * wave + 16 * nb + l16;
+          p.final_state[head_off + (size_t)dv * D + dk] = S[mb][nb][e];
+        }
+  }
+}
+
+constexpr int kScanTile = 32;
+
+size_t chunk_workspace_bytes(int64_t chunk_slots, int R, int Hk, int Hv) {
+  return ws_bytes(chunk_slots, R, Hk, Hv);
+}
+
+hipError_t launch_chunk(const ChunkArgs& p, int io_dtype, hipStream_t stream) {
+  if (io_dtype != 1) return hipErrorInvalidValue;     // fp16 I/O only
+  if (p.R == 0) return hipSuccess;
+  const Ws w = ws_layout(p.workspace, p.max_chunks, p.R, p.Hk, p.Hv);
+  hipLaunchKernelGGL(gdn_chunk_index, dim3(1), dim3(kThreads), 0, stream, p, w);
+  if (p.max_chunks > 0)
+    hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)p.max_chunks, (unsigned)p.Hk), dim3(kThreads),
+                       0, stream, p, w);
+  const int n_items = p.R * p.Hv * (D / kScanTile);
+  const int grid = (n_items + 7) / 8 * 8;
+  hipLaunchKernelGGL(gdn_chunk_scan<kScanTile>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p, w,
+                     n_items);
+  return hipGetLastError();
+}
 
 }  // namespace gdn

@@ -71,10 +71,12 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
 
-/* Kernel path. AUTO takes RECURRENT when a capsule is requested, when Dk or Dv
- * is not 128, or when the longest request (from cu_seqlens_host, else the mean
- * N / R) is at most 32 tokens; otherwise CHUNK. A forced plan overrides this
- * ("forced-plan behavior", first page, Dependency). */
+/* Kernel path. CHUNK (fp16 MFMA, chunk 64) needs fp16 I/O and Dk = Dv = 128 and
+ * writes no capsule. AUTO takes RECURRENT when a capsule is requested, when the
+ * CHUNK conditions do not hold, or when the longest request (from
+ * cu_seqlens_host, else the mean N / R) is at most 32 tokens; otherwise CHUNK.
+ * A forced plan overrides this ("forced-plan behavior", first page, Dependency);
+ * forcing CHUNK where it cannot run is GDN_ERR_PLAN. */
 typedef enum gdn_plan { GDN_PLAN_AUTO = 0, GDN_PLAN_RECURRENT = 1, GDN_PLAN_CHUNK = 2 } gdn_plan;
 
 /* Only the gated delta rule is implemented ("update-rule input validation",

@@ -103,6 +103,27 @@ def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=No
                          capture_count=capture_count, state_update_init=init)
 
 
+def sample_heads_inputs(inp, heads):
+    """The sub-problem of the given value heads only, with each head's key head
+    repeated (grouped keys equal repeat-interleaved keys; pinned by the oracle's
+    GQA check), so the oracle can run full-length sequences on a few heads."""
+    heads = np.asarray(heads)
+    G = inp["Hv"] // inp["Hk"]
+    kh = heads // G
+    sub = dict(inp)
+    sub["q"] = inp["q"][:, kh]
+    sub["k"] = inp["k"][:, kh]
+    sub["v"] = inp["v"][:, heads]
+    sub["a"] = np.ascontiguousarray(inp["a"][:, heads])
+    sub["b"] = np.ascontiguousarray(inp["b"][:, heads])
+    sub["A_log"] = inp["A_log"][heads]
+    sub["dt_bias"] = inp["dt_bias"][heads]
+    if inp["initial_state"] is not None:
+        sub["initial_state"] = inp["initial_state"][:, heads]
+    sub["Hk"] = sub["Hv"] = len(heads)
+    return sub
+
+
 def assert_parity(io_dtype, out, ref_out, fin=None, ref_fin=None, what=""):
     if io_dtype == "f32":
         e_o = rel_max(out, ref_out)
