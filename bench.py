@@ -12,7 +12,10 @@ several state banks (>= 512 MiB in total), so every step reads cold state.
 Prints one JSON line: tokens/s, ms per step, the dominant kernel's roofline
 (algorithmic bytes / its average duration from HIP events on the launch
 stream, against the 8 TB/s HBM peak) and the float64 oracle timed on this
-host's cores on a bounded sample of the same workload.
+host's cores on a bounded sample of the same workload. The line also carries,
+under "workloads", the same measurements for the operator's other workloads:
+speculative verify + replay (HBM roofline) and the ragged and long prefills
+(fp16 MFMA roofline); --workload NAME times just one of them.
 """
 from __future__ import annotations
 
@@ -29,13 +32,35 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "GDN tokens/s + achieved HBM GB/s (decode/replay), MFMA % (prefill)"
 BANK_TARGET_BYTES = 512 * 2 ** 20
 
-# HBM traffic of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# runs of this workload (KiB per dispatch, scaled by the copy-kernel calibration).
-# None until measured for the current kernel.
-MEASURED_TRAFFIC = {}
+# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs of this workload (KiB per dispatch), each scaled by what the same
+# counter reads for the 128 MiB hbm_copy workload (FETCH_SIZE reads 65547.6 KiB
+# for 131072 KiB copied: factor 1.9996; WRITE_SIZE is exact: factor 1.0000).
+# Keyed by the hash of the kernel's sources: a changed kernel reports null until
+# its counters are taken again.
+MEASURED_TRAFFIC = {
+    "gdn_decode": {"sources": ["gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip",
+                               "gateddeltanet_recurrence_amd/csrc/gdn_common.h"],
+                   "sha256_16": "28fe2b71996c468d", "fetch_kib": 66993.0, "write_kib": 131611.7,
+                   "bytes": 271947764},
+}
+
+
+def measured_traffic(kernel):
+    """Calibrated HBM bytes per launch of `kernel`, or None if its sources changed."""
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(kernel)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if h.hexdigest()[:16] == rec["sha256_16"] else None
 
 
 def _log(msg):
@@ -94,7 +119,7 @@ def run_decode(args, torch, gdn):
     ms_step = total_ms / args.steps
     nbytes = decode_bytes(inp)
     achieved = nbytes / (ms_step * 1e-3) / 1e9
-    traffic = MEASURED_TRAFFIC.get("gdn_decode")
+    traffic = measured_traffic("gdn_decode")
     line = {
         "metric": METRIC, "value": N / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
@@ -109,6 +134,138 @@ def run_decode(args, torch, gdn):
                      "avg_kernel_us": ms_step * 1e3},
     }
     return line, inp
+
+
+def _time_steps(torch, step, steps, warmup):
+    """Average ms per step of `step(i)` over `steps` calls, HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def run_verify_replay(args, torch, gdn):
+    """Speculative verify (capsule, committed bank read-only) then replay of the
+    accepted prefix into the inactive bank, per step."""
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs("spec_verify_replay")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R, cap = len(inp["cu_seqlens"]) - 1, inp["capacity"]
+    W = gdn.capsule_width(Hk, Hv, Dk, Dv)
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    acc_host = inp["accepted"]
+    acc = _dev(acc_host, torch)
+    state_bytes = R * Hv * Dv * Dk * 4
+    n_banks = max(4, 2 * -(-(3 * BANK_TARGET_BYTES // 2) // (2 * state_bytes)))
+    init = _dev(inp["initial_state"], torch)
+    banks = [init.clone() for _ in range(n_banks)]
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    capsule = torch.empty((R, cap, W), dtype=torch.float32, device="cuda")
+    host_cu = inp["cu_seqlens"]
+
+    def step(i):
+        committed = banks[(2 * i) % n_banks]
+        inactive = banks[(2 * i + 1) % n_banks]
+        gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=committed,
+                        state_update=capsule, state_update_capacity=cap, cu_seqlens_host=host_cu,
+                        plan=gdn.PLAN_RECURRENT)
+        gdn.gdn_replay(committed, capsule, acc, inactive, num_k_heads=Hk, state_update_capacity=cap,
+                       accepted_host=acc_host)
+
+    _log(f"verify+replay: R={R} T=4 Hv={Hv} banks={n_banks}")
+    ms = _time_steps(torch, step, args.steps, args.warmup)
+    io = 2
+    verify_bytes = (state_bytes + R * cap * W * 4 + 2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io
+                    + 2 * N * Hv * 4 + 2 * Hv * 4 + (R + 1) * 4)
+    replay_bytes = 2 * state_bytes + int(acc_host.sum()) * W * 4 + R * 4
+    nbytes = verify_bytes + replay_bytes
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"requests": R, "draft_tokens": 4, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                       "capacity": cap, "accepted": acc_host.tolist(), "state_banks": n_banks},
+            "roofline": {"bound": "hbm", "kernel": "gdn_capsule+gdn_replay", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_step": nbytes,
+                         "verify_bytes": verify_bytes, "replay_bytes": replay_bytes}}
+
+
+def prefill_flops(lengths, Hk, Hv, D, chunk=64):
+    """Algorithmic MFMA flops of the chunked prefill: per chunk of L tokens,
+    Hk * 4 L^2 D (Q K^T and K K^T per key head) + Hv * (6 L^2 D + 6 L D^2)
+    (the WY products and the three state contractions per value head)."""
+    total = 0
+    for n in lengths:
+        for c0 in range(0, int(n), chunk):
+            L = min(chunk, int(n) - c0)
+            total += Hk * 4 * L * L * D + Hv * (6 * L * L * D + 6 * L * D * D)
+    return total
+
+
+def run_prefill(args, torch, gdn, name):
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs(name)
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R = len(inp["cu_seqlens"]) - 1
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    init = _dev(inp["initial_state"], torch)
+    fin = torch.empty_like(init)
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    host_cu = inp["cu_seqlens"]
+    nws = gdn.gdn_forward_workspace_bytes(N, R, Hk, Hv, Dk, Dv, gdn.GDN_F16, cu_seqlens_host=host_cu)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    plan = gdn.gdn_resolve_plan(N, R, Hk, Hv, Dk, Dv, gdn.GDN_F16, cu_seqlens_host=host_cu)
+
+    def step(i):
+        gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=init, final_state=fin,
+                        cu_seqlens_host=host_cu, workspace=ws)
+
+    steps = max(5, args.steps // 25)
+    warm = max(2, args.warmup // 10)
+    _log(f"{name}: N={N} R={R} Hv={Hv} plan={'chunk' if plan == gdn.PLAN_CHUNK else 'recurrent'} steps={steps}")
+    ms = _time_steps(torch, step, steps, warm)
+    flops = prefill_flops(inp["lengths"], Hk, Hv, Dk)
+    io = 2
+    nbytes = (2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io + 2 * N * Hv * 4 + 2 * Hv * 4
+              + (R + 1) * 4 + 2 * R * Hv * Dv * Dk * 4)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"tokens": N, "requests": R, "lengths": [int(x) for x in inp["lengths"]],
+                       "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "chunk": 64, "workspace_bytes": nws},
+            "roofline": {"bound": "mfma", "kernel": "gdn_chunk_index+gdn_chunk_prep+gdn_chunk_scan",
+                         "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                         "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": nbytes,
+                         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
+def run_hbm_copy(args, torch):
+    """Reference stream: device-to-device copies of 128 MiB fp32 buffers rotated over
+    banks (read 128 MiB + write 128 MiB per step). Its known byte count calibrates
+    the FETCH_SIZE / WRITE_SIZE counters, and its rate is the achievable HBM rate of
+    a plain read+write stream."""
+    n = 32 * 2 ** 20
+    banks = max(2, -(-BANK_TARGET_BYTES // (n * 4)))
+    src = [torch.randn(n, device="cuda") for _ in range(banks)]
+    dst = [torch.empty_like(x) for x in src]
+    ms = _time_steps(torch, lambda i: dst[i % banks].copy_(src[i % banks]), args.steps, args.warmup)
+    nbytes = 2 * n * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"value": gbs, "unit": "GB/s", "ms_per_step": ms, "bytes_per_step": nbytes,
+            "config": {"buffer_bytes": n * 4, "banks": banks},
+            "roofline": {"bound": "hbm", "kernel": "copy", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
 
 
 def cpu_baseline_decode(inp, seconds):
@@ -139,7 +296,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="batched_decode", choices=["batched_decode"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
+                             "hbm_copy"],
+                    help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="length of the oracle CPU-baseline sample (0 skips it)")
     args = ap.parse_args()
@@ -155,7 +315,21 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     gdn.lib()
+    if args.workload not in ("all", "batched_decode"):
+        fn = {"spec_verify_replay": lambda: run_verify_replay(args, torch, gdn),
+              "ragged_prefill": lambda: run_prefill(args, torch, gdn, "ragged_prefill"),
+              "long_prefill": lambda: run_prefill(args, torch, gdn, "long_prefill"),
+              "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
+        res = fn()
+        print(json.dumps({"metric": METRIC, "workload": args.workload, **res}), flush=True)
+        return
     line, inp = run_decode(args, torch, gdn)
+    if args.workload == "all":
+        line["workloads"] = {
+            "spec_verify_replay": run_verify_replay(args, torch, gdn),
+            "ragged_prefill": run_prefill(args, torch, gdn, "ragged_prefill"),
+            "long_prefill": run_prefill(args, torch, gdn, "long_prefill"),
+        }
     if args.cpu_seconds > 0:
         _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)

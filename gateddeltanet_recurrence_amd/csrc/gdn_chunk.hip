@@ -46,14 +46,17 @@ __device__ __forceinline__ half8_t lds8(const _Float16* p) {
 }
 
 // Workspace layout: chunk offsets, then per (slot, value head) T and P (fp16
-// 64x64 row-major), per (slot, value head) [g; beta] and per (slot, key head)
-// [rk; rq] (fp32, 64 each).
+// 64x64 row-major) and the per-token factors the scan applies (fp32 rows of 64):
+//   kVecZ  e^{g_t} rk_t            kVecBeta beta_t
+//   kVecO  e^{g_t} rq_t            kVecU    e^{g_L - g_t} rk_t
+//   kVecGamma  element 0: e^{g_L}, the decay of the whole chunk
+constexpr int kVecZ = 0, kVecBeta = 1, kVecO = 2, kVecU = 3, kVecGamma = 4, kVecRows = 5;
+
 struct Ws {
   int32_t* chunk_start;
   _Float16* T;
   _Float16* P;
-  float* gb;
-  float* nrm;
+  float* vec;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -68,15 +71,14 @@ __host__ __device__ inline Ws ws_layout(void* base, int64_t slots, int R, int Hk
   off += align256((size_t)slots * Hv * C * C * 2);
   w.P = reinterpret_cast<_Float16*>(p + off);
   off += align256((size_t)slots * Hv * C * C * 2);
-  w.gb = reinterpret_cast<float*>(p + off);
-  off += align256((size_t)slots * Hv * 2 * C * 4);
-  w.nrm = reinterpret_cast<float*>(p + off);
+  w.vec = reinterpret_cast<float*>(p + off);
   return w;
 }
 
 __host__ inline size_t ws_bytes(int64_t slots, int R, int Hk, int Hv) {
+  (void)Hk;
   return align256((size_t)(R + 1) * 4) + 2 * align256((size_t)slots * Hv * C * C * 2) +
-         align256((size_t)slots * Hv * 2 * C * 4) + align256((size_t)slots * Hk * 2 * C * 4);
+         align256((size_t)slots * Hv * kVecRows * C * 4);
 }
 
 __device__ __forceinline__ int clamp_cu(const int32_t* cu, int i, int N) {
@@ -140,18 +142,66 @@ __device__ __forceinline__ bool locate_chunk(const ChunkArgs& p, const Ws& w, in
 
 // ----------------------------------------------------------------------------
 // gdn_chunk_prep: one workgroup per (chunk slot, key head)
+//
+// T = (I + A)^-1 of every value head is built blockwise from 16x16 blocks:
+// the four diagonal blocks by forward substitution (one lane per column), then
+// the blocks below the diagonal column by column,
+//   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj,
+// on fp32 MFMA into a buffer of its own (A stays intact). Block columns are
+// independent of each other, so two waves share a head: one sweeps column 0,
+// the other columns 1 and 2; two heads are in flight at once.
 // ----------------------------------------------------------------------------
+constexpr int kHeadsPerPass = 2;
+
 struct PrepSmem {
   union {
     struct {
       _Float16 K[C * KS];
       _Float16 Q[C * KS];
     } in;
-    float A[4][C * AS];        // A of up to four value heads (after the Gram step)
+    struct {
+      float A[kHeadsPerPass][C * AS];   // A of the heads of one pass
+      float T[kHeadsPerPass][C * AS];   // their T (blocks on and below the diagonal)
+    } m;
   } u;
+  float wtmp[4][16 * 17];             // per-wave 16x16 staging for MFMA operands
   float rk[C], rq[C];
-  float g[4][C], beta[4][C];
+  float g[kHeadsPerPass][C], beta[kHeadsPerPass][C];
 };
+
+__device__ __forceinline__ float4_t mfma_f32(float a, float b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Block (ib, jb) below the diagonal of T; T already holds column jb's blocks
+// above ib and the diagonal blocks.
+__device__ __forceinline__ void t_offdiag_block(const float* A, float* T, float* wt, int ib, int jb,
+                                                int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  float4_t W = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = jb; kb < ib; ++kb) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float a = A[(16 * ib + m) * AS + 16 * kb + 4 * s4 + kq];
+      const float b = T[(16 * kb + 4 * s4 + kq) * AS + 16 * jb + m];
+      W = mfma_f32(a, b, W);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) wt[(4 * kq + e) * 17 + m] = W[e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  float4_t Tb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const float a = T[(16 * ib + m) * AS + 16 * ib + 4 * s4 + kq];
+    const float b = wt[(4 * s4 + kq) * 17 + m];
+    Tb = mfma_f32(a, b, Tb);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) T[(16 * ib + 4 * kq + e) * AS + 16 * jb + m] = -Tb[e];
+}
 
 __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
   __shared__ PrepSmem sm;
@@ -163,7 +213,9 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
   const _Float16* kp = static_cast<const _Float16*>(p.k);
   const _Float16* qp = static_cast<const _Float16*>(p.q);
 
-  // ---- K, Q chunk tiles into LDS (rows >= L zero)
+  // ---- K, Q chunk tiles into LDS (rows >= L zero); 16 lanes per row, so the
+  // per-token sums of squares reduce across those 16 lanes
+  float ssk[4], ssq[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int idx = tid + kThreads * it;    // 1024 16-byte pieces per tile
@@ -176,32 +228,27 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
     }
     *reinterpret_cast<half8_t*>(&sm.u.in.K[row * KS + c8]) = kv;
     *reinterpret_cast<half8_t*>(&sm.u.in.Q[row * KS + c8]) = qv;
-  }
-  __syncthreads();
-
-  // ---- per-token inverse norms: 4 threads per row, 32 elements each
-  {
-    const int row = tid >> 2, part = tid & 3;
     float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float kx = (float)sm.u.in.K[row * KS + part * 32 + j];
-      const float qx = (float)sm.u.in.Q[row * KS + part * 32 + j];
-      sk = fmaf(kx, kx, sk);
-      sq = fmaf(qx, qx, sq);
+    for (int j = 0; j < 8; ++j) {
+      sk = fmaf((float)kv[j], (float)kv[j], sk);
+      sq = fmaf((float)qv[j], (float)qv[j], sq);
     }
-    sk = group_sum<4>(sk);
-    sq = group_sum<4>(sq);
-    if (part == 0) {
-      const float rk = rsqrtf(sk + kNormEps);
-      const float rq = rsqrtf(sq + kNormEps) * p.scale;
+    ssk[it] = group_sum<16>(sk);
+    ssq[it] = group_sum<16>(sq);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + kThreads * it;
+    if ((idx & 15) == 0) {
+      const int row = idx >> 4;
+      const float rk = rsqrtf(ssk[it] + kNormEps);
+      const float rq = rsqrtf(ssq[it] + kNormEps) * p.scale;
       sm.rk[row] = rk;
       sm.rq[row] = rq;
-      float* nrm = w.nrm + ((size_t)slot * p.Hk + g) * 2 * C;
-      nrm[row] = rk;
-      nrm[C + row] = rq;
     }
   }
+  lds_barrier();
 
   // ---- Gram matrices K K^T and Q K^T, rows 16*wave .. +15, column blocks <= wave
   float4_t kk[4], qk[4];
@@ -221,35 +268,36 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
       }
     }
   }
-  __syncthreads();   // K, Q tiles are dead from here; their LDS becomes A
+  lds_barrier();   // K, Q tiles are dead from here; their LDS becomes A
 
-  const float* a_in = p.a;
-  const float* b_in = p.b;
-  for (int base = 0; base < p.group; base += 4) {
-    const int nb_heads = min(4, p.group - base);
+  for (int base = 0; base < p.group; base += kHeadsPerPass) {
+    const int nb_heads = min(kHeadsPerPass, p.group - base);
     // ---- gates and in-chunk cumulative log decay: wave hv handles head base + hv
     if (wave < nb_heads) {
       const int h = g * p.group + base + wave;
       const int t = lane;
       float la = 0.f, be = 0.f;
       if (t < L) {
-        const float x = a_in[(size_t)(t0 + t) * p.Hv + h] + p.dt_bias[h];
+        const float x = p.a[(size_t)(t0 + t) * p.Hv + h] + p.dt_bias[h];
         la = -expf(p.A_log[h]) * softplus_f(x);
-        be = sigmoid_f(b_in[(size_t)(t0 + t) * p.Hv + h]);
+        be = sigmoid_f(p.b[(size_t)(t0 + t) * p.Hv + h]);
       }
-      // inclusive prefix sum over the 64 lanes
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
+      for (int d = 1; d < 64; d <<= 1) {      // inclusive prefix sum over the 64 lanes
         const float y = __shfl_up(la, d, 64);
         if (t >= d) la += y;
       }
       sm.g[wave][t] = la;
       sm.beta[wave][t] = be;
-      float* gb = w.gb + ((size_t)slot * p.Hv + h) * 2 * C;
-      gb[t] = la;
-      gb[C + t] = be;
+      const float gL = __shfl(la, C - 1, 64);
+      float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
+      vec[kVecZ * C + t] = expf(la) * sm.rk[t];
+      vec[kVecBeta * C + t] = be;
+      vec[kVecO * C + t] = expf(la) * sm.rq[t];
+      vec[kVecU * C + t] = expf(gL - la) * sm.rk[t];
+      vec[kVecGamma * C + t] = expf(gL);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- A (fp32, LDS) and P (fp16, workspace) from the Gram accumulators
     for (int hv = 0; hv < nb_heads; ++hv) {
@@ -257,11 +305,11 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
       _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int i = 16 * nb + (lane & 15);            // column (key token)
+        const int i = 16 * nb + (lane & 15);            // column (earlier token)
         const float gi = sm.g[hv][i], rki = sm.rk[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * wave + 4 * (lane >> 4) + e;  // row (query / later token)
+          const int r = 16 * wave + 4 * (lane >> 4) + e;  // row (later token)
           const float gr = sm.g[hv][r];
           float av = 0.f, pv = 0.f;
           if (nb <= wave) {
@@ -269,27 +317,29 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
             if (i < r) av = sm.beta[hv][r] * dec * sm.rk[r] * rki * kk[nb][e];
             if (i <= r) pv = dec * sm.rq[r] * rki * qk[nb][e];
           }
-          sm.u.A[hv][r * AS + i] = av;
+          sm.u.m.A[hv][r * AS + i] = av;
           Pw[r * C + i] = (_Float16)pv;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- T = (I + A)^-1 by forward substitution, one column per lane; wave hv = head
-    if (wave < nb_heads) {
-      const int h = g * p.group + base + wave;
-      const float* A = sm.u.A[wave];
-      const int j = lane;
-      float x[C];
+    // ---- T, step 1: the four diagonal 16x16 blocks (wave 2*hv, lane = 16*block + column)
+    const int hv = wave >> 1, half_w = wave & 1;
+    if (hv < nb_heads && half_w == 0) {
+      const float* A = sm.u.m.A[hv];
+      float* T = sm.u.m.T[hv];
+      const int blk = lane >> 4, j = lane & 15;
+      float x[16];
 #pragma unroll
-      for (int r = 0; r < C; ++r) x[r] = 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
+      for (int r = 0; r < 16; ++r) {
+        const float* arow = &A[(16 * blk + r) * AS + 16 * blk];
         float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
         for (int i = 0; i < r; i += 4) {
-          const float4_t a4 = *reinterpret_cast<const float4_t*>(&A[r * AS + i]);
+          const float4_t a4 = *reinterpret_cast<const float4_t*>(&arow[i]);
           s0 = fmaf(a4.x, x[i], s0);
           s1 = fmaf(a4.y, x[i + 1], s1);
           s2 = fmaf(a4.z, x[i + 2], s2);
@@ -297,11 +347,45 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
         }
         x[r] = (r == j ? 1.f : 0.f) - ((s0 + s1) + (s2 + s3));
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) T[(16 * blk + r) * AS + 16 * blk + j] = x[r];
+    }
+    lds_barrier();
+
+    // ---- T, step 2: blocks below the diagonal; wave 2*hv: column 0, wave 2*hv+1: columns 1, 2
+    if (hv < nb_heads) {
+      const float* A = sm.u.m.A[hv];
+      float* T = sm.u.m.T[hv];
+      float* wt = sm.wtmp[wave];
+      if (half_w == 0) {
+        for (int ib = 1; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, 0, lane);
+      } else {
+        for (int ib = 2; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, 1, lane);
+        t_offdiag_block(A, T, wt, 3, 2, lane);
+      }
+    }
+    lds_barrier();
+
+    // ---- T (fp16) to the workspace: the two waves of a head write 32 rows each
+    if (hv < nb_heads) {
+      const int h = g * p.group + base + hv;
+      const float* T = sm.u.m.T[hv];
       _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * C * C;
 #pragma unroll
-      for (int r = 0; r < C; ++r) Tw[r * C + j] = (_Float16)x[r];
+      for (int it = 0; it < 4; ++it) {
+        const int idx = 64 * (4 * half_w + it) + lane;   // 512 pieces of 8 per head
+        const int row = idx >> 3, c8 = (idx & 7) * 8;
+        half8_t hv8 = {};                                // blocks above the diagonal are 0
+        if ((c8 >> 4) <= (row >> 4)) {
+          const float4_t lo = *reinterpret_cast<const float4_t*>(&T[row * AS + c8]);
+          const float4_t hi = *reinterpret_cast<const float4_t*>(&T[row * AS + c8 + 4]);
+          hv8 = half8_t{(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
+                        (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+        }
+        *reinterpret_cast<half8_t*>(Tw + row * C + c8) = hv8;
+      }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -319,7 +403,8 @@ struct ScanSmem {
   _Float16 Zt[TV * TS];    // Z^T  [dv][token]
   _Float16 Ut[TV * TS];    // U^T  [dv][token]
   _Float16 Uk[TV * TS];    // (diag(e^{gL-g} rk) U)^T
-  float g[C], beta[C], rk[C], rq[C];
+  float zf[C], beta[C], of[C], uf[C];
+  float gamma;
 };
 
 // Registers holding the next chunk's inputs while the current one computes.
@@ -328,6 +413,7 @@ struct Prefetch {
   half8_t k[4], q[4], t[2], pm[2];
   half8_t v;
   float vec;
+  float gamma;
 };
 
 template <int TV>
@@ -366,10 +452,9 @@ __device__ __forceinline__ void prefetch_chunk(const ChunkArgs& p, const Ws& w, 
     }
   }
   {
-    const int which = tid >> 6, t = tid & 63;  // 0: g, 1: beta, 2: rk, 3: rq
-    const float* src = which < 2 ? w.gb + ((size_t)slot * p.Hv + h) * 2 * C + which * C
-                                 : w.nrm + ((size_t)slot * p.Hk + g) * 2 * C + (which - 2) * C;
-    f.vec = src[t];
+    const float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
+    f.vec = vec[tid];                          // rows kVecZ .. kVecU, 64 floats each
+    f.gamma = vec[kVecGamma * C];
   }
 }
 
@@ -399,8 +484,9 @@ __device__ __forceinline__ void stage_chunk(ScanSmem<TV>& sm, const Prefetch<TV>
   }
   {
     const int which = tid >> 6, t = tid & 63;
-    float* dst = which == 0 ? sm.g : which == 1 ? sm.beta : which == 2 ? sm.rk : sm.rq;
+    float* dst = which == kVecZ ? sm.zf : which == kVecBeta ? sm.beta : which == kVecO ? sm.of : sm.uf;
     dst[t] = f.vec;
+    if (tid == 0) sm.gamma = f.gamma;
   }
 }
 
@@ -461,7 +547,7 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           sm.S16[(16 * mb + 4 * q4 + e) * KS + 32 * wave + 16 * nb + l16] = (_Float16)S[mb][nb][e];
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < nch) {
       const int tn = t0 + C;
       prefetch_chunk<TV>(p, w, slot0 + c + 1, tn, min(C, end - tn), h, g, d0, f);
@@ -492,14 +578,13 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
         const int t = 16 * wave + 4 * q4 + e;
         const int dv = 16 * nb + l16;
         const float vv = (float)sm.V[t * (TV + 8) + dv];
-        z4[e] = (_Float16)(sm.beta[t] * (vv - expf(sm.g[t]) * sm.rk[t] * X[nb][e]));
+        z4[e] = (_Float16)(sm.beta[t] * (vv - sm.zf[t] * X[nb][e]));
       }
       *reinterpret_cast<half4_t*>(&sm.Zt[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = z4;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- U = T Z (T is lower triangular: tokens beyond this row block add nothing)
-    const float gL = sm.g[C - 1];
     float4_t U[MB];
 #pragma unroll
     for (int nb = 0; nb < MB; ++nb) {
@@ -518,12 +603,12 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * wave + 4 * q4 + e;
         u4[e] = (_Float16)U[nb][e];
-        w4[e] = (_Float16)(expf(gL - sm.g[t]) * sm.rk[t] * U[nb][e]);
+        w4[e] = (_Float16)(sm.uf[t] * U[nb][e]);
       }
       *reinterpret_cast<half4_t*>(&sm.Ut[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = u4;
       *reinterpret_cast<half4_t*>(&sm.Uk[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = w4;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- O = diag(e^g rq) Y + P U  -> output rows < L
 #pragma unroll
@@ -532,7 +617,7 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * wave + 4 * q4 + e;
-        o[e] = expf(sm.g[t]) * sm.rq[t] * Y[nb][e];
+        o[e] = sm.of[t] * Y[nb][e];
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -551,7 +636,7 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
     }
 
     // ---- S = e^{gL} S + Uk^T K  (wave: dk columns 32*wave .. +31)
-    const float decay_L = expf(gL);
+    const float decay_L = sm.gamma;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -568,7 +653,7 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
           S[mb][nb] = mfma_f16(au, bk, S[mb][nb]);
         }
       }
-    __syncthreads();   // all LDS reads of this chunk are done before the next stage
+    lds_barrier();   // all LDS reads of this chunk are done before the next stage
   }
 
   if (p.final_state != nullptr) {

@@ -69,3 +69,16 @@ __device__ __forceinline__ float decay_from_raw(float a, float expA, float dt_bi
 __device__ __forceinline__ float sigmoid_f(float b) { return 1.0f / (1.0f + expf(-b)); }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations
+// (not its outstanding global loads) before s_barrier, so register prefetches
+// of global data stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace gdn
