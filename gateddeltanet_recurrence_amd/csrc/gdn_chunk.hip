@@ -41,6 +41,12 @@ __device__ __forceinline__ float4_t mfma_f16(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// e^x on the hardware exp2 (about 1 ulp); used where the result is stored at
+// fp16 or enters a product already rounded to fp16.
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 __device__ __forceinline__ half8_t lds8(const _Float16* p) {
   return *reinterpret_cast<const half8_t*>(p);
 }
@@ -213,19 +219,29 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
   const _Float16* kp = static_cast<const _Float16*>(p.k);
   const _Float16* qp = static_cast<const _Float16*>(p.q);
 
+  // gate inputs of the first pass, loaded early (wave w < heads of the pass: head g*G + w);
+  // tokens >= L and heads past the group read as zero
+  const int gate_bytes = ((L - 1) * p.Hv + 1) * 4;
+  float a_pf, b_pf;
+  {
+    const bool on = wave < min(kHeadsPerPass, p.group);
+    const int h = g * p.group + (on ? wave : 0);
+    a_pf = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + h, on ? gate_bytes : 0), lane * p.Hv * 4);
+    b_pf = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + h, on ? gate_bytes : 0), lane * p.Hv * 4);
+  }
+
   // ---- K, Q chunk tiles into LDS (rows >= L zero); 16 lanes per row, so the
   // per-token sums of squares reduce across those 16 lanes
   float ssk[4], ssq[4];
+  const int krow = p.Hk * D;
+  const rsrc_t rk = make_rsrc(kp + ((size_t)t0 * p.Hk + g) * D, ((L - 1) * krow + D) * 2);
+  const rsrc_t rq = make_rsrc(qp + ((size_t)t0 * p.Hk + g) * D, ((L - 1) * krow + D) * 2);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int idx = tid + kThreads * it;    // 1024 16-byte pieces per tile
     const int row = idx >> 4, c8 = (idx & 15) * 8;
-    half8_t kv = {}, qv = {};
-    if (row < L) {
-      const size_t off = ((size_t)(t0 + row) * p.Hk + g) * D + c8;
-      kv = *reinterpret_cast<const half8_t*>(kp + off);
-      qv = *reinterpret_cast<const half8_t*>(qp + off);
-    }
+    const half8_t kv = buf_load_h8(rk, (row * krow + c8) * 2);   // rows >= L read as zero
+    const half8_t qv = buf_load_h8(rq, (row * krow + c8) * 2);
     *reinterpret_cast<half8_t*>(&sm.u.in.K[row * KS + c8]) = kv;
     *reinterpret_cast<half8_t*>(&sm.u.in.Q[row * KS + c8]) = qv;
     float sk = 0.f, sq = 0.f;
@@ -278,10 +294,14 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
       const int t = lane;
       float la = 0.f, be = 0.f;
       if (t < L) {
-        const float x = p.a[(size_t)(t0 + t) * p.Hv + h] + p.dt_bias[h];
-        la = -expf(p.A_log[h]) * softplus_f(x);
-        be = sigmoid_f(p.b[(size_t)(t0 + t) * p.Hv + h]);
+        la = -expf(p.A_log[h]) * softplus_f(a_pf + p.dt_bias[h]);
+        be = sigmoid_f(b_pf);
       }
+      // the next pass's gate inputs, in flight while this pass computes
+      const bool on = base + kHeadsPerPass + wave < p.group;
+      const int hn = on ? h + kHeadsPerPass : h;
+      a_pf = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + hn, on ? gate_bytes : 0), t * p.Hv * 4);
+      b_pf = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + hn, on ? gate_bytes : 0), t * p.Hv * 4);
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {      // inclusive prefix sum over the 64 lanes
         const float y = __shfl_up(la, d, 64);
@@ -299,10 +319,11 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
     }
     lds_barrier();
 
-    // ---- A (fp32, LDS) and P (fp16, workspace) from the Gram accumulators
-    for (int hv = 0; hv < nb_heads; ++hv) {
-      const int h = g * p.group + base + hv;
-      _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
+    // ---- A (fp32, LDS) and P (fp16, kept in registers until T is out) from the Gram
+    half4_t pk[kHeadsPerPass][4];
+#pragma unroll
+    for (int hv = 0; hv < kHeadsPerPass; ++hv) {
+      if (hv >= nb_heads) break;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int i = 16 * nb + (lane & 15);            // column (earlier token)
@@ -313,12 +334,12 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
           const float gr = sm.g[hv][r];
           float av = 0.f, pv = 0.f;
           if (nb <= wave) {
-            const float dec = expf(fminf(gr - gi, 0.f));
+            const float dec = fast_exp(fminf(gr - gi, 0.f));
             if (i < r) av = sm.beta[hv][r] * dec * sm.rk[r] * rki * kk[nb][e];
             if (i <= r) pv = dec * sm.rq[r] * rki * qk[nb][e];
           }
           sm.u.m.A[hv][r * AS + i] = av;
-          Pw[r * C + i] = (_Float16)pv;
+          pk[hv][nb][e] = (_Float16)pv;
         }
       }
     }
@@ -386,23 +407,56 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
       }
     }
     lds_barrier();
+
+    // ---- P (fp16) through LDS (the T buffers are free now) to the workspace
+#pragma unroll
+    for (int hvp = 0; hvp < kHeadsPerPass; ++hvp) {
+      if (hvp >= nb_heads) break;
+      _Float16* Ps = reinterpret_cast<_Float16*>(sm.u.m.T[hvp]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Ps[(16 * wave + 4 * (lane >> 4) + e) * TS + 16 * nb + (lane & 15)] = pk[hvp][nb][e];
+    }
+    lds_barrier();
+    if (hv < nb_heads) {
+      const int h = g * p.group + base + hv;
+      const _Float16* Ps = reinterpret_cast<const _Float16*>(sm.u.m.T[hv]);
+      _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int idx = 64 * (4 * half_w + it) + lane;
+        const int row = idx >> 3, c8 = (idx & 7) * 8;
+        *reinterpret_cast<half8_t*>(Pw + row * C + c8) = lds8(&Ps[row * TS + c8]);
+      }
+    }
+    lds_barrier();
   }
 }
 
 // ----------------------------------------------------------------------------
 // gdn_chunk_scan: one workgroup per (request, value head, Dv tile of TV rows)
+//
+// The state tile is held transposed, S^T [dk][dv], in MFMA accumulators: wave w
+// owns dk rows 32w .. 32w+31 for all TV dv columns. X, Y, Z, U and O are split
+// by token rows: wave w computes tokens 16w .. 16w+15. K and Q of the chunk are
+// staged once, row-major; the update S^T += K^T (uf o U) takes its K^T operand
+// from the row-major tile with transposing LDS reads (ds_read_b64_tr_b16).
 // ----------------------------------------------------------------------------
+constexpr int VS_PAD = 4;           // V tile row padding (halves)
+
 template <int TV>
 struct ScanSmem {
-  _Float16 K[C * KS];      // raw k of the chunk, token-major
-  _Float16 Q[C * KS];      // raw q of the chunk
+  _Float16 K[C * KS];      // k of the chunk, [token][dk]
+  _Float16 Q[C * KS];      // q of the chunk, [token][dk]
   _Float16 T[C * TS];
   _Float16 P[C * TS];
-  _Float16 V[C * (TV + 8)];
+  _Float16 V[C * (TV + VS_PAD)];
   _Float16 S16[TV * KS];   // fp16 copy of the state tile, [dv][dk]
   _Float16 Zt[TV * TS];    // Z^T  [dv][token]
   _Float16 Ut[TV * TS];    // U^T  [dv][token]
-  _Float16 Uk[TV * TS];    // (diag(e^{gL-g} rk) U)^T
+  _Float16 Uk[TV * TS];    // (diag(uf) U)^T
   float zf[C], beta[C], of[C], uf[C];
   float gamma;
 };
@@ -410,52 +464,89 @@ struct ScanSmem {
 // Registers holding the next chunk's inputs while the current one computes.
 template <int TV>
 struct Prefetch {
-  half8_t k[4], q[4], t[2], pm[2];
-  half8_t v;
+  static constexpr int VH = TV / 4;   // halves of the V tile per thread (64 rows x TV)
+  half8_t k[4], q[4];                 // row-major pieces of K and Q
+  half8_t t[2], pm[2];
+  _Float16 v[VH];
   float vec;
   float gamma;
 };
 
+// Loads of the chunk that starts at token t0 with L tokens (L = 0: all loads
+// return zeros and touch no memory). Every load is a range-checked buffer load.
 template <int TV>
-__device__ __forceinline__ void prefetch_chunk(const ChunkArgs& p, const Ws& w, int slot, int t0,
-                                               int L, int h, int g, int d0, Prefetch<TV>& f) {
+__device__ __forceinline__ void prefetch_chunk(const ChunkArgs& p, const Ws& w, int slot, int t0, int L,
+                                               int h, int g, int d0, Prefetch<TV>& f) {
   const int tid = threadIdx.x;
-  const _Float16* kp = static_cast<const _Float16*>(p.k);
-  const _Float16* qp = static_cast<const _Float16*>(p.q);
-  const _Float16* vp = static_cast<const _Float16*>(p.v);
+  const int krow = p.Hk * D;                   // elements between consecutive tokens of k, q
+  const int vrow = p.Hv * D;
+  const size_t kq_base = ((size_t)t0 * p.Hk + g) * D;
+  const int kq_bytes = L > 0 ? ((L - 1) * krow + D) * 2 : 0;
+  const rsrc_t rk = make_rsrc(static_cast<const _Float16*>(p.k) + kq_base, kq_bytes);
+  const rsrc_t rq = make_rsrc(static_cast<const _Float16*>(p.q) + kq_base, kq_bytes);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int idx = tid + kThreads * it;
+    const int idx = tid + kThreads * it;       // 64 rows x 16 pieces of 8
     const int row = idx >> 4, c8 = (idx & 15) * 8;
-    f.k[it] = half8_t{};
-    f.q[it] = half8_t{};
-    if (row < L) {
-      const size_t off = ((size_t)(t0 + row) * p.Hk + g) * D + c8;
-      f.k[it] = *reinterpret_cast<const half8_t*>(kp + off);
-      f.q[it] = *reinterpret_cast<const half8_t*>(qp + off);
-    }
+    f.k[it] = buf_load_h8(rk, (row * krow + c8) * 2);
+    f.q[it] = buf_load_h8(rq, (row * krow + c8) * 2);
   }
-  const _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * C * C;
-  const _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
+  const int wsz = L > 0 ? C * C * 2 : 0;
+  const rsrc_t rt = make_rsrc(w.T + ((size_t)slot * p.Hv + h) * C * C, wsz);
+  const rsrc_t rp = make_rsrc(w.P + ((size_t)slot * p.Hv + h) * C * C, wsz);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int idx = tid + kThreads * it;       // 512 pieces of 8 halves
-    f.t[it] = *reinterpret_cast<const half8_t*>(Tw + idx * 8);
-    f.pm[it] = *reinterpret_cast<const half8_t*>(Pw + idx * 8);
+    f.t[it] = buf_load_h8(rt, idx * 16);
+    f.pm[it] = buf_load_h8(rp, idx * 16);
   }
   {
-    constexpr int PER_ROW = TV / 8;
-    f.v = half8_t{};
-    if (tid < C * PER_ROW) {
-      const int row = tid / PER_ROW, c8 = (tid % PER_ROW) * 8;
-      if (row < L) f.v = *reinterpret_cast<const half8_t*>(vp + ((size_t)(t0 + row) * p.Hv + h) * D + d0 + c8);
+    const rsrc_t rv = make_rsrc(static_cast<const _Float16*>(p.v) + ((size_t)t0 * p.Hv + h) * D + d0,
+                                L > 0 ? ((L - 1) * vrow + TV) * 2 : 0);
+    constexpr int VH = Prefetch<TV>::VH, PER_ROW = TV / VH;
+    const int row = tid / PER_ROW, cc = (tid % PER_ROW) * VH;
+    if constexpr (VH == 8) {
+      const half8_t x = buf_load_h8(rv, (row * vrow + cc) * 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+    } else {
+      const half4_t x = buf_load_h4(rv, (row * vrow + cc) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.v[j] = x[j];
     }
   }
   {
-    const float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
-    f.vec = vec[tid];                          // rows kVecZ .. kVecU, 64 floats each
-    f.gamma = vec[kVecGamma * C];
+    const rsrc_t rvec = make_rsrc(w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C,
+                                  L > 0 ? kVecRows * C * 4 : 0);
+    f.vec = buf_load_f32(rvec, tid * 4);       // rows kVecZ .. kVecU, 64 floats each
+    f.gamma = buf_load_f32(rvec, kVecGamma * C * 4);
   }
+}
+
+// Waits here for the prefetched registers (an empty asm that reads them), so the
+// wait lands at the end of an iteration and the loop header inherits nothing
+// outstanding.
+template <typename V>
+__device__ __forceinline__ void settle(const V& x) {
+  asm volatile("" ::"v"(x));
+}
+
+template <int TV>
+__device__ __forceinline__ void settle_prefetch(const Prefetch<TV>& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    settle(f.k[i]);
+    settle(f.q[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    settle(f.t[i]);
+    settle(f.pm[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < Prefetch<TV>::VH; ++j) settle(f.v[j]);
+  settle(f.vec);
+  settle(f.gamma);
 }
 
 template <int TV>
@@ -476,11 +567,10 @@ __device__ __forceinline__ void stage_chunk(ScanSmem<TV>& sm, const Prefetch<TV>
     *reinterpret_cast<half8_t*>(&sm.P[row * TS + c8]) = f.pm[it];
   }
   {
-    constexpr int PER_ROW = TV / 8;
-    if (tid < C * PER_ROW) {
-      const int row = tid / PER_ROW, c8 = (tid % PER_ROW) * 8;
-      *reinterpret_cast<half8_t*>(&sm.V[row * (TV + 8) + c8]) = f.v;
-    }
+    constexpr int VH = Prefetch<TV>::VH, PER_ROW = TV / VH;
+    const int row = tid / PER_ROW, cc = (tid % PER_ROW) * VH;
+#pragma unroll
+    for (int j = 0; j < VH; ++j) sm.V[row * (TV + VS_PAD) + cc + j] = f.v[j];
   }
   {
     const int which = tid >> 6, t = tid & 63;
@@ -490,10 +580,30 @@ __device__ __forceinline__ void stage_chunk(ScanSmem<TV>& sm, const Prefetch<TV>
   }
 }
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// MFMA operand holding, for lane (n = lane % 16, q = lane / 16), the eight values
+// X[t0 + 8q + j][n0 + n] (j = 0..7) of a row-major fp16 LDS tile X with row
+// stride `ld` halves: two transposing 64-bit LDS reads. Within each 16-lane group
+// the read hands lane n element e of lane 4e + n/4's 4-element row segment, so
+// lane i addresses row t0 + 8q + 4h + i/4, columns n0 + 4 (i % 4) .. +3.
+// The halves are reinterpreted as whole vectors: element-wise casts of the read's
+// result were folded into a broadcast of element 0 by the compiler.
+__device__ __forceinline__ half8_t lds_col8(const _Float16* X, int ld, int t0, int n0) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, q = lane >> 4;
+  const _Float16* a0 = X + (t0 + 8 * q + (i >> 2)) * ld + n0 + 4 * (i & 3);
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(a0));
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(a0 + 4 * ld));
+  const half4_t l4 = __builtin_bit_cast(half4_t, lo), h4 = __builtin_bit_cast(half4_t, hi);
+  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int TV>
 __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_items) {
   constexpr int NT = D / TV;        // Dv tiles per head
-  constexpr int MB = TV / 16;       // 16-row blocks of the tile
+  constexpr int MB = TV / 16;       // 16-column dv blocks of the tile
   __shared__ ScanSmem<TV> sm;
 
   // XCD-aware order: consecutive items (same request and key head) share an XCD's L2
@@ -518,40 +628,43 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
   int nch = (end - beg + C - 1) / C;
   nch = max(0, min(nch, p.max_chunks - slot0));
 
-  // ---- state tile: wave owns dk columns 32*wave .. +31; S[mb][nb] is a 16x16 block
-  float4_t S[MB][2];
+  // ---- state tile, transposed: ST[i][nb] holds S[dv = d0+16nb+l16][dk = 32*wave+16i+4q4+e]
+  float4_t ST[2][MB];
   const size_t head_off = ((size_t)req * p.Hv + h) * D * D;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dv = d0 + 16 * mb + 4 * q4 + e, dk = 32 * wave + 16 * nb + l16;
-        S[mb][nb][e] = p.initial_state != nullptr ? p.initial_state[head_off + (size_t)dv * D + dk] : 0.f;
-      }
+    for (int nb = 0; nb < MB; ++nb) {
+      const int dv = d0 + 16 * nb + l16, dk = 32 * wave + 16 * i + 4 * q4;
+      ST[i][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      if (p.initial_state != nullptr)
+        ST[i][nb] = *reinterpret_cast<const float4_t*>(p.initial_state + head_off + (size_t)dv * D + dk);
+    }
 
   Prefetch<TV> f;
-  if (nch > 0) prefetch_chunk<TV>(p, w, slot0, beg, min(C, end - beg), h, g, d0, f);
+  prefetch_chunk<TV>(p, w, slot0, beg, nch > 0 ? min(C, end - beg) : 0, h, g, d0, f);
+  settle_prefetch<TV>(f);
 
   _Float16* op = static_cast<_Float16*>(p.output);
   for (int c = 0; c < nch; ++c) {
     const int t0 = beg + C * c;
     const int L = min(C, end - t0);
+    const bool more = c + 1 < nch;
+    const int tn = t0 + C;
+    const int Ln = more ? min(C, end - tn) : 0;       // 0: the prefetch below loads nothing
+    const int slot_n = more ? slot0 + c + 1 : slot0 + c;
     // ---- chunk inputs and the fp16 state copy into LDS
     stage_chunk<TV>(sm, f);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sm.S16[(16 * mb + 4 * q4 + e) * KS + 32 * wave + 16 * nb + l16] = (_Float16)S[mb][nb][e];
+      for (int nb = 0; nb < MB; ++nb) {
+        half4_t s4 = {(_Float16)ST[i][nb][0], (_Float16)ST[i][nb][1], (_Float16)ST[i][nb][2],
+                      (_Float16)ST[i][nb][3]};
+        *reinterpret_cast<half4_t*>(&sm.S16[(16 * nb + l16) * KS + 32 * wave + 16 * i + 4 * q4]) = s4;
+      }
     lds_barrier();
-    if (c + 1 < nch) {
-      const int tn = t0 + C;
-      prefetch_chunk<TV>(p, w, slot0 + c + 1, tn, min(C, end - tn), h, g, d0, f);
-    }
+    prefetch_chunk<TV>(p, w, slot_n, tn, Ln, h, g, d0, f);
 
     // ---- X = K S0^T and Y = Q S0^T for tokens 16*wave .. +15
     float4_t X[MB], Y[MB];
@@ -559,25 +672,27 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
     for (int nb = 0; nb < MB; ++nb) {
       X[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
       Y[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int col = 32 * ks + 8 * q4;
-        const half8_t ak = lds8(&sm.K[(16 * wave + l16) * KS + col]);
-        const half8_t aq = lds8(&sm.Q[(16 * wave + l16) * KS + col]);
+    for (int ks = 0; ks < 4; ++ks) {
+      const int col = 32 * ks + 8 * q4;
+      const half8_t ak = lds8(&sm.K[(16 * wave + l16) * KS + col]);
+      const half8_t aq = lds8(&sm.Q[(16 * wave + l16) * KS + col]);
+#pragma unroll
+      for (int nb = 0; nb < MB; ++nb) {
         const half8_t bs = lds8(&sm.S16[(16 * nb + l16) * KS + col]);
         X[nb] = mfma_f16(ak, bs, X[nb]);
         Y[nb] = mfma_f16(aq, bs, Y[nb]);
       }
     }
-    // ---- Z = beta (V - e^g rk X) -> Zt[dv][token]
+    // ---- Z = beta (V - zf X) -> Zt[dv][token]
 #pragma unroll
     for (int nb = 0; nb < MB; ++nb) {
       half4_t z4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * wave + 4 * q4 + e;
-        const int dv = 16 * nb + l16;
-        const float vv = (float)sm.V[t * (TV + 8) + dv];
+        const float vv = (float)sm.V[t * (TV + VS_PAD) + 16 * nb + l16];
         z4[e] = (_Float16)(sm.beta[t] * (vv - sm.zf[t] * X[nb][e]));
       }
       *reinterpret_cast<half4_t*>(&sm.Zt[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = z4;
@@ -587,17 +702,21 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
     // ---- U = T Z (T is lower triangular: tokens beyond this row block add nothing)
     float4_t U[MB];
 #pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      U[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < MB; ++nb) U[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (32 * ks <= 16 * wave + 15) {
-          const int col = 32 * ks + 8 * q4;
-          const half8_t at = lds8(&sm.T[(16 * wave + l16) * TS + col]);
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks <= 16 * wave + 15) {
+        const int col = 32 * ks + 8 * q4;
+        const half8_t at = lds8(&sm.T[(16 * wave + l16) * TS + col]);
+#pragma unroll
+        for (int nb = 0; nb < MB; ++nb) {
           const half8_t bz = lds8(&sm.Zt[(16 * nb + l16) * TS + col]);
           U[nb] = mfma_f16(at, bz, U[nb]);
         }
       }
+    }
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
       half4_t u4, w4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -610,62 +729,67 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
     }
     lds_barrier();
 
-    // ---- O = diag(e^g rq) Y + P U  -> output rows < L
+    // ---- O = diag(of) Y + P U  -> output rows < L
+    float4_t O[MB];
 #pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      float4_t o;
+    for (int nb = 0; nb < MB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * wave + 4 * q4 + e;
-        o[e] = sm.of[t] * Y[nb][e];
-      }
+      for (int e = 0; e < 4; ++e) O[nb][e] = sm.of[16 * wave + 4 * q4 + e] * Y[nb][e];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (32 * ks <= 16 * wave + 15) {
-          const int col = 32 * ks + 8 * q4;
-          const half8_t ap = lds8(&sm.P[(16 * wave + l16) * TS + col]);
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks <= 16 * wave + 15) {
+        const int col = 32 * ks + 8 * q4;
+        const half8_t ap = lds8(&sm.P[(16 * wave + l16) * TS + col]);
+#pragma unroll
+        for (int nb = 0; nb < MB; ++nb) {
           const half8_t bu = lds8(&sm.Ut[(16 * nb + l16) * TS + col]);
-          o = mfma_f16(ap, bu, o);
+          O[nb] = mfma_f16(ap, bu, O[nb]);
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * wave + 4 * q4 + e;
-        if (t < L) op[((size_t)(t0 + t) * p.Hv + h) * D + d0 + 16 * nb + l16] = (_Float16)o[e];
       }
     }
+    {
+      const int vrow = p.Hv * D;
+      const rsrc_t ro = make_rsrc(op + ((size_t)t0 * p.Hv + h) * D + d0, ((L - 1) * vrow + TV) * 2);
+#pragma unroll
+      for (int nb = 0; nb < MB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * wave + 4 * q4 + e;   // rows t >= L fall outside the range: dropped
+          buf_store_h1((_Float16)O[nb][e], ro, (t * vrow + 16 * nb + l16) * 2);
+        }
+    }
 
-    // ---- S = e^{gL} S + Uk^T K  (wave: dk columns 32*wave .. +31)
+    // ---- S^T = gamma S^T + K^T (uf o U)   (wave: dk rows 32*wave .. +31)
     const float decay_L = sm.gamma;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        S[mb][nb] *= decay_L;
+      for (int nb = 0; nb < MB; ++nb) ST[i][nb] *= decay_L;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int tk = 32 * ks + 8 * q4;
-          const half8_t au = lds8(&sm.Uk[(16 * mb + l16) * TS + tk]);
-          const int dk = 32 * wave + 16 * nb + l16;
-          half8_t bk;
+    for (int ks = 0; ks < 2; ++ks) {
+      const int col = 32 * ks + 8 * q4;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) bk[j] = sm.K[(tk + j) * KS + dk];
-          S[mb][nb] = mfma_f16(au, bk, S[mb][nb]);
+      for (int i = 0; i < 2; ++i) {
+        const half8_t ak = lds_col8(sm.K, KS, 32 * ks, 32 * wave + 16 * i);
+#pragma unroll
+        for (int nb = 0; nb < MB; ++nb) {
+          const half8_t bu = lds8(&sm.Uk[(16 * nb + l16) * TS + col]);
+          ST[i][nb] = mfma_f16(ak, bu, ST[i][nb]);
         }
       }
+    }
+    settle_prefetch<TV>(f);
     lds_barrier();   // all LDS reads of this chunk are done before the next stage
   }
 
   if (p.final_state != nullptr) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dv = d0 + 16 * mb + 4 * q4 + e, dk = 32 * wave + 16 * nb + l16;
-          p.final_state[head_off + (size_t)dv * D + dk] = S[mb][nb][e];
-        }
+      for (int nb = 0; nb < MB; ++nb) {
+        const int dv = d0 + 16 * nb + l16, dk = 32 * wave + 16 * i + 4 * q4;
+        *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)dv * D + dk) = ST[i][nb];
+      }
   }
 }
 

@@ -82,3 +82,35 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// Raw buffer access with a hardware range check: a load past `bytes` returns 0
+// and a store past it is dropped, so ragged tails need no branches (which keeps
+// the number of memory instructions per loop iteration fixed and lets the
+// compiler wait for just the data it needs).
+constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer descriptor word 3
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ half8_t buf_load_h8(rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ half4_t buf_load_h4(rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store_h1(_Float16 x, rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, byte_off, 0, 0);
+}
+
+}  // namespace gdn
