@@ -34,6 +34,10 @@
 #ifndef GDN_STATE_NT
 #define GDN_STATE_NT 1
 #endif
+// Rows per lane group of the Dk = 128 capsule (verify) instantiation.
+#ifndef GDN_CAP_NI128
+#define GDN_CAP_NI128 4
+#endif
 
 namespace gdn {
 
@@ -225,6 +229,211 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   }
 }
 
+// Token-staged variant: the workgroup stages groups of up to kStageTokens tokens
+// into LDS before its waves walk them (raw k, q and v loaded once per workgroup;
+// unit key, scaled unit query, k^.q^, alpha and beta computed once per token). The
+// waves' state loads are issued before the staging, so a short segment (the
+// speculative verify) pays one memory latency instead of one per token.
+constexpr int kStageTokens = 16;
+
+template <int DK>
+struct StageSmem {
+  float kh[kStageTokens][DK];      // unit keys
+  float qh[kStageTokens][DK];      // unit queries times the scale
+  float v[kStageTokens][256];      // this block's value rows (at most 4 waves x 64 rows)
+  float alpha[kStageTokens], beta[kStageTokens], kq[kStageTokens];
+};
+
+template <typename IO, int DK, int NI, bool CAPTURE>
+__device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, int waves_per_block,
+                                                      int blocks_per_head) {
+  using L = RecLayout<DK>;
+  constexpr int LPR = L::LPR, E = L::E, V4 = L::V4, RI = L::RI, RW = RI * NI;
+  constexpr int TPT = 16;                 // threads per staged token
+  constexpr int EPT = DK / TPT;           // elements per staging thread
+  __shared__ StageSmem<DK> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = lane / LPR;
+  const int c = lane % LPR;
+
+  int item = blockIdx.x;
+  const int blk = item % blocks_per_head;
+  item /= blocks_per_head;
+  const int h = item % p.Hv;
+  const int r = item / p.Hv;
+  const int g = h / p.group;
+  const int Dv = p.Dv;
+  const int block_row0 = blk * waves_per_block * RW;
+  const int block_rows = waves_per_block * RW;
+  const int row_base = block_row0 + wave * RW;
+
+  const int t0 = min(max(p.cu_seqlens[r], 0), p.N);
+  const int t1 = min(max(p.cu_seqlens[r + 1], t0), p.N);
+  const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
+
+  // ---- state rows into registers (issued before any staging)
+  float S[NI][E];
+  bool valid[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = row_base + i * RI + rg;
+    valid[i] = row < Dv;
+#pragma unroll
+    for (int j = 0; j < V4; ++j) {
+      float4_t x = {0.f, 0.f, 0.f, 0.f};
+      if (p.initial_state != nullptr && valid[i])
+        x = load_state4(p.initial_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j);
+      S[i][4 * j + 0] = x.x;
+      S[i][4 * j + 1] = x.y;
+      S[i][4 * j + 2] = x.z;
+      S[i][4 * j + 3] = x.w;
+    }
+  }
+
+  const float expA = expf(p.A_log[h]);
+  const float dtb = p.dt_bias[h];
+  const IO* __restrict__ qp = static_cast<const IO*>(p.q);
+  const IO* __restrict__ kp = static_cast<const IO*>(p.k);
+  const IO* __restrict__ vp = static_cast<const IO*>(p.v);
+  IO* __restrict__ op = static_cast<IO*>(p.output);
+  float* __restrict__ cap = p.state_update;
+
+  int ncap = 0;
+  if constexpr (CAPTURE) {
+    int cmax = p.capacity;
+    if (p.capture_count != nullptr) cmax = min(max(p.capture_count[r], 0), p.capacity);
+    ncap = min(t1 - t0, cmax);
+  }
+
+  for (int ts = t0; ts < t1; ts += kStageTokens) {
+    const int nt = min(kStageTokens, t1 - ts);
+    // ---- stage: 16 threads per token normalise k and q and form the gates
+    {
+      const int j = tid / TPT, part = tid % TPT;
+      if (j < nt) {
+        const int t = ts + j;
+        const IO* krow = kp + ((size_t)t * p.Hk + g) * DK + part * EPT;
+        const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK + part * EPT;
+        float kv[EPT], qv[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          kv[e] = IoOps<IO>::load1(krow + e);
+          qv[e] = IoOps<IO>::load1(qrow + e);
+        }
+        float ssk = 0.f, ssq = 0.f, skq = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          ssk = fmaf(kv[e], kv[e], ssk);
+          ssq = fmaf(qv[e], qv[e], ssq);
+          skq = fmaf(kv[e], qv[e], skq);
+        }
+        ssk = group_sum<TPT>(ssk);
+        ssq = group_sum<TPT>(ssq);
+        skq = group_sum<TPT>(skq);
+        const float rk = rsqrtf(ssk + kNormEps);
+        const float rq = rsqrtf(ssq + kNormEps) * p.scale;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          sm.kh[j][part * EPT + e] = kv[e] * rk;
+          sm.qh[j][part * EPT + e] = qv[e] * rq;
+        }
+        if (part == 0) {
+          sm.alpha[j] = decay_from_raw(p.a[(size_t)t * p.Hv + h], expA, dtb);
+          sm.beta[j] = sigmoid_f(p.b[(size_t)t * p.Hv + h]);
+          sm.kq[j] = skq * rk * rq;
+        }
+      }   // a token's 16 lanes are one aligned DPP row group: active or idle together
+      // this block's value rows of every staged token
+      for (int idx = tid; idx < nt * block_rows; idx += blockDim.x) {
+        const int jj = idx / block_rows, rr = idx % block_rows;
+        const int row = block_row0 + rr;
+        sm.v[jj][rr] = row < Dv ? IoOps<IO>::load1(vp + ((size_t)(ts + jj) * p.Hv + h) * Dv + row) : 0.f;
+      }
+    }
+    __syncthreads();
+
+    for (int j = 0; j < nt; ++j) {
+      const int t = ts + j;
+      float kv[E], qv[E];
+#pragma unroll
+      for (int jj = 0; jj < V4; ++jj) {
+        const float4_t kx = *reinterpret_cast<const float4_t*>(&sm.kh[j][4 * c + 4 * LPR * jj]);
+        const float4_t qx = *reinterpret_cast<const float4_t*>(&sm.qh[j][4 * c + 4 * LPR * jj]);
+        kv[4 * jj + 0] = kx.x; kv[4 * jj + 1] = kx.y; kv[4 * jj + 2] = kx.z; kv[4 * jj + 3] = kx.w;
+        qv[4 * jj + 0] = qx.x; qv[4 * jj + 1] = qx.y; qv[4 * jj + 2] = qx.z; qv[4 * jj + 3] = qx.w;
+      }
+      const float alpha = sm.alpha[j], beta = sm.beta[j], kq = sm.kq[j];
+      float pk[NI], pq[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          sk = fmaf(S[i][e], kv[e], sk);
+          sq = fmaf(S[i][e], qv[e], sq);
+        }
+        pk[i] = sk;
+        pq[i] = sq;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        pk[i] = group_sum<LPR>(pk[i]);
+        pq[i] = group_sum<LPR>(pq[i]);
+      }
+      const int jcap = t - t0;
+      float* caprow = nullptr;
+      if constexpr (CAPTURE) {
+        if (jcap < ncap) caprow = cap + ((size_t)r * p.capacity + jcap) * p.capsule_width;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = row_base + i * RI + rg;
+        const float vv = valid[i] ? sm.v[j][row - block_row0] : 0.f;
+        const float u = beta * (vv - alpha * pk[i]);
+        const float o = fmaf(alpha, pq[i], u * kq);
+#pragma unroll
+        for (int e = 0; e < E; ++e) S[i][e] = fmaf(alpha, S[i][e], u * kv[e]);
+        if (valid[i] && c == 0) {
+          IoOps<IO>::store1(op + ((size_t)t * p.Hv + h) * Dv + row, o);
+          if constexpr (CAPTURE) {
+            if (caprow != nullptr) caprow[p.Hv + p.Hk * DK + h * Dv + row] = u;
+          }
+        }
+      }
+      if constexpr (CAPTURE) {
+        if (caprow != nullptr && blk == 0 && wave == 0) {
+          if (lane == 0) caprow[h] = alpha;
+          // the shared key is written once per key head, by its first value head
+          if (h % p.group == 0 && rg == 0) {
+#pragma unroll
+            for (int jj = 0; jj < V4; ++jj)
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                caprow[p.Hv + g * DK + 4 * c + 4 * LPR * jj + x] = kv[4 * jj + x];
+          }
+        }
+      }
+    }
+    __syncthreads();   // the next group's staging overwrites the staged tokens
+  }
+
+  if (p.final_state != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (!valid[i]) continue;
+      const int row = row_base + i * RI + rg;
+#pragma unroll
+      for (int j = 0; j < V4; ++j) {
+        float4_t x = {S[i][4 * j + 0], S[i][4 * j + 1], S[i][4 * j + 2], S[i][4 * j + 3]};
+        store_state4(p.final_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
+      }
+    }
+  }
+}
+
 // Distinct kernel names for the profiler: gdn_decode (no capture) and gdn_capsule.
 template <typename IO, int DK, int NI>
 __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_decode(RecurrentArgs p, int wpb, int bph) {
@@ -232,31 +441,39 @@ __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_decode(RecurrentArgs p
 }
 template <typename IO, int DK, int NI>
 __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_capsule(RecurrentArgs p, int wpb, int bph) {
-  recurrent_body<IO, DK, NI, true>(p, wpb, bph);
+  recurrent_body_staged<IO, DK, NI, true>(p, wpb, bph);
 }
 
-template <typename IO, int DK, int NI>
-static hipError_t launch_dk(const RecurrentArgs& p, hipStream_t stream) {
+template <int DK, int NI>
+static void launch_shape(int Dv, int* wpb, int* bph) {
   constexpr int RW = RecLayout<DK>::RI * NI;
-  const int waves_needed = (p.Dv + RW - 1) / RW;
-  const int wpb = waves_needed < GDN_REC_WAVES ? waves_needed : GDN_REC_WAVES;
-  const int bph = (p.Dv + wpb * RW - 1) / (wpb * RW);
-  const dim3 grid((unsigned)((size_t)p.R * p.Hv * bph));
-  const dim3 block((unsigned)(64 * wpb));
-  if (p.state_update != nullptr)
-    hipLaunchKernelGGL((gdn_capsule<IO, DK, NI>), grid, block, 0, stream, p, wpb, bph);
-  else
-    hipLaunchKernelGGL((gdn_decode<IO, DK, NI>), grid, block, 0, stream, p, wpb, bph);
+  const int waves_needed = (Dv + RW - 1) / RW;
+  *wpb = waves_needed < GDN_REC_WAVES ? waves_needed : GDN_REC_WAVES;
+  *bph = (Dv + *wpb * RW - 1) / (*wpb * RW);
+}
+
+template <typename IO, int DK, int NI, int NI_CAP>
+static hipError_t launch_dk(const RecurrentArgs& p, hipStream_t stream) {
+  int wpb, bph;
+  if (p.state_update != nullptr) {
+    launch_shape<DK, NI_CAP>(p.Dv, &wpb, &bph);
+    hipLaunchKernelGGL((gdn_capsule<IO, DK, NI_CAP>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+                       dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+  } else {
+    launch_shape<DK, NI>(p.Dv, &wpb, &bph);
+    hipLaunchKernelGGL((gdn_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+                       dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+  }
   return hipGetLastError();
 }
 
 template <typename IO>
 static hipError_t launch_io(const RecurrentArgs& p, hipStream_t stream) {
   switch (p.Dk) {
-    case 16: return launch_dk<IO, 16, 1>(p, stream);
-    case 32: return launch_dk<IO, 32, 2>(p, stream);
-    case 64: return launch_dk<IO, 64, 2>(p, stream);
-    case 128: return launch_dk<IO, 128, GDN_REC_NI128>(p, stream);
+    case 16: return launch_dk<IO, 16, 1, 1>(p, stream);
+    case 32: return launch_dk<IO, 32, 2, 2>(p, stream);
+    case 64: return launch_dk<IO, 64, 2, 2>(p, stream);
+    case 128: return launch_dk<IO, 128, GDN_REC_NI128, GDN_CAP_NI128>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
