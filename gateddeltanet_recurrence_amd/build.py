@@ -24,6 +24,9 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed FP32 instructions are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the kernels apply vector arithmetic to
+    # them (row scalings, fp16 conversion), which AGPRs would turn into copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(os.path.dirname(PKG), "include"),
 ]
 

@@ -9,17 +9,17 @@
 // short, length L <= 64). For one chunk and value head h (key head g = h / G),
 // with k^ = rk k, q^ = rq q (rq includes the query scale), g_t the in-chunk
 // cumulative log decay and S0 the state entering the chunk:
-//   A[r,i] = beta_r e^{g_r - g_i} k^_r.k^_i  (i < r),   T = (I + A)^-1
+//   A[r,i] = beta_r e^{g_r - g_i} k^_r.k^_i  (i < r),   T' = (I + A)^-1 diag(beta)
 //   P[r,i] = e^{g_r - g_i} q^_r.k^_i         (i <= r)
 //   X = K S0^T,  Y = Q S0^T                              (raw fp16 k, q)
-//   Z = diag(beta) (V - diag(e^g rk) X),   U = T Z       (U rows: the deltas u_t)
+//   U = T' (V - diag(e^g rk) X)                          (U rows: the deltas u_t)
 //   O = diag(e^g rq) Y + P U
 //   S = e^{g_L} S0 + (diag(e^{g_L - g} rk) U)^T K
-// Everything that does not depend on S0 (Gram matrices, T, P, gates, norms) is
+// Everything that does not depend on S0 (Gram matrices, T', P, gates, norms) is
 // chunk-parallel and done first by gdn_chunk_prep; gdn_chunk_scan then walks
 // the chunks of each sequence in order. The rows of S evolve independently,
-// so the scan splits every head's state into Dv tiles of TV rows, one
-// workgroup each: the serial chain is spread over heads x tiles workgroups.
+// so the scan splits every head's state into Dv tiles, one workgroup each, and
+// every wave of a workgroup runs the whole chain for 16 state rows of its own.
 //
 // Kernels: gdn_chunk_index (chunk offsets per sequence), gdn_chunk_prep,
 // gdn_chunk_scan. Dk = Dv = 128, fp16 I/O only.
@@ -51,12 +51,28 @@ __device__ __forceinline__ half8_t lds8(const _Float16* p) {
   return *reinterpret_cast<const half8_t*>(p);
 }
 
-// Workspace layout: chunk offsets, then per (slot, value head) T and P (fp16
-// 64x64 row-major) and the per-token factors the scan applies (fp32 rows of 64):
-//   kVecZ  e^{g_t} rk_t            kVecBeta beta_t
-//   kVecO  e^{g_t} rq_t            kVecU    e^{g_L - g_t} rk_t
-//   kVecGamma  element 0: e^{g_L}, the decay of the whole chunk
-constexpr int kVecZ = 0, kVecBeta = 1, kVecO = 2, kVecU = 3, kVecGamma = 4, kVecRows = 5;
+// T' and P reach the scan as MFMA operand fragments of v_mfma_f32_16x16x32_f16:
+// the six 16x32 blocks on and below the diagonal (row block rb, column step s),
+// 64 lanes x 8 halves each. Lane (l16 = lane % 16, q = lane / 16) of block f
+// holds row 16 rb + l16 at columns
+//   32 s + 4 q + j        (j = 0..3)
+//   32 s + 16 + 4 q + j-4 (j = 4..7),
+// the column order in which a 16x16 accumulator tile (rows 4q .. 4q+3 in lane
+// group q) of two adjacent row blocks serves as the other operand.
+constexpr int kFrags = 6;
+constexpr int kFragHalves = kFrags * 64 * 8;     // 3072 halves = 6 KiB per (chunk, head)
+__device__ constexpr int kFragRow[kFrags] = {0, 1, 2, 2, 3, 3};
+__device__ constexpr int kFragStep[kFrags] = {0, 0, 0, 1, 0, 1};
+
+__host__ __device__ constexpr int frag_col(int s, int q, int j) {
+  return 32 * s + (j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4));
+}
+
+// Workspace layout: chunk offsets, then per (slot, value head) the T' and P
+// fragments and the per-token factors the scan applies (fp32 rows of 64):
+//   kVecZ  e^{g_t} rk_t            kVecO  e^{g_t} rq_t
+//   kVecU  e^{g_L - g_t} rk_t      kVecGamma  element 0: e^{g_L}, the decay of the whole chunk
+constexpr int kVecZ = 0, kVecO = 1, kVecU = 2, kVecGamma = 3, kVecRows = 4;
 
 struct Ws {
   int32_t* chunk_start;
@@ -68,22 +84,23 @@ struct Ws {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 __host__ __device__ inline Ws ws_layout(void* base, int64_t slots, int R, int Hk, int Hv) {
+  (void)Hk;
   char* p = static_cast<char*>(base);
   Ws w;
   size_t off = 0;
   w.chunk_start = reinterpret_cast<int32_t*>(p + off);
   off += align256((size_t)(R + 1) * 4);
   w.T = reinterpret_cast<_Float16*>(p + off);
-  off += align256((size_t)slots * Hv * C * C * 2);
+  off += align256((size_t)slots * Hv * kFragHalves * 2);
   w.P = reinterpret_cast<_Float16*>(p + off);
-  off += align256((size_t)slots * Hv * C * C * 2);
+  off += align256((size_t)slots * Hv * kFragHalves * 2);
   w.vec = reinterpret_cast<float*>(p + off);
   return w;
 }
 
 __host__ inline size_t ws_bytes(int64_t slots, int R, int Hk, int Hv) {
   (void)Hk;
-  return align256((size_t)(R + 1) * 4) + 2 * align256((size_t)slots * Hv * C * C * 2) +
+  return align256((size_t)(R + 1) * 4) + 2 * align256((size_t)slots * Hv * kFragHalves * 2) +
          align256((size_t)slots * Hv * kVecRows * C * 4);
 }
 
@@ -312,7 +329,6 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
       const float gL = __shfl(la, C - 1, 64);
       float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
       vec[kVecZ * C + t] = expf(la) * sm.rk[t];
-      vec[kVecBeta * C + t] = be;
       vec[kVecO * C + t] = expf(la) * sm.rq[t];
       vec[kVecU * C + t] = expf(gL - la) * sm.rk[t];
       vec[kVecGamma * C + t] = expf(gL);
@@ -387,28 +403,30 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
     }
     lds_barrier();
 
-    // ---- T (fp16) to the workspace: the two waves of a head write 32 rows each
+    // ---- T' = T diag(beta) (fp16 fragments) to the workspace: the two waves of a head
+    // write three fragments each; blocks above the diagonal are zero
     if (hv < nb_heads) {
       const int h = g * p.group + base + hv;
       const float* T = sm.u.m.T[hv];
-      _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * C * C;
+      const float* be = sm.beta[hv];
+      _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * kFragHalves;
+      const int l16 = lane & 15, q = lane >> 4;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int idx = 64 * (4 * half_w + it) + lane;   // 512 pieces of 8 per head
-        const int row = idx >> 3, c8 = (idx & 7) * 8;
-        half8_t hv8 = {};                                // blocks above the diagonal are 0
-        if ((c8 >> 4) <= (row >> 4)) {
-          const float4_t lo = *reinterpret_cast<const float4_t*>(&T[row * AS + c8]);
-          const float4_t hi = *reinterpret_cast<const float4_t*>(&T[row * AS + c8 + 4]);
-          hv8 = half8_t{(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
-                        (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+      for (int fi = 0; fi < 3; ++fi) {
+        const int f = 3 * half_w + fi;
+        const int r = 16 * kFragRow[f] + l16;
+        half8_t x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = frag_col(kFragStep[f], q, j);
+          x[j] = (c >> 4) <= (r >> 4) ? (_Float16)(T[r * AS + c] * be[c]) : (_Float16)0.f;
         }
-        *reinterpret_cast<half8_t*>(Tw + row * C + c8) = hv8;
+        *reinterpret_cast<half8_t*>(Tw + f * 512 + lane * 8) = x;
       }
     }
     lds_barrier();
 
-    // ---- P (fp16) through LDS (the T buffers are free now) to the workspace
+    // ---- P (fp16) through LDS (the T buffers are free now) to the workspace, as fragments
 #pragma unroll
     for (int hvp = 0; hvp < kHeadsPerPass; ++hvp) {
       if (hvp >= nb_heads) break;
@@ -423,12 +441,15 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
     if (hv < nb_heads) {
       const int h = g * p.group + base + hv;
       const _Float16* Ps = reinterpret_cast<const _Float16*>(sm.u.m.T[hv]);
-      _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * C * C;
+      _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * kFragHalves;
+      const int l16 = lane & 15, q = lane >> 4;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int idx = 64 * (4 * half_w + it) + lane;
-        const int row = idx >> 3, c8 = (idx & 7) * 8;
-        *reinterpret_cast<half8_t*>(Pw + row * C + c8) = lds8(&Ps[row * TS + c8]);
+      for (int fi = 0; fi < 3; ++fi) {
+        const int f = 3 * half_w + fi;
+        const _Float16* row = Ps + (16 * kFragRow[f] + l16) * TS;
+        const half4_t lo = *reinterpret_cast<const half4_t*>(row + frag_col(kFragStep[f], q, 0));
+        const half4_t hi = *reinterpret_cast<const half4_t*>(row + frag_col(kFragStep[f], q, 4));
+        *reinterpret_cast<half8_t*>(Pw + f * 512 + lane * 8) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
     lds_barrier();
@@ -436,175 +457,439 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
 }
 
 // ----------------------------------------------------------------------------
-// gdn_chunk_scan: one workgroup per (request, value head, Dv tile of TV rows)
+// gdn_chunk_scan: one workgroup per (request, value head, tile of 32 state rows);
+// each of its two waves owns 16 rows dv of the state and runs the whole chain
+// for them, with no data exchanged between the waves:
+//   X  = K S0^T        (tokens x dv)      A: K rows (LDS)      B: fp16 copy of S0
+//   Y^T = S0 Q^T       (dv x tokens)      A: the same S0 copy  B: Q rows (LDS)
+//   U  = T' (V - zf X)                    A: T' fragments      B: Z, straight from X's accumulators
+//   O^T = of Y^T + U^T P^T                A: U, from accumulators  B: P fragments
+//   S^T = gamma S^T + K^T (uf U)          A: K^T (transposing LDS reads)  B: uf U, from accumulators
+// An accumulator tile (rows 4q .. 4q+3 in lane group q) of two adjacent 16-row
+// blocks is an operand whose 32 contraction indices run in the order of
+// frag_col, which is why T' and P are stored in that order.
 //
-// The state tile is held transposed, S^T [dk][dv], in MFMA accumulators: wave w
-// owns dk rows 32w .. 32w+31 for all TV dv columns. X, Y, Z, U and O are split
-// by token rows: wave w computes tokens 16w .. 16w+15. K and Q of the chunk are
-// staged once, row-major; the update S^T += K^T (uf o U) takes its K^T operand
-// from the row-major tile with transposing LDS reads (ds_read_b64_tr_b16).
+// K, Q and V of a chunk are copied into LDS by buffer loads that write LDS
+// directly, one chunk ahead, into two alternating buffers; one barrier per
+// chunk. K and Q rows are stored without padding, their 16-byte units permuted
+// by an XOR of the row (kv_swizzle) so that the row-fragment reads and the
+// transposing column reads are both free of bank conflicts.
 // ----------------------------------------------------------------------------
-constexpr int VS_PAD = 4;           // V tile row padding (halves)
+constexpr int kScanWaves = 2;                 // waves that compute
+constexpr int kLoaderWaves = 2;               // waves that only copy chunks into LDS
+constexpr int kScanThreads = 64 * (kScanWaves + kLoaderWaves);
+constexpr int kRowsPerWave = 16;
+constexpr int kScanTile = kScanWaves * kRowsPerWave;    // 32 state rows per workgroup
 
-template <int TV>
-struct ScanSmem {
-  _Float16 K[C * KS];      // k of the chunk, [token][dk]
-  _Float16 Q[C * KS];      // q of the chunk, [token][dk]
-  _Float16 T[C * TS];
-  _Float16 P[C * TS];
-  _Float16 V[C * (TV + VS_PAD)];
-  _Float16 S16[TV * KS];   // fp16 copy of the state tile, [dv][dk]
-  _Float16 Zt[TV * TS];    // Z^T  [dv][token]
-  _Float16 Ut[TV * TS];    // U^T  [dv][token]
-  _Float16 Uk[TV * TS];    // (diag(uf) U)^T
-  float zf[C], beta[C], of[C], uf[C];
-  float gamma;
+// 16-byte unit u of row r of a K or Q tile is stored at unit u ^ kv_swizzle(r).
+__device__ __forceinline__ int kv_swizzle(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// 16-byte unit u (of 4) of row r of a V tile is stored at unit u ^ v_swizzle(r).
+__device__ __forceinline__ int v_swizzle(int r) { return ((r >> 2) & 1) << 1; }
+
+// Operands of three chunks in LDS (buffer b = chunk index mod 3). Each piece is an LDS
+// object of its own: the compiler then knows that the direct-to-LDS loads into
+// one buffer do not alias the reads of the other, and does not wait for the
+// loads of the next chunk before reading the current one.
+#define GDN_SCAN_LDS(type, name, count) \
+  __shared__ __attribute__((aligned(16))) type name##0[count]; \
+  __shared__ __attribute__((aligned(16))) type name##1[count]; \
+  __shared__ __attribute__((aligned(16))) type name##2[count];
+GDN_SCAN_LDS(_Float16, lds_K, C * D)            // [token][dk], units permuted by kv_swizzle
+GDN_SCAN_LDS(_Float16, lds_Q, C * D)
+GDN_SCAN_LDS(_Float16, lds_T, kFragHalves)      // T' fragments as stored by gdn_chunk_prep
+GDN_SCAN_LDS(_Float16, lds_P, kFragHalves)
+GDN_SCAN_LDS(_Float16, lds_V, C * kScanTile)    // [token][dv of the tile], units permuted by v_swizzle
+GDN_SCAN_LDS(float, lds_vec, kVecRows * C)
+#undef GDN_SCAN_LDS
+__shared__ __attribute__((aligned(16))) _Float16 lds_S16[kScanWaves][kRowsPerWave * D];  // per wave [dv][dk]
+__shared__ __attribute__((aligned(16))) unsigned lds_touch[2][64];   // discarded L2 prefetch data
+
+template <int B> struct ScanBuf {
+  static __device__ __forceinline__ _Float16* K() { return B == 0 ? lds_K0 : B == 1 ? lds_K1 : lds_K2; }
+  static __device__ __forceinline__ _Float16* Q() { return B == 0 ? lds_Q0 : B == 1 ? lds_Q1 : lds_Q2; }
+  static __device__ __forceinline__ _Float16* T() { return B == 0 ? lds_T0 : B == 1 ? lds_T1 : lds_T2; }
+  static __device__ __forceinline__ _Float16* P() { return B == 0 ? lds_P0 : B == 1 ? lds_P1 : lds_P2; }
+  static __device__ __forceinline__ _Float16* V() { return B == 0 ? lds_V0 : B == 1 ? lds_V1 : lds_V2; }
+  static __device__ __forceinline__ float* vec() { return B == 0 ? lds_vec0 : B == 1 ? lds_vec1 : lds_vec2; }
 };
 
-// Registers holding the next chunk's inputs while the current one computes.
-template <int TV>
-struct Prefetch {
-  static constexpr int VH = TV / 4;   // halves of the V tile per thread (64 rows x TV)
-  half8_t k[4], q[4];                 // row-major pieces of K and Q
-  half8_t t[2], pm[2];
-  _Float16 v[VH];
-  float vec;
-  float gamma;
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Loads of the chunk that starts at token t0 with L tokens (L = 0: all loads
-// return zeros and touch no memory). Every load is a range-checked buffer load.
-template <int TV>
-__device__ __forceinline__ void prefetch_chunk(const ChunkArgs& p, const Ws& w, int slot, int t0, int L,
-                                               int h, int g, int d0, Prefetch<TV>& f) {
-  const int tid = threadIdx.x;
-  const int krow = p.Hk * D;                   // elements between consecutive tokens of k, q
-  const int vrow = p.Hv * D;
-  const size_t kq_base = ((size_t)t0 * p.Hk + g) * D;
-  const int kq_bytes = L > 0 ? ((L - 1) * krow + D) * 2 : 0;
-  const rsrc_t rk = make_rsrc(static_cast<const _Float16*>(p.k) + kq_base, kq_bytes);
-  const rsrc_t rq = make_rsrc(static_cast<const _Float16*>(p.q) + kq_base, kq_bytes);
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = tid + kThreads * it;       // 64 rows x 16 pieces of 8
-    const int row = idx >> 4, c8 = (idx & 15) * 8;
-    f.k[it] = buf_load_h8(rk, (row * krow + c8) * 2);
-    f.q[it] = buf_load_h8(rq, (row * krow + c8) * 2);
+// Lane l of a direct load fills LDS bytes 16 l .. 16 l + 15 of the load's 1 KiB destination.
+__device__ __forceinline__ void load_lds16(rsrc_t r, void* lds, int byte_off, int uniform_off = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, byte_off, uniform_off, 0, 0);
+}
+
+// Copies chunk (slot, t0, L) into LDS buffer B; rows >= L read as zero (L = 0: no
+// memory is read, the buffer fills with zeros). Wave w copies rows 32 w .. 32 w + 31
+// of K, Q and V and fragments 3 w .. 3 w + 2 of T' and P; both waves write the
+// 1 KiB of factors (the same bytes). kStageLoads loads per wave, issued in four
+// parts between the phases of a scan step so that the wave keeps computing while
+// the vector memory path (about 64 bytes per clock per CU) works through them.
+constexpr int kStageLoads = 25;
+constexpr int kTouchLoads = 3;     // L2 prefetch loads per loader wave and chunk
+constexpr int kTouchAhead = 3;     // prefetched this many chunks ahead of the direct loads
+
+template <int B>
+struct Stage {
+  rsrc_t rk, rq, rt, rp, rv, rvec;
+  int krow, vrow, wave, lane;
+
+  __device__ __forceinline__ Stage(const ChunkArgs& p, const Ws& w, int slot, int t0, int L, int h, int g,
+                                   int d0, int wave_, int lane_)
+      : krow(p.Hk * D), vrow(p.Hv * D), wave(wave_), lane(lane_) {
+    const size_t kq_base = ((size_t)t0 * p.Hk + g) * D;
+    const int kq_bytes = L > 0 ? ((L - 1) * krow + D) * 2 : 0;
+    rk = make_rsrc(static_cast<const _Float16*>(p.k) + kq_base, kq_bytes);
+    rq = make_rsrc(static_cast<const _Float16*>(p.q) + kq_base, kq_bytes);
+    const size_t fo = ((size_t)slot * p.Hv + h) * kFragHalves;
+    const int f_bytes = L > 0 ? kFragHalves * 2 : 0;
+    rt = make_rsrc(w.T + fo, f_bytes);
+    rp = make_rsrc(w.P + fo, f_bytes);
+    rv = make_rsrc(static_cast<const _Float16*>(p.v) + ((size_t)t0 * p.Hv + h) * D + d0,
+                   L > 0 ? ((L - 1) * vrow + kScanTile) * 2 : 0);
+    rvec = make_rsrc(w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C, L > 0 ? kVecRows * C * 4 : 0);
   }
-  const int wsz = L > 0 ? C * C * 2 : 0;
-  const rsrc_t rt = make_rsrc(w.T + ((size_t)slot * p.Hv + h) * C * C, wsz);
-  const rsrc_t rp = make_rsrc(w.P + ((size_t)slot * p.Hv + h) * C * C, wsz);
+
+  // K or Q rows 32 wave .. +31: 4 rows of 256 bytes per load; kv_swizzle repeats
+  // every 16 rows, so four per-lane offsets serve all loads and the row block
+  // goes in the uniform offset (8 loads)
+  __device__ __forceinline__ void kq(rsrc_t r, _Float16* dst) const {
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = tid + kThreads * it;       // 512 pieces of 8 halves
-    f.t[it] = buf_load_h8(rt, idx * 16);
-    f.pm[it] = buf_load_h8(rp, idx * 16);
-  }
-  {
-    const rsrc_t rv = make_rsrc(static_cast<const _Float16*>(p.v) + ((size_t)t0 * p.Hv + h) * D + d0,
-                                L > 0 ? ((L - 1) * vrow + TV) * 2 : 0);
-    constexpr int VH = Prefetch<TV>::VH, PER_ROW = TV / VH;
-    const int row = tid / PER_ROW, cc = (tid % PER_ROW) * VH;
-    if constexpr (VH == 8) {
-      const half8_t x = buf_load_h8(rv, (row * vrow + cc) * 2);
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + (lane >> 4);
+      const int off = row * krow * 2 + 16 * ((lane & 15) ^ kv_swizzle(row));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f.v[j] = x[j];
-    } else {
-      const half4_t x = buf_load_h4(rv, (row * vrow + cc) * 2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f.v[j] = x[j];
+      for (int i = 0; i < 2; ++i) {
+        const int blk = 8 * wave + 4 * i + j;          // rows 4 blk .. 4 blk + 3
+        load_lds16(r, dst + 4 * blk * D, off, (32 * wave + 16 * i) * krow * 2);
+      }
     }
   }
-  {
-    const rsrc_t rvec = make_rsrc(w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C,
-                                  L > 0 ? kVecRows * C * 4 : 0);
-    f.vec = buf_load_f32(rvec, tid * 4);       // rows kVecZ .. kVecU, 64 floats each
-    f.gamma = buf_load_f32(rvec, kVecGamma * C * 4);
+  __device__ __forceinline__ void part_k() const { kq(rk, ScanBuf<B>::K()); }
+  __device__ __forceinline__ void part_q() const { kq(rq, ScanBuf<B>::Q()); }
+  // T' and P fragments 3 wave .. +2 (6 loads)
+  __device__ __forceinline__ void part_tp() const {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = 3 * wave + i;
+      load_lds16(rt, ScanBuf<B>::T() + f * 512, lane * 16, f * 1024);
+      load_lds16(rp, ScanBuf<B>::P() + f * 512, lane * 16, f * 1024);
+    }
   }
-}
+  // V rows 32 wave .. +31, 16 rows of 64 bytes per load (v_swizzle repeats every
+  // 8 rows), and the factors (3 loads)
+  __device__ __forceinline__ void part_v() const {
+    const int vr = lane >> 2;
+    const int voff = vr * vrow * 2 + 16 * ((lane & 3) ^ v_swizzle(vr));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = 2 * wave + i;
+      load_lds16(rv, ScanBuf<B>::V() + 16 * blk * kScanTile, voff, 16 * blk * vrow * 2);
+    }
+    load_lds16(rvec, ScanBuf<B>::vec(), lane * 16);
+  }
+  __device__ __forceinline__ void all() const {
+    part_k();
+    part_q();
+    part_tp();
+    part_v();
+  }
+};
 
-// Waits here for the prefetched registers (an empty asm that reads them), so the
-// wait lands at the end of an iteration and the loop header inherits nothing
-// outstanding.
-template <typename V>
-__device__ __forceinline__ void settle(const V& x) {
-  asm volatile("" ::"v"(x));
-}
-
-template <int TV>
-__device__ __forceinline__ void settle_prefetch(const Prefetch<TV>& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    settle(f.k[i]);
-    settle(f.q[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    settle(f.t[i]);
-    settle(f.pm[i]);
-  }
-#pragma unroll
-  for (int j = 0; j < Prefetch<TV>::VH; ++j) settle(f.v[j]);
-  settle(f.vec);
-  settle(f.gamma);
-}
-
-template <int TV>
-__device__ __forceinline__ void stage_chunk(ScanSmem<TV>& sm, const Prefetch<TV>& f) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = tid + kThreads * it;
-    const int row = idx >> 4, c8 = (idx & 15) * 8;
-    *reinterpret_cast<half8_t*>(&sm.K[row * KS + c8]) = f.k[it];
-    *reinterpret_cast<half8_t*>(&sm.Q[row * KS + c8]) = f.q[it];
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = tid + kThreads * it;
-    const int row = idx >> 3, c8 = (idx & 7) * 8;
-    *reinterpret_cast<half8_t*>(&sm.T[row * TS + c8]) = f.t[it];
-    *reinterpret_cast<half8_t*>(&sm.P[row * TS + c8]) = f.pm[it];
-  }
-  {
-    constexpr int VH = Prefetch<TV>::VH, PER_ROW = TV / VH;
-    const int row = tid / PER_ROW, cc = (tid % PER_ROW) * VH;
-#pragma unroll
-    for (int j = 0; j < VH; ++j) sm.V[row * (TV + VS_PAD) + cc + j] = f.v[j];
-  }
-  {
-    const int which = tid >> 6, t = tid & 63;
-    float* dst = which == kVecZ ? sm.zf : which == kVecBeta ? sm.beta : which == kVecO ? sm.of : sm.uf;
-    dst[t] = f.vec;
-    if (tid == 0) sm.gamma = f.gamma;
-  }
+__device__ __forceinline__ half8_t lds_b128(const _Float16* base, int byte_off) {
+  return *reinterpret_cast<const half8_t*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
 
-// MFMA operand holding, for lane (n = lane % 16, q = lane / 16), the eight values
-// X[t0 + 8q + j][n0 + n] (j = 0..7) of a row-major fp16 LDS tile X with row
-// stride `ld` halves: two transposing 64-bit LDS reads. Within each 16-lane group
-// the read hands lane n element e of lane 4e + n/4's 4-element row segment, so
-// lane i addresses row t0 + 8q + 4h + i/4, columns n0 + 4 (i % 4) .. +3.
-// The halves are reinterpreted as whole vectors: element-wise casts of the read's
-// result were folded into a broadcast of element 0 by the compiler.
-__device__ __forceinline__ half8_t lds_col8(const _Float16* X, int ld, int t0, int n0) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, q = lane >> 4;
-  const _Float16* a0 = X + (t0 + 8 * q + (i >> 2)) * ld + n0 + 4 * (i & 3);
-  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(a0));
-  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(a0 + 4 * ld));
-  const half4_t l4 = __builtin_bit_cast(half4_t, lo), h4 = __builtin_bit_cast(half4_t, hi);
-  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+__device__ __forceinline__ half4_t lds_tr4(const _Float16* base, int byte_off) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_t*)(reinterpret_cast<const char*>(base) + byte_off));
+  return __builtin_bit_cast(half4_t, v);
 }
 
-template <int TV>
-__global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_items) {
-  constexpr int NT = D / TV;        // Dv tiles per head
-  constexpr int MB = TV / 16;       // 16-column dv blocks of the tile
-  __shared__ ScanSmem<TV> sm;
+__device__ __forceinline__ half4_t to_half4(float4_t x) {
+  return half4_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+
+__device__ __forceinline__ half8_t cat8(half4_t lo, half4_t hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Loader waves: wait until this wave has at most kStageLoads + 2 kTouchLoads
+// vector memory operations in flight, then the workgroup barrier. Per chunk a
+// loader issues kStageLoads direct loads, then kTouchLoads prefetches; loads
+// complete in issue order, so while any direct load of the chunk the barrier
+// releases (issued two chunks earlier) is pending, so is everything issued after
+// it: at least its own chunk's prefetches and the next chunk's loads and
+// prefetches, more than the limit. No release fence: one would wait for every
+// direct load still in flight (they write LDS).
+__device__ __forceinline__ void loader_barrier() {
+  constexpr int kLimit = kStageLoads + 2 * kTouchLoads;
+  static_assert(kLimit < 64, "vmcnt holds 6 bits");
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in [15:14]
+  constexpr int kWait = (kLimit & 15) | (7 << 4) | (15 << 8) | ((kLimit >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(kWait);
+  __builtin_amdgcn_s_barrier();
+}
+
+// Compute waves: the same barrier; the acquire fence keeps this chunk's LDS reads
+// below it. The reads of the buffer that the loaders refill next returned their
+// data before this wave got here, and the wave-private state copy is never read
+// by another wave, so no release fence is needed.
+__device__ __forceinline__ void compute_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct ScanCtx {
+  const ChunkArgs& p;
+  const Ws& w;
+  int h, g, d0, dvw, wave, lane, beg, end, slot0, nch;
+};
+
+// Output rows (t0 .. t0 + L - 1) of O^T tiles: lane (l16, q) holds dv 4q .. 4q+3 of
+// token 16 nb + l16; rows >= L fall outside the range and are dropped.
+__device__ __forceinline__ void store_out(const ScanCtx& x, const float4_t (&O)[4], int t0, int L) {
+  const int vrow = x.p.Hv * D;
+  const int l16 = x.lane & 15, q = x.lane >> 4;
+  const rsrc_t ro = make_rsrc(static_cast<_Float16*>(x.p.output) + ((size_t)t0 * x.p.Hv + x.h) * D + x.dvw,
+                              L > 0 ? ((L - 1) * vrow + kRowsPerWave) * 2 : 0);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const half4_t o4 = to_half4(O[nb]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_t, o4), ro,
+                                          ((16 * nb + l16) * vrow + 4 * q) * 2, 0, 0);
+  }
+}
+
+// Per-lane LDS byte offsets that do not change from chunk to chunk; every
+// access adds only compile-time constants to one of them.
+struct LaneOffsets {
+  int row[4];     // K / Q / S16 row-fragment reads, per 32-wide k step: row l16, unit (4 ks + q) ^ sw
+  int s16w[8];    // S16 writes, per 16-wide dk block mb: unit (2 mb + q / 2) ^ sw, half q % 2
+  int tr[8];      // K^T transposing reads, per dk block mb (token 4q + l16/4 of the first block)
+  int v;          // V transposing reads
+  int frag;       // T' / P fragment reads
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
+  LaneOffsets o;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int sw = kv_swizzle(l16);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) o.row[ks] = l16 * (D * 2) + 16 * ((4 * ks + q) ^ sw);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) o.s16w[mb] = l16 * (D * 2) + 16 * ((2 * mb + (q >> 1)) ^ sw) + 8 * (q & 1);
+  // token r0 = 32 s + 4 q + l16 / 4 (+16): kv_swizzle depends on r0 % 16 = 4 q + l16 / 4 only
+  const int r0 = 4 * q + (l16 >> 2), swt = kv_swizzle(r0);
+  const int unit = (l16 & 3) >> 1;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) o.tr[mb] = r0 * (D * 2) + 16 * ((2 * mb + unit) ^ swt) + 8 * (l16 & 1);
+  // V: row 16 mb + 4 q + l16 / 4, whose v_swizzle is (q & 1) << 1 for every mb
+  const int col8 = kRowsPerWave * 2 * wave + 8 * (l16 & 3);
+  o.v = (4 * q + (l16 >> 2)) * (kScanTile * 2) + 16 * ((col8 >> 4) ^ ((q & 1) << 1)) + (col8 & 15);
+  o.frag = lane * 16;
+  return o;
+}
+
+// L2 prefetch of chunk (slot, t0, L) for the direct loads a few chunks later:
+// one 4-byte load per 128-byte line into a discarded LDS area. Lines shared by
+// several workgroups are split between them: K and Q of a key head among its
+// nshare = group x tiles workgroups (share index sub), T', P and the factors of
+// a head among its tiles, and a V line (two tiles' 64-byte row pieces) goes to
+// the even tile. Loader 0 takes K, Q and the factors, loader 1 T', P and V:
+// kTouchLoads loads each; a lane without a line gets an offset past the range.
+__device__ __forceinline__ void touch_chunk(const ScanCtx& x, int slot, int t0, int L, int loader, int sub,
+                                            int nshare, int tile) {
+  constexpr int kNone = 0x7FFFFFF0;                // past every range below
+  constexpr int NT = D / kScanTile;
+  const int lane = x.lane;
+  lds_void_t* dst = (lds_void_t*)lds_touch[loader];
+  const size_t fo = ((size_t)slot * x.p.Hv + x.h) * kFragHalves;
+  const int f_bytes = L > 0 ? kFragHalves * 2 : 0;
+  if (loader == 0) {
+    const int krow = x.p.Hk * D;
+    const size_t kq_base = ((size_t)t0 * x.p.Hk + x.g) * D;
+    const int kq_bytes = L > 0 ? ((L - 1) * krow + D) * 2 : 0;
+    const int i = sub + nshare * lane;             // line i: row i / 2, half i % 2 of the 256-byte row
+    const int off = i < 2 * C ? (i >> 1) * krow * 2 + (i & 1) * 128 : kNone;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(static_cast<const _Float16*>(x.p.k) + kq_base, kq_bytes),
+                                             dst, 4, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(static_cast<const _Float16*>(x.p.q) + kq_base, kq_bytes),
+                                             dst, 4, off, 0, 0, 0);
+    const rsrc_t rvec = make_rsrc(x.w.vec + ((size_t)slot * x.p.Hv + x.h) * kVecRows * C,
+                                  (L > 0 && tile == 0) ? kVecRows * C * 4 : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rvec, dst, 4, lane < 8 ? 128 * lane : kNone, 0, 0, 0);
+  } else {
+    const int m = tile + NT * lane;                // fragment line m of 48
+    const int off = m < kFragHalves * 2 / 128 ? 128 * m : kNone;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(x.w.T + fo, f_bytes), dst, 4, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(x.w.P + fo, f_bytes), dst, 4, off, 0, 0, 0);
+    const int vrow = x.p.Hv * D;
+    const rsrc_t rv = make_rsrc(static_cast<const _Float16*>(x.p.v) + ((size_t)t0 * x.p.Hv + x.h) * D + 64 * (tile >> 1),
+                                (L > 0 && (tile & 1) == 0) ? ((L - 1) * vrow + 64) * 2 : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 4, lane * vrow * 2, 0, 0, 0);
+  }
+}
+
+// Loader step: chunk c is in LDS buffer B once the barrier passes; then the loads
+// of chunk c + 2 into buffer (B + 2) mod 3 and the L2 prefetch of chunk c + 2 + kTouchAhead.
+template <int B>
+__device__ __forceinline__ void loader_step(const ScanCtx& x, int c, int loader, int sub, int nshare, int tile) {
+  const bool more = c + 2 < x.nch;
+  const int t0 = x.beg + C * (c + 2);
+  loader_barrier();
+  Stage<(B + 2) % 3>(x.p, x.w, more ? x.slot0 + c + 2 : x.slot0 + c, t0, more ? min(C, x.end - t0) : 0, x.h, x.g,
+                     x.d0, loader, x.lane)
+      .all();
+  const int ca = c + 2 + kTouchAhead;
+  const bool ahead = ca < x.nch;
+  const int ta = x.beg + C * ca;
+  touch_chunk(x, ahead ? x.slot0 + ca : x.slot0, ta, ahead ? min(C, x.end - ta) : 0, loader, sub, nshare, tile);
+}
+
+// Compute step: chunk c from LDS buffer B = c mod 3; stores the output of chunk c - 1.
+template <int B>
+__device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& lo_in, int c, float4_t (&ST)[8],
+                                          float4_t (&O)[4], int& o_t0, int& o_L) {
+  const int lane = x.lane, l16 = lane & 15, q = lane >> 4;
+  const int t0 = x.beg + C * c;
+  const LaneOffsets& lo = lo_in;
+  typedef ScanBuf<B> Buf;
+  const float* vec = Buf::vec();
+  _Float16* const S16w = lds_S16[x.wave];
+  compute_barrier();                                   // chunk c is in LDS buffer B
+  store_out(x, O, o_t0, o_L);
+
+  // ---- fp16 copy of the state rows, [dv][dk] (wave-private)
+  char* const S16 = reinterpret_cast<char*>(S16w);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<half4_t*>(S16 + lo.s16w[mb]) = to_half4(ST[mb]);
+
+  // ---- X = K S0^T (X[mb]: tokens 16 mb + 4q + e, column dv = l16) and Y^T = S0 Q^T
+  // (Yt[nb]: dv 4q + e, token 16 nb + l16); operands of step ks + 1 are read
+  // while the products of step ks run
+  float4_t X[4], Yt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    X[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    Yt[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  half8_t s8[2], k8[2][4], q8[2][4];
+  auto load_xy = [&](int ks, int slot) {
+    s8[slot] = lds_b128(S16w, lo.row[ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k8[slot][i] = lds_b128(Buf::K(), lo.row[ks] + 16 * D * 2 * i);
+      q8[slot][i] = lds_b128(Buf::Q(), lo.row[ks] + 16 * D * 2 * i);
+    }
+  };
+  load_xy(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) load_xy(ks + 1, (ks + 1) & 1);
+    const int sl = ks & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      X[i] = mfma_f16(k8[sl][i], s8[sl], X[i]);
+      Yt[i] = mfma_f16(s8[sl], q8[sl][i], Yt[i]);
+    }
+  }
+
+  // ---- Z = V - zf X (fp16); V rows 16 mb + 4q + e at column l16 by transposing reads
+  half4_t v4[4];
+  float4_t zf[4];
+  half8_t tf[kFrags];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    v4[mb] = lds_tr4(Buf::V(), lo.v + 16 * mb * (kScanTile * 2));
+    zf[mb] = *reinterpret_cast<const float4_t*>(&vec[kVecZ * C + 16 * mb + 4 * q]);
+  }
+#pragma unroll
+  for (int f = 0; f < kFrags; ++f) tf[f] = lds_b128(Buf::T(), lo.frag + f * 1024);
+  half4_t Zh[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    float4_t z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = (float)v4[mb][e] - zf[mb][e] * X[mb][e];
+    Zh[mb] = to_half4(z);
+  }
+
+  // ---- U = T' Z
+  float4_t U[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) U[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int f = 0; f < kFrags; ++f) {
+    const int s2 = 2 * kFragStep[f];
+    U[kFragRow[f]] = mfma_f16(tf[f], cat8(Zh[s2], Zh[s2 + 1]), U[kFragRow[f]]);
+  }
+
+  // ---- O^T = of Y^T + U^T P^T (stored at the next step)
+  half8_t pf[kFrags];
+  float4_t uf[4];
+  float of[4];
+#pragma unroll
+  for (int f = 0; f < kFrags; ++f) pf[f] = lds_b128(Buf::P(), lo.frag + f * 1024);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uf[i] = *reinterpret_cast<const float4_t*>(&vec[kVecU * C + 16 * i + 4 * q]);
+    of[i] = vec[kVecO * C + 16 * i + l16];
+  }
+  half4_t Uh[4], Wh[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    Uh[mb] = to_half4(U[mb]);
+    Wh[mb] = to_half4(uf[mb] * U[mb]);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) O[nb] = of[nb] * Yt[nb];
+#pragma unroll
+  for (int f = 0; f < kFrags; ++f) {
+    const int s2 = 2 * kFragStep[f];
+    O[kFragRow[f]] = mfma_f16(cat8(Uh[s2], Uh[s2 + 1]), pf[f], O[kFragRow[f]]);
+  }
+  o_t0 = t0;
+  o_L = min(C, x.end - t0);
+
+  // ---- S^T = gamma S^T + K^T W, W = uf U; K^T rows dk = 16 mb + i by transposing reads
+  // of tokens 32 s + 4 q + i / 4 (first half) and 16 tokens later (second half)
+  const float gamma = vec[kVecGamma * C];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) ST[mb] *= gamma;
+  // 16 products (s, mb) in groups of four; the transposing reads of group j + 1
+  // are issued before the products of group j
+  half8_t kt[2][4];
+  auto load_kt = [&](int grp, int slot) {
+    const int s = grp >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mb = 4 * (grp & 1) + i;
+      const half4_t a0 = lds_tr4(Buf::K(), lo.tr[mb] + 32 * s * (D * 2));
+      const half4_t a1 = lds_tr4(Buf::K(), lo.tr[mb] + (32 * s + 16) * (D * 2));
+      kt[slot][i] = cat8(a0, a1);
+    }
+  };
+  const half8_t w8[2] = {cat8(Wh[0], Wh[1]), cat8(Wh[2], Wh[3])};
+  load_kt(0, 0);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    if (grp < 3) load_kt(grp + 1, (grp + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mb = 4 * (grp & 1) + i;
+      ST[mb] = mfma_f16(kt[grp & 1][i], w8[grp >> 1], ST[mb]);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_items) {
+  constexpr int NT = D / kScanTile;     // tiles per head
 
   // XCD-aware order: consecutive items (same request and key head) share an XCD's L2
   const int per_xcd = (int)(gridDim.x / 8);
@@ -617,10 +902,11 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
   const int g = rest % p.Hk;
   const int req = rest / p.Hk;
   const int h = g * p.group + hv;
-  const int d0 = tile * TV;
+  const int d0 = tile * kScanTile;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, q4 = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, q = lane >> 4;
 
   const int beg = clamp_cu(p.cu_seqlens, req, p.N);
   const int end = max(clamp_cu(p.cu_seqlens, req + 1, p.N), beg);
@@ -628,172 +914,72 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_scan(ChunkArgs p, Ws w, in
   int nch = (end - beg + C - 1) / C;
   nch = max(0, min(nch, p.max_chunks - slot0));
 
-  // ---- state tile, transposed: ST[i][nb] holds S[dv = d0+16nb+l16][dk = 32*wave+16i+4q4+e]
-  float4_t ST[2][MB];
+  if (wave >= kScanWaves) {
+    // ---- loader waves: chunks 0 and 1 (a missing chunk has length 0: its loads
+    // read nothing), then chunk c + 2 after the barrier of chunk c
+    const int loader = wave - kScanWaves;
+    ScanCtx x{p, w, h, g, d0, 0, loader, lane, beg, end, slot0, nch};
+    Stage<0>(p, w, slot0, beg, nch > 0 ? min(C, end - beg) : 0, h, g, d0, loader, lane).all();
+    Stage<1>(p, w, nch > 1 ? slot0 + 1 : slot0, beg + C, nch > 1 ? min(C, end - beg - C) : 0, h, g, d0, loader,
+             lane)
+        .all();
+    // L2 prefetch of chunks 2 .. 2 + kTouchAhead - 1 (the later ones go with the loader steps)
+    const int sub = hv * NT + tile, nshare = p.group * NT;
+#pragma unroll
+    for (int ca = 2; ca < 2 + kTouchAhead; ++ca) {
+      const bool ahead = ca < nch;
+      const int ta = beg + C * ca;
+      touch_chunk(x, ahead ? slot0 + ca : slot0, ta, ahead ? min(C, end - ta) : 0, loader, sub, nshare, tile);
+    }
+    int c = 0;
+    for (; c + 2 < nch; c += 3) {
+      loader_step<0>(x, c, loader, sub, nshare, tile);
+      loader_step<1>(x, c + 1, loader, sub, nshare, tile);
+      loader_step<2>(x, c + 2, loader, sub, nshare, tile);
+    }
+    if (c < nch) loader_step<0>(x, c, loader, sub, nshare, tile);
+    if (c + 1 < nch) loader_step<1>(x, c + 1, loader, sub, nshare, tile);
+    return;
+  }
+
+  // ---- state rows of this wave, transposed: ST[mb] = S[dv][dk = 16 mb + 4 q + e], dv = dvw + l16
+  const int dvw = d0 + kRowsPerWave * wave;
+  float4_t ST[8];
   const size_t head_off = ((size_t)req * p.Hv + h) * D * D;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      const int dv = d0 + 16 * nb + l16, dk = 32 * wave + 16 * i + 4 * q4;
-      ST[i][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-      if (p.initial_state != nullptr)
-        ST[i][nb] = *reinterpret_cast<const float4_t*>(p.initial_state + head_off + (size_t)dv * D + dk);
-    }
-
-  Prefetch<TV> f;
-  prefetch_chunk<TV>(p, w, slot0, beg, nch > 0 ? min(C, end - beg) : 0, h, g, d0, f);
-  settle_prefetch<TV>(f);
-
-  _Float16* op = static_cast<_Float16*>(p.output);
-  for (int c = 0; c < nch; ++c) {
-    const int t0 = beg + C * c;
-    const int L = min(C, end - t0);
-    const bool more = c + 1 < nch;
-    const int tn = t0 + C;
-    const int Ln = more ? min(C, end - tn) : 0;       // 0: the prefetch below loads nothing
-    const int slot_n = more ? slot0 + c + 1 : slot0 + c;
-    // ---- chunk inputs and the fp16 state copy into LDS
-    stage_chunk<TV>(sm, f);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int nb = 0; nb < MB; ++nb) {
-        half4_t s4 = {(_Float16)ST[i][nb][0], (_Float16)ST[i][nb][1], (_Float16)ST[i][nb][2],
-                      (_Float16)ST[i][nb][3]};
-        *reinterpret_cast<half4_t*>(&sm.S16[(16 * nb + l16) * KS + 32 * wave + 16 * i + 4 * q4]) = s4;
-      }
-    lds_barrier();
-    prefetch_chunk<TV>(p, w, slot_n, tn, Ln, h, g, d0, f);
-
-    // ---- X = K S0^T and Y = Q S0^T for tokens 16*wave .. +15
-    float4_t X[MB], Y[MB];
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      X[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-      Y[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int col = 32 * ks + 8 * q4;
-      const half8_t ak = lds8(&sm.K[(16 * wave + l16) * KS + col]);
-      const half8_t aq = lds8(&sm.Q[(16 * wave + l16) * KS + col]);
-#pragma unroll
-      for (int nb = 0; nb < MB; ++nb) {
-        const half8_t bs = lds8(&sm.S16[(16 * nb + l16) * KS + col]);
-        X[nb] = mfma_f16(ak, bs, X[nb]);
-        Y[nb] = mfma_f16(aq, bs, Y[nb]);
-      }
-    }
-    // ---- Z = beta (V - zf X) -> Zt[dv][token]
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      half4_t z4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * wave + 4 * q4 + e;
-        const float vv = (float)sm.V[t * (TV + VS_PAD) + 16 * nb + l16];
-        z4[e] = (_Float16)(sm.beta[t] * (vv - sm.zf[t] * X[nb][e]));
-      }
-      *reinterpret_cast<half4_t*>(&sm.Zt[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = z4;
-    }
-    lds_barrier();
-
-    // ---- U = T Z (T is lower triangular: tokens beyond this row block add nothing)
-    float4_t U[MB];
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb) U[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (32 * ks <= 16 * wave + 15) {
-        const int col = 32 * ks + 8 * q4;
-        const half8_t at = lds8(&sm.T[(16 * wave + l16) * TS + col]);
-#pragma unroll
-        for (int nb = 0; nb < MB; ++nb) {
-          const half8_t bz = lds8(&sm.Zt[(16 * nb + l16) * TS + col]);
-          U[nb] = mfma_f16(at, bz, U[nb]);
-        }
-      }
-    }
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      half4_t u4, w4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * wave + 4 * q4 + e;
-        u4[e] = (_Float16)U[nb][e];
-        w4[e] = (_Float16)(sm.uf[t] * U[nb][e]);
-      }
-      *reinterpret_cast<half4_t*>(&sm.Ut[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = u4;
-      *reinterpret_cast<half4_t*>(&sm.Uk[(16 * nb + l16) * TS + 16 * wave + 4 * q4]) = w4;
-    }
-    lds_barrier();
-
-    // ---- O = diag(of) Y + P U  -> output rows < L
-    float4_t O[MB];
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) O[nb][e] = sm.of[16 * wave + 4 * q4 + e] * Y[nb][e];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (32 * ks <= 16 * wave + 15) {
-        const int col = 32 * ks + 8 * q4;
-        const half8_t ap = lds8(&sm.P[(16 * wave + l16) * TS + col]);
-#pragma unroll
-        for (int nb = 0; nb < MB; ++nb) {
-          const half8_t bu = lds8(&sm.Ut[(16 * nb + l16) * TS + col]);
-          O[nb] = mfma_f16(ap, bu, O[nb]);
-        }
-      }
-    }
-    {
-      const int vrow = p.Hv * D;
-      const rsrc_t ro = make_rsrc(op + ((size_t)t0 * p.Hv + h) * D + d0, ((L - 1) * vrow + TV) * 2);
-#pragma unroll
-      for (int nb = 0; nb < MB; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * wave + 4 * q4 + e;   // rows t >= L fall outside the range: dropped
-          buf_store_h1((_Float16)O[nb][e], ro, (t * vrow + 16 * nb + l16) * 2);
-        }
-    }
-
-    // ---- S^T = gamma S^T + K^T (uf o U)   (wave: dk rows 32*wave .. +31)
-    const float decay_L = sm.gamma;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int nb = 0; nb < MB; ++nb) ST[i][nb] *= decay_L;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int col = 32 * ks + 8 * q4;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const half8_t ak = lds_col8(sm.K, KS, 32 * ks, 32 * wave + 16 * i);
-#pragma unroll
-        for (int nb = 0; nb < MB; ++nb) {
-          const half8_t bu = lds8(&sm.Uk[(16 * nb + l16) * TS + col]);
-          ST[i][nb] = mfma_f16(ak, bu, ST[i][nb]);
-        }
-      }
-    }
-    settle_prefetch<TV>(f);
-    lds_barrier();   // all LDS reads of this chunk are done before the next stage
+  for (int mb = 0; mb < 8; ++mb) {
+    ST[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (p.initial_state != nullptr)
+      ST[mb] = *reinterpret_cast<const float4_t*>(p.initial_state + head_off + (size_t)(dvw + l16) * D +
+                                                  16 * mb + 4 * q);
   }
 
+  ScanCtx x{p, w, h, g, d0, dvw, wave, lane, beg, end, slot0, nch};
+  const LaneOffsets lo = lane_offsets(wave, lane);
+  float4_t O[4];
+  int o_t0 = beg, o_L = 0;                 // output rows of the previous chunk, stored one step late
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) O[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // three chunks per iteration, one LDS buffer each (one barrier per chunk, as the loaders)
+  int c = 0;
+  for (; c + 2 < nch; c += 3) {
+    scan_step<0>(x, lo, c, ST, O, o_t0, o_L);
+    scan_step<1>(x, lo, c + 1, ST, O, o_t0, o_L);
+    scan_step<2>(x, lo, c + 2, ST, O, o_t0, o_L);
+  }
+  if (c < nch) scan_step<0>(x, lo, c, ST, O, o_t0, o_L);
+  if (c + 1 < nch) scan_step<1>(x, lo, c + 1, ST, O, o_t0, o_L);
+
+  // ---- output of the last chunk, final state
+  __builtin_amdgcn_s_waitcnt(0);
+  store_out(x, O, o_t0, o_L);
   if (p.final_state != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int nb = 0; nb < MB; ++nb) {
-        const int dv = d0 + 16 * nb + l16, dk = 32 * wave + 16 * i + 4 * q4;
-        *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)dv * D + dk) = ST[i][nb];
-      }
+    for (int mb = 0; mb < 8; ++mb)
+      *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)(dvw + l16) * D + 16 * mb + 4 * q) = ST[mb];
   }
 }
-
-constexpr int kScanTile = 32;
 
 size_t chunk_workspace_bytes(int64_t chunk_slots, int R, int Hk, int Hv) {
   return ws_bytes(chunk_slots, R, Hk, Hv);
@@ -809,8 +995,7 @@ hipError_t launch_chunk(const ChunkArgs& p, int io_dtype, hipStream_t stream) {
                        0, stream, p, w);
   const int n_items = p.R * p.Hv * (D / kScanTile);
   const int grid = (n_items + 7) / 8 * 8;
-  hipLaunchKernelGGL(gdn_chunk_scan<kScanTile>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p, w,
-                     n_items);
+  hipLaunchKernelGGL(gdn_chunk_scan, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, p, w, n_items);
   return hipGetLastError();
 }
 
