@@ -32,8 +32,6 @@ namespace {
 
 constexpr int C = kChunk;     // 64 tokens per chunk
 constexpr int D = 128;        // Dk = Dv
-constexpr int KS = D + 8;     // LDS row stride (halves) of 128-wide fp16 tiles
-constexpr int TS = C + 8;     // LDS row stride (halves) of 64-wide fp16 tiles
 constexpr int AS = C + 4;     // LDS row stride (floats) of the fp32 A matrix
 constexpr int kThreads = 256;
 
@@ -47,9 +45,6 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
-__device__ __forceinline__ half8_t lds8(const _Float16* p) {
-  return *reinterpret_cast<const half8_t*>(p);
-}
 
 // T' and P reach the scan as MFMA operand fragments of v_mfma_f32_16x16x32_f16:
 // the six 16x32 blocks on and below the diagonal (row block rb, column step s),
@@ -163,35 +158,6 @@ __device__ __forceinline__ bool locate_chunk(const ChunkArgs& p, const Ws& w, in
   return *len > 0;
 }
 
-// ----------------------------------------------------------------------------
-// gdn_chunk_prep: one workgroup per (chunk slot, key head)
-//
-// T = (I + A)^-1 of every value head is built blockwise from 16x16 blocks:
-// the four diagonal blocks by forward substitution (one lane per column), then
-// the blocks below the diagonal column by column,
-//   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj,
-// on fp32 MFMA into a buffer of its own (A stays intact). Block columns are
-// independent of each other, so two waves share a head: one sweeps column 0,
-// the other columns 1 and 2; two heads are in flight at once.
-// ----------------------------------------------------------------------------
-constexpr int kHeadsPerPass = 2;
-
-struct PrepSmem {
-  union {
-    struct {
-      _Float16 K[C * KS];
-      _Float16 Q[C * KS];
-    } in;
-    struct {
-      float A[kHeadsPerPass][C * AS];   // A of the heads of one pass
-      float T[kHeadsPerPass][C * AS];   // their T (blocks on and below the diagonal)
-    } m;
-  } u;
-  float wtmp[4][16 * 17];             // per-wave 16x16 staging for MFMA operands
-  float rk[C], rq[C];
-  float g[kHeadsPerPass][C], beta[kHeadsPerPass][C];
-};
-
 __device__ __forceinline__ float4_t mfma_f32(float a, float b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -224,236 +190,6 @@ __device__ __forceinline__ void t_offdiag_block(const float* A, float* T, float*
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) T[(16 * ib + 4 * kq + e) * AS + 16 * jb + m] = -Tb[e];
-}
-
-__global__ void __launch_bounds__(kThreads) gdn_chunk_prep(ChunkArgs p, Ws w) {
-  __shared__ PrepSmem sm;
-  const int slot = blockIdx.x;
-  const int g = blockIdx.y;
-  int req, t0, L;
-  if (!locate_chunk(p, w, slot, &req, &t0, &L)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const _Float16* kp = static_cast<const _Float16*>(p.k);
-  const _Float16* qp = static_cast<const _Float16*>(p.q);
-
-  // gate inputs of the first pass, loaded early (wave w < heads of the pass: head g*G + w);
-  // tokens >= L and heads past the group read as zero
-  const int gate_bytes = ((L - 1) * p.Hv + 1) * 4;
-  float a_pf, b_pf;
-  {
-    const bool on = wave < min(kHeadsPerPass, p.group);
-    const int h = g * p.group + (on ? wave : 0);
-    a_pf = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + h, on ? gate_bytes : 0), lane * p.Hv * 4);
-    b_pf = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + h, on ? gate_bytes : 0), lane * p.Hv * 4);
-  }
-
-  // ---- K, Q chunk tiles into LDS (rows >= L zero); 16 lanes per row, so the
-  // per-token sums of squares reduce across those 16 lanes
-  float ssk[4], ssq[4];
-  const int krow = p.Hk * D;
-  const rsrc_t rk = make_rsrc(kp + ((size_t)t0 * p.Hk + g) * D, ((L - 1) * krow + D) * 2);
-  const rsrc_t rq = make_rsrc(qp + ((size_t)t0 * p.Hk + g) * D, ((L - 1) * krow + D) * 2);
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = tid + kThreads * it;    // 1024 16-byte pieces per tile
-    const int row = idx >> 4, c8 = (idx & 15) * 8;
-    const half8_t kv = buf_load_h8(rk, (row * krow + c8) * 2);   // rows >= L read as zero
-    const half8_t qv = buf_load_h8(rq, (row * krow + c8) * 2);
-    *reinterpret_cast<half8_t*>(&sm.u.in.K[row * KS + c8]) = kv;
-    *reinterpret_cast<half8_t*>(&sm.u.in.Q[row * KS + c8]) = qv;
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sk = fmaf((float)kv[j], (float)kv[j], sk);
-      sq = fmaf((float)qv[j], (float)qv[j], sq);
-    }
-    ssk[it] = group_sum<16>(sk);
-    ssq[it] = group_sum<16>(sq);
-  }
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = tid + kThreads * it;
-    if ((idx & 15) == 0) {
-      const int row = idx >> 4;
-      const float rk = rsqrtf(ssk[it] + kNormEps);
-      const float rq = rsqrtf(ssq[it] + kNormEps) * p.scale;
-      sm.rk[row] = rk;
-      sm.rq[row] = rq;
-    }
-  }
-  lds_barrier();
-
-  // ---- Gram matrices K K^T and Q K^T, rows 16*wave .. +15, column blocks <= wave
-  float4_t kk[4], qk[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    kk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    qk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (nb <= wave) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int col = 32 * ks + 8 * (lane >> 4);
-        const half8_t ak = lds8(&sm.u.in.K[(16 * wave + (lane & 15)) * KS + col]);
-        const half8_t aq = lds8(&sm.u.in.Q[(16 * wave + (lane & 15)) * KS + col]);
-        const half8_t bk = lds8(&sm.u.in.K[(16 * nb + (lane & 15)) * KS + col]);
-        kk[nb] = mfma_f16(ak, bk, kk[nb]);
-        qk[nb] = mfma_f16(aq, bk, qk[nb]);
-      }
-    }
-  }
-  lds_barrier();   // K, Q tiles are dead from here; their LDS becomes A
-
-  for (int base = 0; base < p.group; base += kHeadsPerPass) {
-    const int nb_heads = min(kHeadsPerPass, p.group - base);
-    // ---- gates and in-chunk cumulative log decay: wave hv handles head base + hv
-    if (wave < nb_heads) {
-      const int h = g * p.group + base + wave;
-      const int t = lane;
-      float la = 0.f, be = 0.f;
-      if (t < L) {
-        la = -expf(p.A_log[h]) * softplus_f(a_pf + p.dt_bias[h]);
-        be = sigmoid_f(b_pf);
-      }
-      // the next pass's gate inputs, in flight while this pass computes
-      const bool on = base + kHeadsPerPass + wave < p.group;
-      const int hn = on ? h + kHeadsPerPass : h;
-      a_pf = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + hn, on ? gate_bytes : 0), t * p.Hv * 4);
-      b_pf = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + hn, on ? gate_bytes : 0), t * p.Hv * 4);
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {      // inclusive prefix sum over the 64 lanes
-        const float y = __shfl_up(la, d, 64);
-        if (t >= d) la += y;
-      }
-      sm.g[wave][t] = la;
-      sm.beta[wave][t] = be;
-      const float gL = __shfl(la, C - 1, 64);
-      float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
-      vec[kVecZ * C + t] = expf(la) * sm.rk[t];
-      vec[kVecO * C + t] = expf(la) * sm.rq[t];
-      vec[kVecU * C + t] = expf(gL - la) * sm.rk[t];
-      vec[kVecGamma * C + t] = expf(gL);
-    }
-    lds_barrier();
-
-    // ---- A (fp32, LDS) and P (fp16, kept in registers until T is out) from the Gram
-    half4_t pk[kHeadsPerPass][4];
-#pragma unroll
-    for (int hv = 0; hv < kHeadsPerPass; ++hv) {
-      if (hv >= nb_heads) break;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int i = 16 * nb + (lane & 15);            // column (earlier token)
-        const float gi = sm.g[hv][i], rki = sm.rk[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * wave + 4 * (lane >> 4) + e;  // row (later token)
-          const float gr = sm.g[hv][r];
-          float av = 0.f, pv = 0.f;
-          if (nb <= wave) {
-            const float dec = fast_exp(fminf(gr - gi, 0.f));
-            if (i < r) av = sm.beta[hv][r] * dec * sm.rk[r] * rki * kk[nb][e];
-            if (i <= r) pv = dec * sm.rq[r] * rki * qk[nb][e];
-          }
-          sm.u.m.A[hv][r * AS + i] = av;
-          pk[hv][nb][e] = (_Float16)pv;
-        }
-      }
-    }
-    lds_barrier();
-
-    // ---- T, step 1: the four diagonal 16x16 blocks (wave 2*hv, lane = 16*block + column)
-    const int hv = wave >> 1, half_w = wave & 1;
-    if (hv < nb_heads && half_w == 0) {
-      const float* A = sm.u.m.A[hv];
-      float* T = sm.u.m.T[hv];
-      const int blk = lane >> 4, j = lane & 15;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float* arow = &A[(16 * blk + r) * AS + 16 * blk];
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; i += 4) {
-          const float4_t a4 = *reinterpret_cast<const float4_t*>(&arow[i]);
-          s0 = fmaf(a4.x, x[i], s0);
-          s1 = fmaf(a4.y, x[i + 1], s1);
-          s2 = fmaf(a4.z, x[i + 2], s2);
-          s3 = fmaf(a4.w, x[i + 3], s3);
-        }
-        x[r] = (r == j ? 1.f : 0.f) - ((s0 + s1) + (s2 + s3));
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) T[(16 * blk + r) * AS + 16 * blk + j] = x[r];
-    }
-    lds_barrier();
-
-    // ---- T, step 2: blocks below the diagonal; wave 2*hv: column 0, wave 2*hv+1: columns 1, 2
-    if (hv < nb_heads) {
-      const float* A = sm.u.m.A[hv];
-      float* T = sm.u.m.T[hv];
-      float* wt = sm.wtmp[wave];
-      if (half_w == 0) {
-        for (int ib = 1; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, 0, lane);
-      } else {
-        for (int ib = 2; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, 1, lane);
-        t_offdiag_block(A, T, wt, 3, 2, lane);
-      }
-    }
-    lds_barrier();
-
-    // ---- T' = T diag(beta) (fp16 fragments) to the workspace: the two waves of a head
-    // write three fragments each; blocks above the diagonal are zero
-    if (hv < nb_heads) {
-      const int h = g * p.group + base + hv;
-      const float* T = sm.u.m.T[hv];
-      const float* be = sm.beta[hv];
-      _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * kFragHalves;
-      const int l16 = lane & 15, q = lane >> 4;
-#pragma unroll
-      for (int fi = 0; fi < 3; ++fi) {
-        const int f = 3 * half_w + fi;
-        const int r = 16 * kFragRow[f] + l16;
-        half8_t x;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = frag_col(kFragStep[f], q, j);
-          x[j] = (c >> 4) <= (r >> 4) ? (_Float16)(T[r * AS + c] * be[c]) : (_Float16)0.f;
-        }
-        *reinterpret_cast<half8_t*>(Tw + f * 512 + lane * 8) = x;
-      }
-    }
-    lds_barrier();
-
-    // ---- P (fp16) through LDS (the T buffers are free now) to the workspace, as fragments
-#pragma unroll
-    for (int hvp = 0; hvp < kHeadsPerPass; ++hvp) {
-      if (hvp >= nb_heads) break;
-      _Float16* Ps = reinterpret_cast<_Float16*>(sm.u.m.T[hvp]);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Ps[(16 * wave + 4 * (lane >> 4) + e) * TS + 16 * nb + (lane & 15)] = pk[hvp][nb][e];
-    }
-    lds_barrier();
-    if (hv < nb_heads) {
-      const int h = g * p.group + base + hv;
-      const _Float16* Ps = reinterpret_cast<const _Float16*>(sm.u.m.T[hv]);
-      _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * kFragHalves;
-      const int l16 = lane & 15, q = lane >> 4;
-#pragma unroll
-      for (int fi = 0; fi < 3; ++fi) {
-        const int f = 3 * half_w + fi;
-        const _Float16* row = Ps + (16 * kFragRow[f] + l16) * TS;
-        const half4_t lo = *reinterpret_cast<const half4_t*>(row + frag_col(kFragStep[f], q, 0));
-        const half4_t hi = *reinterpret_cast<const half4_t*>(row + frag_col(kFragStep[f], q, 4));
-        *reinterpret_cast<half8_t*>(Pw + f * 512 + lane * 8) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    }
-    lds_barrier();
-  }
 }
 
 // ----------------------------------------------------------------------------
@@ -981,6 +717,248 @@ __global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w
   }
 }
 
+// ----------------------------------------------------------------------------
+// gdn_chunk_prep: one workgroup per (chunk slot, value head h); key head g = h / G
+//
+//   K, Q tiles -> LDS (direct loads, the scan's swizzled layout); gates of h
+//   Gram tiles on fp16 MFMA, wave w = row block w:
+//     KK[w][nb] = K_w K_nb^T, KQ[nb][w] = K_nb Q_w^T (nb <= w), QQ[w][w]
+//   norms from the Gram diagonals: rk_t = (k_t.k_t + eps)^-1/2, rq_t likewise times the scale
+//   A (fp32, LDS) from KK; P straight from KQ: the accumulator tile of K_nb Q_w^T holds,
+//   in lane (l16, q), P[16 w + l16][16 nb + 4 q + e], which is P's MFMA fragment
+//   layout (frag_col) for row block w
+//   T = (I + A)^-1 blockwise from 16x16 blocks: the diagonal blocks by forward
+//   substitution, the blocks below the diagonal column by column,
+//     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj,
+//   on fp32 MFMA (waves 0, 1, 2 take block columns 0, 1, 2); T' = T diag(beta).
+// The K, Q tiles are dead once the Gram tiles are in registers; A and T reuse
+// their LDS, which keeps a workgroup at 40 KiB (four per CU).
+// ----------------------------------------------------------------------------
+constexpr int kPrepThreads = 256;
+
+struct PrepSmem {
+  union {
+    _Float16 kq[2][C * D];        // K, Q tiles, units permuted by kv_swizzle
+    struct {
+      float A[C * AS];
+      float T[C * AS];            // blocks on and below the diagonal
+    } m;
+  } u;
+  float wtmp[4][16 * 17];         // per-wave 16x16 staging for MFMA operands
+  float g[C], beta[C], rk[C], rq[C];
+};
+
+// row block of the Gram/P tiles -> fragment indices (kFragRow / kFragStep order)
+__device__ __forceinline__ int frag_index(int rb, int s) { return rb == 3 ? 4 + s : rb == 2 ? 2 + s : rb; }
+
+__global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w, int n_items) {
+  __shared__ PrepSmem sm;
+  // XCD-aware order: the value heads of one chunk and key head share an XCD's L2
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int slot = item / p.Hv, h = item % p.Hv, g = h / p.group;
+  int req, t0, L;
+  if (!locate_chunk(p, w, slot, &req, &t0, &L)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q = lane >> 4;
+
+  // ---- K, Q tiles into LDS (rows >= L read as zero): wave w copies rows 16 w .. 16 w + 15
+  {
+    const int krow = p.Hk * D;
+    const size_t kq_base = ((size_t)t0 * p.Hk + g) * D;
+    const int kq_bytes = ((L - 1) * krow + D) * 2;
+    const rsrc_t rk = make_rsrc(static_cast<const _Float16*>(p.k) + kq_base, kq_bytes);
+    const rsrc_t rq = make_rsrc(static_cast<const _Float16*>(p.q) + kq_base, kq_bytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + (lane >> 4);
+      const int off = row * krow * 2 + 16 * ((lane & 15) ^ kv_swizzle(row));
+      const int blk = 4 * wave + j;                       // rows 4 blk .. 4 blk + 3
+      load_lds16(rk, sm.u.kq[0] + 4 * blk * D, off, 16 * wave * krow * 2);
+      load_lds16(rq, sm.u.kq[1] + 4 * blk * D, off, 16 * wave * krow * 2);
+    }
+  }
+
+  // ---- gates of head h (wave 0, while the loads are in flight): cumulative log decay, beta
+  if (wave == 0) {
+    const int t = lane;
+    const int gate_bytes = ((L - 1) * p.Hv + 1) * 4;      // tokens >= L read as zero
+    const float a = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
+    const float b = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
+    float la = 0.f, be = 0.f;
+    if (t < L) {
+      la = -expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]);
+      be = sigmoid_f(b);
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {            // inclusive prefix sum over the 64 lanes
+      const float y = __shfl_up(la, d, 64);
+      if (t >= d) la += y;
+    }
+    sm.g[t] = la;
+    sm.beta[t] = be;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+
+  // ---- Gram tiles of row block wave
+  const _Float16* Kt = sm.u.kq[0];
+  const _Float16* Qt = sm.u.kq[1];
+  float4_t kk[4], kq[4], qq = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    kk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    kq[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int sw = kv_swizzle(l16);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int uoff = 16 * ((4 * ks + q) ^ sw);
+    const half8_t kw = lds_b128(Kt, (16 * wave + l16) * (D * 2) + uoff);
+    const half8_t qw = lds_b128(Qt, (16 * wave + l16) * (D * 2) + uoff);
+    half8_t kn[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) kn[nb] = lds_b128(Kt, (16 * nb + l16) * (D * 2) + uoff);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if (nb <= wave) {
+        kk[nb] = mfma_f16(kw, kn[nb], kk[nb]);    // KK[16 w + 4q + e][16 nb + l16]
+        kq[nb] = mfma_f16(kn[nb], qw, kq[nb]);    // QK[16 w + l16][16 nb + 4q + e]
+      }
+    }
+    qq = mfma_f16(qw, qw, qq);
+  }
+  // norms: the diagonal element of row 16 w + l16 sits in lane group q = l16 / 4, element e = l16 % 4
+  {
+    float4_t kd = kk[0];
+#pragma unroll
+    for (int nb = 1; nb < 4; ++nb)
+      if (nb == wave) kd = kk[nb];
+    const int e = l16 & 3;
+    const float kdiag = e == 0 ? kd[0] : e == 1 ? kd[1] : e == 2 ? kd[2] : kd[3];
+    const float qdiag = e == 0 ? qq[0] : e == 1 ? qq[1] : e == 2 ? qq[2] : qq[3];
+    if (q == (l16 >> 2)) {
+      sm.rk[16 * wave + l16] = rsqrtf(kdiag + kNormEps);
+      sm.rq[16 * wave + l16] = rsqrtf(qdiag + kNormEps) * p.scale;
+    }
+  }
+  lds_barrier();                                   // K, Q tiles dead from here; their LDS becomes A, T
+
+  // ---- per-token factors (wave 0)
+  if (wave == 0) {
+    const int t = lane;
+    const float gt = sm.g[t], gL = sm.g[C - 1];
+    float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
+    vec[kVecZ * C + t] = expf(gt) * sm.rk[t];
+    vec[kVecO * C + t] = expf(gt) * sm.rq[t];
+    vec[kVecU * C + t] = expf(gL - gt) * sm.rk[t];
+    vec[kVecGamma * C + t] = expf(gL);
+  }
+
+  // ---- A rows 16 w + 4q + e (blocks nb <= w; the blocks above are never read)
+  {
+    float gr[4], br[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * wave + 4 * q + e;
+      gr[e] = sm.g[r];
+      br[e] = sm.beta[r] * sm.rk[r];
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if (nb <= wave) {
+        const int i = 16 * nb + l16;
+        const float gi = sm.g[i], rki = sm.rk[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * wave + 4 * q + e;
+          const float av = i < r ? br[e] * fast_exp(fminf(gr[e] - gi, 0.f)) * rki * kk[nb][e] : 0.f;
+          sm.u.m.A[r * AS + i] = av;
+        }
+      }
+    }
+  }
+
+  // ---- P fragments of row block w straight from the KQ tiles: row r = 16 w + l16,
+  // columns i = 16 nb + 4q + e
+  {
+    const int r = 16 * wave + l16;
+    const float gr = sm.g[r], rqr = sm.rq[r];
+    half4_t ph[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const float4_t gi = *reinterpret_cast<const float4_t*>(&sm.g[16 * nb + 4 * q]);
+      const float4_t ki = *reinterpret_cast<const float4_t*>(&sm.rk[16 * nb + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * nb + 4 * q + e;
+        ph[nb][e] = (_Float16)(nb <= wave && i <= r ? fast_exp(fminf(gr - gi[e], 0.f)) * rqr * ki[e] * kq[nb][e]
+                                                     : 0.f);
+      }
+    }
+    _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * kFragHalves;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (2 * s <= wave)
+        *reinterpret_cast<half8_t*>(Pw + frag_index(wave, s) * 512 + lane * 8) = cat8(ph[2 * s], ph[2 * s + 1]);
+  }
+  lds_barrier();
+
+  // ---- T, step 1: the four diagonal 16x16 blocks (wave 0, lane = 16 block + column)
+  float* const A = sm.u.m.A;
+  float* const T = sm.u.m.T;
+  if (wave == 0) {
+    const int blk = lane >> 4, j = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float* arow = &A[(16 * blk + r) * AS + 16 * blk];
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; i += 4) {
+        const float4_t a4 = *reinterpret_cast<const float4_t*>(&arow[i]);
+        s0 = fmaf(a4.x, x[i], s0);
+        s1 = fmaf(a4.y, x[i + 1], s1);
+        s2 = fmaf(a4.z, x[i + 2], s2);
+        s3 = fmaf(a4.w, x[i + 3], s3);
+      }
+      x[r] = (r == j ? 1.f : 0.f) - ((s0 + s1) + (s2 + s3));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) T[(16 * blk + r) * AS + 16 * blk + j] = x[r];
+  }
+  lds_barrier();
+
+  // ---- T, step 2: blocks below the diagonal; wave j sweeps block column j
+  if (wave < 3) {
+    float* wt = sm.wtmp[wave];
+    for (int ib = wave + 1; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, wave, lane);
+  }
+  lds_barrier();
+
+  // ---- T' = T diag(beta) fragments of row block w (blocks above the diagonal are zero)
+  {
+    _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * kFragHalves;
+    const int r = 16 * wave + l16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (2 * s <= wave) {
+        half8_t x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = frag_col(s, q, j);
+          x[j] = (c >> 4) <= wave ? (_Float16)(T[r * AS + c] * sm.beta[c]) : (_Float16)0.f;
+        }
+        *reinterpret_cast<half8_t*>(Tw + frag_index(wave, s) * 512 + lane * 8) = x;
+      }
+    }
+  }
+}
+
 size_t chunk_workspace_bytes(int64_t chunk_slots, int R, int Hk, int Hv) {
   return ws_bytes(chunk_slots, R, Hk, Hv);
 }
@@ -990,9 +968,11 @@ hipError_t launch_chunk(const ChunkArgs& p, int io_dtype, hipStream_t stream) {
   if (p.R == 0) return hipSuccess;
   const Ws w = ws_layout(p.workspace, p.max_chunks, p.R, p.Hk, p.Hv);
   hipLaunchKernelGGL(gdn_chunk_index, dim3(1), dim3(kThreads), 0, stream, p, w);
-  if (p.max_chunks > 0)
-    hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)p.max_chunks, (unsigned)p.Hk), dim3(kThreads),
-                       0, stream, p, w);
+  if (p.max_chunks > 0) {
+    const int n_prep = p.max_chunks * p.Hv;
+    const int grid_prep = (n_prep + 7) / 8 * 8;
+    hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)grid_prep), dim3(kPrepThreads), 0, stream, p, w, n_prep);
+  }
   const int n_items = p.R * p.Hv * (D / kScanTile);
   const int grid = (n_items + 7) / 8 * 8;
   hipLaunchKernelGGL(gdn_chunk_scan, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, p, w, n_items);
