@@ -721,12 +721,12 @@ __global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w
 // gdn_chunk_prep: one workgroup per (chunk slot, value head h); key head g = h / G
 //
 //   K, Q tiles -> LDS (direct loads, the scan's swizzled layout); gates of h
-//   Gram tiles on fp16 MFMA, wave w = row block w:
-//     KK[w][nb] = K_w K_nb^T, KQ[nb][w] = K_nb Q_w^T (nb <= w), QQ[w][w]
+//   Gram tiles on fp16 MFMA, wave w = row block w, taken transposed:
+//     K_nb K_w^T and K_nb Q_w^T (nb <= w), Q_w Q_w^T
+//   so that lane (l16, q) of tile nb holds row r = 16 w + l16, columns
+//   i = 16 nb + 4 q + e of K K^T and Q K^T: P's MFMA fragment layout (frag_col),
+//   and one decay factor e^{g_r - g_i} serves both A and P
 //   norms from the Gram diagonals: rk_t = (k_t.k_t + eps)^-1/2, rq_t likewise times the scale
-//   A (fp32, LDS) from KK; P straight from KQ: the accumulator tile of K_nb Q_w^T holds,
-//   in lane (l16, q), P[16 w + l16][16 nb + 4 q + e], which is P's MFMA fragment
-//   layout (frag_col) for row block w
 //   T = (I + A)^-1 blockwise from 16x16 blocks: the diagonal blocks by forward
 //   substitution, the blocks below the diagonal column by column,
 //     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj,
@@ -824,7 +824,7 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       if (nb <= wave) {
-        kk[nb] = mfma_f16(kw, kn[nb], kk[nb]);    // KK[16 w + 4q + e][16 nb + l16]
+        kk[nb] = mfma_f16(kn[nb], kw, kk[nb]);    // KK[16 w + l16][16 nb + 4q + e]
         kq[nb] = mfma_f16(kn[nb], qw, kq[nb]);    // QK[16 w + l16][16 nb + 4q + e]
       }
     }
@@ -846,57 +846,38 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
   }
   lds_barrier();                                   // K, Q tiles dead from here; their LDS becomes A, T
 
-  // ---- per-token factors (wave 0)
-  if (wave == 0) {
+  // ---- per-token factors, one row per wave:
+  //   kVecZ e^{g_t} rk_t, kVecO e^{g_t} rq_t, kVecU e^{g_L - g_t} rk_t, kVecGamma e^{g_L}
+  {
     const int t = lane;
     const float gt = sm.g[t], gL = sm.g[C - 1];
-    float* vec = w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C;
-    vec[kVecZ * C + t] = expf(gt) * sm.rk[t];
-    vec[kVecO * C + t] = expf(gt) * sm.rq[t];
-    vec[kVecU * C + t] = expf(gL - gt) * sm.rk[t];
-    vec[kVecGamma * C + t] = expf(gL);
+    const float v = wave == kVecZ ? expf(gt) * sm.rk[t]
+                  : wave == kVecO ? expf(gt) * sm.rq[t]
+                  : wave == kVecU ? expf(gL - gt) * sm.rk[t]
+                                  : expf(gL);
+    w.vec[((size_t)slot * p.Hv + h) * kVecRows * C + wave * C + t] = v;
   }
 
-  // ---- A rows 16 w + 4q + e (blocks nb <= w; the blocks above are never read)
-  {
-    float gr[4], br[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * wave + 4 * q + e;
-      gr[e] = sm.g[r];
-      br[e] = sm.beta[r] * sm.rk[r];
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      if (nb <= wave) {
-        const int i = 16 * nb + l16;
-        const float gi = sm.g[i], rki = sm.rk[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * wave + 4 * q + e;
-          const float av = i < r ? br[e] * fast_exp(fminf(gr[e] - gi, 0.f)) * rki * kk[nb][e] : 0.f;
-          sm.u.m.A[r * AS + i] = av;
-        }
-      }
-    }
-  }
-
-  // ---- P fragments of row block w straight from the KQ tiles: row r = 16 w + l16,
-  // columns i = 16 nb + 4q + e
+  // ---- A (rows 16 w + l16 of the fp32 LDS matrix; the blocks above the diagonal
+  // are never read) and the P fragments of row block w, from one decay factor
+  // per element: row r = 16 w + l16, columns i = 16 nb + 4q + e
   {
     const int r = 16 * wave + l16;
-    const float gr = sm.g[r], rqr = sm.rq[r];
+    const float gr = sm.g[r], rqr = sm.rq[r], brk = sm.beta[r] * sm.rk[r];
     half4_t ph[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const float4_t gi = *reinterpret_cast<const float4_t*>(&sm.g[16 * nb + 4 * q]);
       const float4_t ki = *reinterpret_cast<const float4_t*>(&sm.rk[16 * nb + 4 * q]);
+      float4_t av;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * nb + 4 * q + e;
-        ph[nb][e] = (_Float16)(nb <= wave && i <= r ? fast_exp(fminf(gr - gi[e], 0.f)) * rqr * ki[e] * kq[nb][e]
-                                                     : 0.f);
+        const float dec = nb <= wave ? fast_exp(fminf(gr - gi[e], 0.f)) * ki[e] : 0.f;
+        av[e] = i < r ? brk * dec * kk[nb][e] : 0.f;
+        ph[nb][e] = (_Float16)(i <= r ? rqr * dec * kq[nb][e] : 0.f);
       }
+      if (nb <= wave) *reinterpret_cast<float4_t*>(&sm.u.m.A[r * AS + 16 * nb + 4 * q]) = av;
     }
     _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * kFragHalves;
 #pragma unroll
