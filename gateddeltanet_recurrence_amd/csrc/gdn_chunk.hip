@@ -71,6 +71,7 @@ constexpr int kVecZ = 0, kVecO = 1, kVecU = 2, kVecGamma = 3, kVecRows = 4;
 
 struct Ws {
   int32_t* chunk_start;
+  int32_t* order;       // requests by decreasing chunk count (ties: lower index first)
   _Float16* T;
   _Float16* P;
   float* vec;
@@ -85,6 +86,8 @@ __host__ __device__ inline Ws ws_layout(void* base, int64_t slots, int R, int Hk
   size_t off = 0;
   w.chunk_start = reinterpret_cast<int32_t*>(p + off);
   off += align256((size_t)(R + 1) * 4);
+  w.order = reinterpret_cast<int32_t*>(p + off);
+  off += align256((size_t)R * 4);
   w.T = reinterpret_cast<_Float16*>(p + off);
   off += align256((size_t)slots * Hv * kFragHalves * 2);
   w.P = reinterpret_cast<_Float16*>(p + off);
@@ -95,7 +98,7 @@ __host__ __device__ inline Ws ws_layout(void* base, int64_t slots, int R, int Hk
 
 __host__ inline size_t ws_bytes(int64_t slots, int R, int Hk, int Hv) {
   (void)Hk;
-  return align256((size_t)(R + 1) * 4) + 2 * align256((size_t)slots * Hv * kFragHalves * 2) +
+  return align256((size_t)(R + 1) * 4) + align256((size_t)R * 4) + 2 * align256((size_t)slots * Hv * kFragHalves * 2) +
          align256((size_t)slots * Hv * kVecRows * C * 4);
 }
 
@@ -106,8 +109,12 @@ __device__ __forceinline__ int clamp_cu(const int32_t* cu, int i, int N) {
 }  // namespace
 
 // ----------------------------------------------------------------------------
-// chunk offsets: chunk_start[r] = sum_{i<r} ceil(len_i / 64), chunk_start[R] = total
+// chunk offsets: chunk_start[r] = sum_{i<r} ceil(len_i / 64), chunk_start[R] = total;
+// order: the requests sorted by decreasing chunk count (ties by index), so that the
+// scan starts the longest sequences first (identity beyond kMaxSortRequests)
 // ----------------------------------------------------------------------------
+constexpr int kMaxSortRequests = 1024;
+
 __global__ void __launch_bounds__(kThreads) gdn_chunk_index(ChunkArgs p, Ws w) {
   __shared__ int part[kThreads];
   const int tid = threadIdx.x;
@@ -138,6 +145,19 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_index(ChunkArgs p, Ws w) {
     prev = nxt;
   }
   if (tid == kThreads - 1) w.chunk_start[p.R] = part[kThreads - 1];
+  __syncthreads();
+  for (int r = r0; r < r1; ++r) {
+    int rank = r;
+    if (p.R <= kMaxSortRequests) {
+      const int nr = w.chunk_start[r + 1] - w.chunk_start[r];
+      rank = 0;
+      for (int o = 0; o < p.R; ++o) {
+        const int no = w.chunk_start[o + 1] - w.chunk_start[o];
+        rank += (no > nr) || (no == nr && o < r);
+      }
+    }
+    w.order[rank] = r;
+  }
 }
 
 // Locates (request, first token, length) of a chunk slot; false past the end.
@@ -624,19 +644,20 @@ __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& l
   }
 }
 
-__global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_items) {
+__global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_units) {
   constexpr int NT = D / kScanTile;     // tiles per head
 
-  // XCD-aware order: consecutive items (same request and key head) share an XCD's L2
-  const int per_xcd = (int)(gridDim.x / 8);
-  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (item >= n_items) return;
-  const int tile = item % NT;
-  int rest = item / NT;
-  const int hv = rest % p.group;
-  rest /= p.group;
-  const int g = rest % p.Hk;
-  const int req = rest / p.Hk;
+  // Work units are (request, key head) pairs, group x NT workgroups each, which
+  // share the unit's k and q in L2. Workgroups are dealt to the 8 XCDs round-robin
+  // by block index, so unit u goes to XCD u % 8: every XCD gets an equal share of
+  // every request, and within an XCD the units run longest request first.
+  const int per_unit = p.group * NT;
+  const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+  const int unit = xcd + 8 * (j / per_unit), m = j % per_unit;
+  if (unit >= n_units) return;
+  const int req = w.order[unit / p.Hk];
+  const int g = unit % p.Hk;
+  const int hv = m / NT, tile = m % NT;
   const int h = g * p.group + hv;
   const int d0 = tile * kScanTile;
 
@@ -954,9 +975,9 @@ hipError_t launch_chunk(const ChunkArgs& p, int io_dtype, hipStream_t stream) {
     const int grid_prep = (n_prep + 7) / 8 * 8;
     hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)grid_prep), dim3(kPrepThreads), 0, stream, p, w, n_prep);
   }
-  const int n_items = p.R * p.Hv * (D / kScanTile);
-  const int grid = (n_items + 7) / 8 * 8;
-  hipLaunchKernelGGL(gdn_chunk_scan, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, p, w, n_items);
+  const int n_units = p.R * p.Hk;
+  const int grid = 8 * ((n_units + 7) / 8) * p.group * (D / kScanTile);
+  hipLaunchKernelGGL(gdn_chunk_scan, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, p, w, n_units);
   return hipGetLastError();
 }
 
