@@ -23,6 +23,8 @@
 //
 // Kernels: gdn_chunk_index (chunk offsets per sequence), gdn_chunk_prep,
 // gdn_chunk_scan. Dk = Dv = 128, fp16 I/O only.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -231,42 +233,91 @@ __device__ __forceinline__ void t_offdiag_block(const float* A, float* T, float*
 // by an XOR of the row (kv_swizzle) so that the row-fragment reads and the
 // transposing column reads are both free of bank conflicts.
 // ----------------------------------------------------------------------------
-constexpr int kScanWaves = 2;                 // waves that compute
-constexpr int kLoaderWaves = 2;               // waves that only copy chunks into LDS
-constexpr int kScanThreads = 64 * (kScanWaves + kLoaderWaves);
+// Tile configurations: NW compute waves own 16 state rows each (tile TV = 16 NW
+// rows); two loader waves copy the chunks. NW = 2 keeps more workgroups in flight
+// for few, long sequences (three LDS buffers); NW = 4 halves the k, q, T', P bytes
+// each CU pulls per state row when there are workgroups enough (two buffers).
+constexpr int kLoaderWaves = 2;
 constexpr int kRowsPerWave = 16;
-constexpr int kScanTile = kScanWaves * kRowsPerWave;    // 32 state rows per workgroup
+
+template <int NW>
+struct ScanCfg {
+  static constexpr int TV = kRowsPerWave * NW;          // state rows per workgroup
+  static constexpr int NT = D / TV;                     // tiles per head
+  static constexpr int NBUF = NW == 2 ? 3 : 2;          // LDS buffers (chunks in flight)
+  static constexpr int THREADS = 64 * (NW + kLoaderWaves);
+  static constexpr int VROW = TV * 2;                   // bytes of a V tile row
+  static constexpr int VROWS_PER_LOAD = 1024 / VROW;
+  static constexpr int VLOADS = C / VROWS_PER_LOAD;     // 1 KiB loads of the V tile (4 or 8)
+  // direct loads per loader wave and chunk: half of K, Q (8 + 8), T', P (3 + 3), V,
+  // and the factors (both loaders write the same bytes)
+  static constexpr int STAGE_LOADS = 8 + 8 + 3 + 3 + VLOADS / 2 + 1;
+};
 
 // 16-byte unit u of row r of a K or Q tile is stored at unit u ^ kv_swizzle(r).
 __device__ __forceinline__ int kv_swizzle(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-// 16-byte unit u (of 4) of row r of a V tile is stored at unit u ^ v_swizzle(r).
-__device__ __forceinline__ int v_swizzle(int r) { return ((r >> 2) & 1) << 1; }
+// 16-byte unit u of row r of a V tile is stored at unit u ^ v_swizzle<NW>(r): the
+// 8 rows that a transposing read of one wave's 32-byte slice touches then fall in
+// distinct banks (64-byte rows: alternate the halves every 4 rows; 128-byte rows:
+// rotate the slice among the four pairs every 2 rows).
+template <int NW>
+__device__ __forceinline__ int v_swizzle(int r) {
+  if constexpr (NW == 2) return ((r >> 2) & 1) << 1;
+  else return ((r >> 1) & 3) << 1;
+}
 
-// Operands of three chunks in LDS (buffer b = chunk index mod 3). Each piece is an LDS
-// object of its own: the compiler then knows that the direct-to-LDS loads into
-// one buffer do not alias the reads of the other, and does not wait for the
-// loads of the next chunk before reading the current one.
-#define GDN_SCAN_LDS(type, name, count) \
+// Operands of NBUF chunks in LDS (buffer b = chunk index mod NBUF). Each piece is
+// an LDS object of its own: the compiler then knows that the direct-to-LDS loads
+// into one buffer do not alias the reads of another, and does not wait for the
+// loads of a later chunk before reading the current one.
+#define GDN_SCAN_LDS3(type, name, count) \
   __shared__ __attribute__((aligned(16))) type name##0[count]; \
   __shared__ __attribute__((aligned(16))) type name##1[count]; \
   __shared__ __attribute__((aligned(16))) type name##2[count];
-GDN_SCAN_LDS(_Float16, lds_K, C * D)            // [token][dk], units permuted by kv_swizzle
-GDN_SCAN_LDS(_Float16, lds_Q, C * D)
-GDN_SCAN_LDS(_Float16, lds_T, kFragHalves)      // T' fragments as stored by gdn_chunk_prep
-GDN_SCAN_LDS(_Float16, lds_P, kFragHalves)
-GDN_SCAN_LDS(_Float16, lds_V, C * kScanTile)    // [token][dv of the tile], units permuted by v_swizzle
-GDN_SCAN_LDS(float, lds_vec, kVecRows * C)
-#undef GDN_SCAN_LDS
-__shared__ __attribute__((aligned(16))) _Float16 lds_S16[kScanWaves][kRowsPerWave * D];  // per wave [dv][dk]
-__shared__ __attribute__((aligned(16))) unsigned lds_touch[2][64];   // discarded L2 prefetch data
+#define GDN_SCAN_LDS2(type, name, count) \
+  __shared__ __attribute__((aligned(16))) type name##0[count]; \
+  __shared__ __attribute__((aligned(16))) type name##1[count];
+// NW = 2
+GDN_SCAN_LDS3(_Float16, lds2_K, C * D)           // [token][dk], units permuted by kv_swizzle
+GDN_SCAN_LDS3(_Float16, lds2_Q, C * D)
+GDN_SCAN_LDS3(_Float16, lds2_T, kFragHalves)     // T' fragments as stored by gdn_chunk_prep
+GDN_SCAN_LDS3(_Float16, lds2_P, kFragHalves)
+GDN_SCAN_LDS3(_Float16, lds2_V, C * 32)          // [token][dv of the tile], units permuted by v_swizzle
+GDN_SCAN_LDS3(float, lds2_vec, kVecRows * C)
+__shared__ __attribute__((aligned(16))) _Float16 lds2_S16[2][kRowsPerWave * D];  // per wave [dv][dk]
+__shared__ __attribute__((aligned(16))) unsigned lds2_touch[kLoaderWaves][64];  // discarded prefetch data
+// NW = 4
+GDN_SCAN_LDS2(_Float16, lds4_K, C * D)
+GDN_SCAN_LDS2(_Float16, lds4_Q, C * D)
+GDN_SCAN_LDS2(_Float16, lds4_T, kFragHalves)
+GDN_SCAN_LDS2(_Float16, lds4_P, kFragHalves)
+GDN_SCAN_LDS2(_Float16, lds4_V, C * 64)
+GDN_SCAN_LDS2(float, lds4_vec, kVecRows * C)
+__shared__ __attribute__((aligned(16))) _Float16 lds4_S16[4][kRowsPerWave * D];
+__shared__ __attribute__((aligned(16))) unsigned lds4_touch[kLoaderWaves][64];
+#undef GDN_SCAN_LDS3
+#undef GDN_SCAN_LDS2
 
-template <int B> struct ScanBuf {
-  static __device__ __forceinline__ _Float16* K() { return B == 0 ? lds_K0 : B == 1 ? lds_K1 : lds_K2; }
-  static __device__ __forceinline__ _Float16* Q() { return B == 0 ? lds_Q0 : B == 1 ? lds_Q1 : lds_Q2; }
-  static __device__ __forceinline__ _Float16* T() { return B == 0 ? lds_T0 : B == 1 ? lds_T1 : lds_T2; }
-  static __device__ __forceinline__ _Float16* P() { return B == 0 ? lds_P0 : B == 1 ? lds_P1 : lds_P2; }
-  static __device__ __forceinline__ _Float16* V() { return B == 0 ? lds_V0 : B == 1 ? lds_V1 : lds_V2; }
-  static __device__ __forceinline__ float* vec() { return B == 0 ? lds_vec0 : B == 1 ? lds_vec1 : lds_vec2; }
+template <int NW, int B> struct ScanBuf;
+template <int B> struct ScanBuf<2, B> {
+  static __device__ __forceinline__ _Float16* K() { return B == 0 ? lds2_K0 : B == 1 ? lds2_K1 : lds2_K2; }
+  static __device__ __forceinline__ _Float16* Q() { return B == 0 ? lds2_Q0 : B == 1 ? lds2_Q1 : lds2_Q2; }
+  static __device__ __forceinline__ _Float16* T() { return B == 0 ? lds2_T0 : B == 1 ? lds2_T1 : lds2_T2; }
+  static __device__ __forceinline__ _Float16* P() { return B == 0 ? lds2_P0 : B == 1 ? lds2_P1 : lds2_P2; }
+  static __device__ __forceinline__ _Float16* V() { return B == 0 ? lds2_V0 : B == 1 ? lds2_V1 : lds2_V2; }
+  static __device__ __forceinline__ float* vec() { return B == 0 ? lds2_vec0 : B == 1 ? lds2_vec1 : lds2_vec2; }
+  static __device__ __forceinline__ _Float16* S16(int wave) { return lds2_S16[wave]; }
+  static __device__ __forceinline__ unsigned* touch(int loader) { return lds2_touch[loader]; }
+};
+template <int B> struct ScanBuf<4, B> {
+  static __device__ __forceinline__ _Float16* K() { return B == 0 ? lds4_K0 : lds4_K1; }
+  static __device__ __forceinline__ _Float16* Q() { return B == 0 ? lds4_Q0 : lds4_Q1; }
+  static __device__ __forceinline__ _Float16* T() { return B == 0 ? lds4_T0 : lds4_T1; }
+  static __device__ __forceinline__ _Float16* P() { return B == 0 ? lds4_P0 : lds4_P1; }
+  static __device__ __forceinline__ _Float16* V() { return B == 0 ? lds4_V0 : lds4_V1; }
+  static __device__ __forceinline__ float* vec() { return B == 0 ? lds4_vec0 : lds4_vec1; }
+  static __device__ __forceinline__ _Float16* S16(int wave) { return lds4_S16[wave]; }
+  static __device__ __forceinline__ unsigned* touch(int loader) { return lds4_touch[loader]; }
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -276,18 +327,17 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, void* lds, int byte_off, in
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, byte_off, uniform_off, 0, 0);
 }
 
-// Copies chunk (slot, t0, L) into LDS buffer B; rows >= L read as zero (L = 0: no
-// memory is read, the buffer fills with zeros). Wave w copies rows 32 w .. 32 w + 31
-// of K, Q and V and fragments 3 w .. 3 w + 2 of T' and P; both waves write the
-// 1 KiB of factors (the same bytes). kStageLoads loads per wave, issued in four
-// parts between the phases of a scan step so that the wave keeps computing while
-// the vector memory path (about 64 bytes per clock per CU) works through them.
-constexpr int kStageLoads = 25;
 constexpr int kTouchLoads = 3;     // L2 prefetch loads per loader wave and chunk
 constexpr int kTouchAhead = 3;     // prefetched this many chunks ahead of the direct loads
 
-template <int B>
+// Copies chunk (slot, t0, L) into LDS buffer B; rows >= L read as zero (L = 0: no
+// memory is read, the buffer fills with zeros). Loader wave w copies rows
+// 32 w .. 32 w + 31 of K, Q and V and fragments 3 w .. 3 w + 2 of T' and P; both
+// write the 1 KiB of factors (the same bytes): STAGE_LOADS loads each.
+template <int NW, int B>
 struct Stage {
+  typedef ScanCfg<NW> Cfg;
+  typedef ScanBuf<NW, B> Buf;
   rsrc_t rk, rq, rt, rp, rv, rvec;
   int krow, vrow, wave, lane;
 
@@ -303,7 +353,7 @@ struct Stage {
     rt = make_rsrc(w.T + fo, f_bytes);
     rp = make_rsrc(w.P + fo, f_bytes);
     rv = make_rsrc(static_cast<const _Float16*>(p.v) + ((size_t)t0 * p.Hv + h) * D + d0,
-                   L > 0 ? ((L - 1) * vrow + kScanTile) * 2 : 0);
+                   L > 0 ? ((L - 1) * vrow + Cfg::TV) * 2 : 0);
     rvec = make_rsrc(w.vec + ((size_t)slot * p.Hv + h) * kVecRows * C, L > 0 ? kVecRows * C * 4 : 0);
   }
 
@@ -322,34 +372,33 @@ struct Stage {
       }
     }
   }
-  __device__ __forceinline__ void part_k() const { kq(rk, ScanBuf<B>::K()); }
-  __device__ __forceinline__ void part_q() const { kq(rq, ScanBuf<B>::Q()); }
   // T' and P fragments 3 wave .. +2 (6 loads)
-  __device__ __forceinline__ void part_tp() const {
+  __device__ __forceinline__ void tp() const {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int f = 3 * wave + i;
-      load_lds16(rt, ScanBuf<B>::T() + f * 512, lane * 16, f * 1024);
-      load_lds16(rp, ScanBuf<B>::P() + f * 512, lane * 16, f * 1024);
+      load_lds16(rt, Buf::T() + f * 512, lane * 16, f * 1024);
+      load_lds16(rp, Buf::P() + f * 512, lane * 16, f * 1024);
     }
   }
-  // V rows 32 wave .. +31, 16 rows of 64 bytes per load (v_swizzle repeats every
-  // 8 rows), and the factors (3 loads)
-  __device__ __forceinline__ void part_v() const {
-    const int vr = lane >> 2;
-    const int voff = vr * vrow * 2 + 16 * ((lane & 3) ^ v_swizzle(vr));
+  // V rows 32 wave .. +31, VROWS_PER_LOAD rows per load (v_swizzle repeats within
+  // that many rows), and the factors
+  __device__ __forceinline__ void v() const {
+    constexpr int UNITS = Cfg::VROW / 16;
+    const int vr = lane / UNITS;
+    const int voff = vr * vrow * 2 + 16 * ((lane % UNITS) ^ v_swizzle<NW>(vr));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = 2 * wave + i;
-      load_lds16(rv, ScanBuf<B>::V() + 16 * blk * kScanTile, voff, 16 * blk * vrow * 2);
+    for (int i = 0; i < Cfg::VLOADS / 2; ++i) {
+      const int blk = (Cfg::VLOADS / 2) * wave + i;
+      load_lds16(rv, Buf::V() + Cfg::VROWS_PER_LOAD * blk * Cfg::TV, voff, Cfg::VROWS_PER_LOAD * blk * vrow * 2);
     }
-    load_lds16(rvec, ScanBuf<B>::vec(), lane * 16);
+    load_lds16(rvec, Buf::vec(), lane * 16);
   }
   __device__ __forceinline__ void all() const {
-    part_k();
-    part_q();
-    part_tp();
-    part_v();
+    kq(rk, Buf::K());
+    kq(rq, Buf::Q());
+    tp();
+    v();
   }
 };
 
@@ -375,16 +424,18 @@ __device__ __forceinline__ half8_t cat8(half4_t lo, half4_t hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Loader waves: wait until this wave has at most kStageLoads + 2 kTouchLoads
-// vector memory operations in flight, then the workgroup barrier. Per chunk a
-// loader issues kStageLoads direct loads, then kTouchLoads prefetches; loads
-// complete in issue order, so while any direct load of the chunk the barrier
-// releases (issued two chunks earlier) is pending, so is everything issued after
-// it: at least its own chunk's prefetches and the next chunk's loads and
-// prefetches, more than the limit. No release fence: one would wait for every
-// direct load still in flight (they write LDS).
+// Loader waves: wait until this wave has at most LIMIT vector memory operations
+// in flight, then the workgroup barrier. Per chunk a loader issues STAGE_LOADS
+// direct loads into the buffer that is NBUF - 1 chunks ahead, then kTouchLoads
+// prefetches; loads complete in issue order, and after the last direct load of
+// the chunk the barrier releases come at least (NBUF - 2) STAGE_LOADS +
+// (NBUF - 1) kTouchLoads more, so once no more than that many are pending the
+// chunk is in LDS. No release fence: one would wait for every direct load still
+// in flight (they write LDS).
+template <int NW>
 __device__ __forceinline__ void loader_barrier() {
-  constexpr int kLimit = kStageLoads + 2 * kTouchLoads;
+  typedef ScanCfg<NW> Cfg;
+  constexpr int kLimit = (Cfg::NBUF - 2) * Cfg::STAGE_LOADS + (Cfg::NBUF - 1) * kTouchLoads;
   static_assert(kLimit < 64, "vmcnt holds 6 bits");
   // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in [15:14]
   constexpr int kWait = (kLimit & 15) | (7 << 4) | (15 << 8) | ((kLimit >> 4) << 14);
@@ -432,6 +483,7 @@ struct LaneOffsets {
   int frag;       // T' / P fragment reads
 };
 
+template <int NW>
 __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
   LaneOffsets o;
   const int l16 = lane & 15, q = lane >> 4;
@@ -445,9 +497,10 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
   const int unit = (l16 & 3) >> 1;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o.tr[mb] = r0 * (D * 2) + 16 * ((2 * mb + unit) ^ swt) + 8 * (l16 & 1);
-  // V: row 16 mb + 4 q + l16 / 4, whose v_swizzle is (q & 1) << 1 for every mb
+  // V: row 16 mb + rv, rv = 4 q + l16 / 4; v_swizzle depends on the row mod 8 only
+  const int rv = 4 * q + (l16 >> 2);
   const int col8 = kRowsPerWave * 2 * wave + 8 * (l16 & 3);
-  o.v = (4 * q + (l16 >> 2)) * (kScanTile * 2) + 16 * ((col8 >> 4) ^ ((q & 1) << 1)) + (col8 & 15);
+  o.v = rv * (ScanCfg<NW>::TV * 2) + 16 * ((col8 >> 4) ^ v_swizzle<NW>(rv)) + (col8 & 15);
   o.frag = lane * 16;
   return o;
 }
@@ -456,15 +509,16 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
 // one 4-byte load per 128-byte line into a discarded LDS area. Lines shared by
 // several workgroups are split between them: K and Q of a key head among its
 // nshare = group x tiles workgroups (share index sub), T', P and the factors of
-// a head among its tiles, and a V line (two tiles' 64-byte row pieces) goes to
-// the even tile. Loader 0 takes K, Q and the factors, loader 1 T', P and V:
+// a head among its tiles, and a V line (128 bytes of a row: one or two tiles) goes to
+// the tile that starts it. Loader 0 takes K, Q and the factors, loader 1 T', P and V:
 // kTouchLoads loads each; a lane without a line gets an offset past the range.
+template <int NW>
 __device__ __forceinline__ void touch_chunk(const ScanCtx& x, int slot, int t0, int L, int loader, int sub,
                                             int nshare, int tile) {
   constexpr int kNone = 0x7FFFFFF0;                // past every range below
-  constexpr int NT = D / kScanTile;
+  typedef ScanCfg<NW> Cfg;
   const int lane = x.lane;
-  lds_void_t* dst = (lds_void_t*)lds_touch[loader];
+  lds_void_t* dst = (lds_void_t*)ScanBuf<NW, 0>::touch(loader);
   const size_t fo = ((size_t)slot * x.p.Hv + x.h) * kFragHalves;
   const int f_bytes = L > 0 ? kFragHalves * 2 : 0;
   if (loader == 0) {
@@ -481,43 +535,47 @@ __device__ __forceinline__ void touch_chunk(const ScanCtx& x, int slot, int t0, 
                                   (L > 0 && tile == 0) ? kVecRows * C * 4 : 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rvec, dst, 4, lane < 8 ? 128 * lane : kNone, 0, 0, 0);
   } else {
-    const int m = tile + NT * lane;                // fragment line m of 48
+    const int m = tile + Cfg::NT * lane;           // fragment line m of 48
     const int off = m < kFragHalves * 2 / 128 ? 128 * m : kNone;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(x.w.T + fo, f_bytes), dst, 4, off, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(x.w.P + fo, f_bytes), dst, 4, off, 0, 0, 0);
     const int vrow = x.p.Hv * D;
-    const rsrc_t rv = make_rsrc(static_cast<const _Float16*>(x.p.v) + ((size_t)t0 * x.p.Hv + x.h) * D + 64 * (tile >> 1),
-                                (L > 0 && (tile & 1) == 0) ? ((L - 1) * vrow + 64) * 2 : 0);
+    const int dline = x.d0 & ~63;                  // first dv of the 128-byte line
+    const rsrc_t rv = make_rsrc(static_cast<const _Float16*>(x.p.v) + ((size_t)t0 * x.p.Hv + x.h) * D + dline,
+                                (L > 0 && dline == x.d0) ? ((L - 1) * vrow + 64) * 2 : 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 4, lane * vrow * 2, 0, 0, 0);
   }
 }
 
 // Loader step: chunk c is in LDS buffer B once the barrier passes; then the loads
-// of chunk c + 2 into buffer (B + 2) mod 3 and the L2 prefetch of chunk c + 2 + kTouchAhead.
-template <int B>
+// of chunk c + NBUF - 1 into the buffer that chunk c - 1 used (the compute waves
+// are past it) and the L2 prefetch of the chunk kTouchAhead after that.
+template <int NW, int B>
 __device__ __forceinline__ void loader_step(const ScanCtx& x, int c, int loader, int sub, int nshare, int tile) {
-  const bool more = c + 2 < x.nch;
-  const int t0 = x.beg + C * (c + 2);
-  loader_barrier();
-  Stage<(B + 2) % 3>(x.p, x.w, more ? x.slot0 + c + 2 : x.slot0 + c, t0, more ? min(C, x.end - t0) : 0, x.h, x.g,
-                     x.d0, loader, x.lane)
+  constexpr int NBUF = ScanCfg<NW>::NBUF, LEAD = NBUF - 1;
+  const bool more = c + LEAD < x.nch;
+  const int t0 = x.beg + C * (c + LEAD);
+  loader_barrier<NW>();
+  Stage<NW, (B + LEAD) % NBUF>(x.p, x.w, more ? x.slot0 + c + LEAD : x.slot0 + c, t0,
+                               more ? min(C, x.end - t0) : 0, x.h, x.g, x.d0, loader, x.lane)
       .all();
-  const int ca = c + 2 + kTouchAhead;
+  const int ca = c + LEAD + kTouchAhead;
   const bool ahead = ca < x.nch;
   const int ta = x.beg + C * ca;
-  touch_chunk(x, ahead ? x.slot0 + ca : x.slot0, ta, ahead ? min(C, x.end - ta) : 0, loader, sub, nshare, tile);
+  touch_chunk<NW>(x, ahead ? x.slot0 + ca : x.slot0, ta, ahead ? min(C, x.end - ta) : 0, loader, sub, nshare,
+                  tile);
 }
 
-// Compute step: chunk c from LDS buffer B = c mod 3; stores the output of chunk c - 1.
-template <int B>
+// Compute step: chunk c from LDS buffer B = c mod NBUF; stores the output of chunk c - 1.
+template <int NW, int B>
 __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& lo_in, int c, float4_t (&ST)[8],
                                           float4_t (&O)[4], int& o_t0, int& o_L) {
   const int lane = x.lane, l16 = lane & 15, q = lane >> 4;
   const int t0 = x.beg + C * c;
   const LaneOffsets& lo = lo_in;
-  typedef ScanBuf<B> Buf;
+  typedef ScanBuf<NW, B> Buf;
   const float* vec = Buf::vec();
-  _Float16* const S16w = lds_S16[x.wave];
+  _Float16* const S16w = Buf::S16(x.wave);
   compute_barrier();                                   // chunk c is in LDS buffer B
   store_out(x, O, o_t0, o_L);
 
@@ -562,7 +620,7 @@ __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& l
   half8_t tf[kFrags];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    v4[mb] = lds_tr4(Buf::V(), lo.v + 16 * mb * (kScanTile * 2));
+    v4[mb] = lds_tr4(Buf::V(), lo.v + 16 * mb * (ScanCfg<NW>::TV * 2));
     zf[mb] = *reinterpret_cast<const float4_t*>(&vec[kVecZ * C + 16 * mb + 4 * q]);
   }
 #pragma unroll
@@ -644,8 +702,10 @@ __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& l
   }
 }
 
-__global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w, int n_units) {
-  constexpr int NT = D / kScanTile;     // tiles per head
+template <int NW>
+__global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs p, Ws w, int n_units) {
+  typedef ScanCfg<NW> Cfg;
+  constexpr int NT = Cfg::NT, NBUF = Cfg::NBUF, LEAD = NBUF - 1;
 
   // Work units are (request, key head) pairs, group x NT workgroups each, which
   // share the unit's k and q in L2. Workgroups are dealt to the 8 XCDs round-robin
@@ -659,7 +719,7 @@ __global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w
   const int g = unit % p.Hk;
   const int hv = m / NT, tile = m % NT;
   const int h = g * p.group + hv;
-  const int d0 = tile * kScanTile;
+  const int d0 = tile * Cfg::TV;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -671,31 +731,46 @@ __global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w
   int nch = (end - beg + C - 1) / C;
   nch = max(0, min(nch, p.max_chunks - slot0));
 
-  if (wave >= kScanWaves) {
-    // ---- loader waves: chunks 0 and 1 (a missing chunk has length 0: its loads
-    // read nothing), then chunk c + 2 after the barrier of chunk c
-    const int loader = wave - kScanWaves;
+  if (wave >= NW) {
+    // ---- loader waves: chunks 0 .. LEAD - 1 (a missing chunk has length 0: its
+    // loads read nothing), then chunk c + LEAD after the barrier of chunk c
+    const int loader = wave - NW;
     ScanCtx x{p, w, h, g, d0, 0, loader, lane, beg, end, slot0, nch};
-    Stage<0>(p, w, slot0, beg, nch > 0 ? min(C, end - beg) : 0, h, g, d0, loader, lane).all();
-    Stage<1>(p, w, nch > 1 ? slot0 + 1 : slot0, beg + C, nch > 1 ? min(C, end - beg - C) : 0, h, g, d0, loader,
-             lane)
-        .all();
-    // L2 prefetch of chunks 2 .. 2 + kTouchAhead - 1 (the later ones go with the loader steps)
+    auto stage_first = [&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      Stage<NW, b>(p, w, nch > b ? slot0 + b : slot0, beg + C * b, nch > b ? min(C, end - beg - C * b) : 0, h, g,
+                   d0, loader, lane)
+          .all();
+    };
+    stage_first(std::integral_constant<int, 0>());
+    if constexpr (LEAD > 1) stage_first(std::integral_constant<int, 1>());
+    // L2 prefetch of chunks LEAD .. LEAD + kTouchAhead - 1 (the later ones go with the loader steps)
     const int sub = hv * NT + tile, nshare = p.group * NT;
 #pragma unroll
-    for (int ca = 2; ca < 2 + kTouchAhead; ++ca) {
+    for (int ca = LEAD; ca < LEAD + kTouchAhead; ++ca) {
       const bool ahead = ca < nch;
       const int ta = beg + C * ca;
-      touch_chunk(x, ahead ? slot0 + ca : slot0, ta, ahead ? min(C, end - ta) : 0, loader, sub, nshare, tile);
+      touch_chunk<NW>(x, ahead ? slot0 + ca : slot0, ta, ahead ? min(C, end - ta) : 0, loader, sub, nshare, tile);
     }
     int c = 0;
-    for (; c + 2 < nch; c += 3) {
-      loader_step<0>(x, c, loader, sub, nshare, tile);
-      loader_step<1>(x, c + 1, loader, sub, nshare, tile);
-      loader_step<2>(x, c + 2, loader, sub, nshare, tile);
+    if constexpr (NBUF == 3) {
+      for (; c + 2 < nch; c += 3) {
+        loader_step<NW, 0>(x, c, loader, sub, nshare, tile);
+        loader_step<NW, 1>(x, c + 1, loader, sub, nshare, tile);
+        loader_step<NW, 2>(x, c + 2, loader, sub, nshare, tile);
+      }
+      if (c < nch) loader_step<NW, 0>(x, c, loader, sub, nshare, tile);
+      if (c + 1 < nch) loader_step<NW, 1>(x, c + 1, loader, sub, nshare, tile);
+    } else {
+      for (; c + 1 < nch; c += 2) {
+        loader_step<NW, 0>(x, c, loader, sub, nshare, tile);
+        loader_step<NW, 1>(x, c + 1, loader, sub, nshare, tile);
+      }
+      if (c < nch) loader_step<NW, 0>(x, c, loader, sub, nshare, tile);
     }
-    if (c < nch) loader_step<0>(x, c, loader, sub, nshare, tile);
-    if (c + 1 < nch) loader_step<1>(x, c + 1, loader, sub, nshare, tile);
+    // the last loads fill buffers that no one reads; let them land before the
+    // wave ends
+    __builtin_amdgcn_s_waitcnt(0);
     return;
   }
 
@@ -712,21 +787,29 @@ __global__ void __launch_bounds__(kScanThreads) gdn_chunk_scan(ChunkArgs p, Ws w
   }
 
   ScanCtx x{p, w, h, g, d0, dvw, wave, lane, beg, end, slot0, nch};
-  const LaneOffsets lo = lane_offsets(wave, lane);
+  const LaneOffsets lo = lane_offsets<NW>(wave, lane);
   float4_t O[4];
   int o_t0 = beg, o_L = 0;                 // output rows of the previous chunk, stored one step late
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) O[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // three chunks per iteration, one LDS buffer each (one barrier per chunk, as the loaders)
+  // NBUF chunks per iteration, one LDS buffer each (one barrier per chunk, as the loaders)
   int c = 0;
-  for (; c + 2 < nch; c += 3) {
-    scan_step<0>(x, lo, c, ST, O, o_t0, o_L);
-    scan_step<1>(x, lo, c + 1, ST, O, o_t0, o_L);
-    scan_step<2>(x, lo, c + 2, ST, O, o_t0, o_L);
+  if constexpr (NBUF == 3) {
+    for (; c + 2 < nch; c += 3) {
+      scan_step<NW, 0>(x, lo, c, ST, O, o_t0, o_L);
+      scan_step<NW, 1>(x, lo, c + 1, ST, O, o_t0, o_L);
+      scan_step<NW, 2>(x, lo, c + 2, ST, O, o_t0, o_L);
+    }
+    if (c < nch) scan_step<NW, 0>(x, lo, c, ST, O, o_t0, o_L);
+    if (c + 1 < nch) scan_step<NW, 1>(x, lo, c + 1, ST, O, o_t0, o_L);
+  } else {
+    for (; c + 1 < nch; c += 2) {
+      scan_step<NW, 0>(x, lo, c, ST, O, o_t0, o_L);
+      scan_step<NW, 1>(x, lo, c + 1, ST, O, o_t0, o_L);
+    }
+    if (c < nch) scan_step<NW, 0>(x, lo, c, ST, O, o_t0, o_L);
   }
-  if (c < nch) scan_step<0>(x, lo, c, ST, O, o_t0, o_L);
-  if (c + 1 < nch) scan_step<1>(x, lo, c + 1, ST, O, o_t0, o_L);
 
   // ---- output of the last chunk, final state
   __builtin_amdgcn_s_waitcnt(0);
@@ -975,9 +1058,22 @@ hipError_t launch_chunk(const ChunkArgs& p, int io_dtype, hipStream_t stream) {
     const int grid_prep = (n_prep + 7) / 8 * 8;
     hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)grid_prep), dim3(kPrepThreads), 0, stream, p, w, n_prep);
   }
+  // Both scan configurations hold one workgroup per CU. 64-row tiles move half the
+  // k, q, T', P bytes per state row; they are taken when their workgroups fill
+  // every CU at least once, else 32-row tiles keep twice as many CUs busy.
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   const int n_units = p.R * p.Hk;
-  const int grid = 8 * ((n_units + 7) / 8) * p.group * (D / kScanTile);
-  hipLaunchKernelGGL(gdn_chunk_scan, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, p, w, n_units);
+  const int units_padded = 8 * ((n_units + 7) / 8);
+  if ((int64_t)n_units * p.group * ScanCfg<4>::NT >= n_cu) {
+    const int grid = units_padded * p.group * ScanCfg<4>::NT;
+    hipLaunchKernelGGL(gdn_chunk_scan<4>, dim3((unsigned)grid), dim3(ScanCfg<4>::THREADS), 0, stream, p, w, n_units);
+  } else {
+    const int grid = units_padded * p.group * ScanCfg<2>::NT;
+    hipLaunchKernelGGL(gdn_chunk_scan<2>, dim3((unsigned)grid), dim3(ScanCfg<2>::THREADS), 0, stream, p, w, n_units);
+  }
   return hipGetLastError();
 }
 

@@ -79,6 +79,37 @@ def test_chunk_packing_invariance_bitwise():
         assert np.array_equal(alone["final_state"][0], packed["final_state"][r])
 
 
+# 8 requests x 16 key heads x group 2: enough workgroups for the 64-row scan tiles
+WIDE = dict(Hk=16, Hv=32)
+
+
+def test_chunk_wide_tiles_vs_oracle():
+    inp = make_inputs(RAGGED, WIDE["Hk"], WIDE["Hv"], 128, 128, "f16", seed=46)
+    _case(f"chunk 64-row tiles Hk={WIDE['Hk']} Hv={WIDE['Hv']} lengths={RAGGED}")
+    res = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK)
+    ref_o, ref_s, _ = oracle_forward(inp, O)
+    assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "chunk 64-row tiles")
+
+
+def test_chunk_tile_width_invariance_bitwise():
+    # the batch runs the 64-row scan tiles, a request alone the 32-row ones; each
+    # wave does the same arithmetic on its 16 state rows in both
+    lengths = [130, 64, 1, 200, 65, 9, 128, 70]
+    inp = make_inputs(lengths, WIDE["Hk"], WIDE["Hv"], 128, 128, "f16", seed=47)
+    _case(f"chunk tile width invariance {lengths}")
+    packed = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK)
+    cu = inp["cu_seqlens"]
+    for r in (0, 3, 5):
+        sub = dict(inp)
+        for n in ("q", "k", "v", "a", "b"):
+            sub[n] = inp[n][cu[r]:cu[r + 1]]
+        sub["cu_seqlens"] = cu_from_lengths([lengths[r]])
+        sub["initial_state"] = inp["initial_state"][r:r + 1]
+        alone = run_forward(sub, torch, gdn, plan=gdn.PLAN_CHUNK)
+        assert np.array_equal(alone["output"], packed["output"][cu[r]:cu[r + 1]])
+        assert np.array_equal(alone["final_state"][0], packed["final_state"][r])
+
+
 def test_chunk_without_host_mirror_is_identical():
     inp = make_inputs([90, 1, 0, 40], 1, 2, 128, 128, "f16", seed=44)
     _case("chunk host mirror vs none")
