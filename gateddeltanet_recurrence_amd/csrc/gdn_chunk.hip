@@ -284,7 +284,6 @@ GDN_SCAN_LDS3(_Float16, lds2_T, kFragHalves)     // T' fragments as stored by gd
 GDN_SCAN_LDS3(_Float16, lds2_P, kFragHalves)
 GDN_SCAN_LDS3(_Float16, lds2_V, C * 32)          // [token][dv of the tile], units permuted by v_swizzle
 GDN_SCAN_LDS3(float, lds2_vec, kVecRows * C)
-__shared__ __attribute__((aligned(16))) _Float16 lds2_S16[2][kRowsPerWave * D];  // per wave [dv][dk]
 __shared__ __attribute__((aligned(16))) unsigned lds2_touch[kLoaderWaves][64];  // discarded prefetch data
 // NW = 4
 GDN_SCAN_LDS2(_Float16, lds4_K, C * D)
@@ -293,7 +292,6 @@ GDN_SCAN_LDS2(_Float16, lds4_T, kFragHalves)
 GDN_SCAN_LDS2(_Float16, lds4_P, kFragHalves)
 GDN_SCAN_LDS2(_Float16, lds4_V, C * 64)
 GDN_SCAN_LDS2(float, lds4_vec, kVecRows * C)
-__shared__ __attribute__((aligned(16))) _Float16 lds4_S16[4][kRowsPerWave * D];
 __shared__ __attribute__((aligned(16))) unsigned lds4_touch[kLoaderWaves][64];
 #undef GDN_SCAN_LDS3
 #undef GDN_SCAN_LDS2
@@ -306,7 +304,6 @@ template <int B> struct ScanBuf<2, B> {
   static __device__ __forceinline__ _Float16* P() { return B == 0 ? lds2_P0 : B == 1 ? lds2_P1 : lds2_P2; }
   static __device__ __forceinline__ _Float16* V() { return B == 0 ? lds2_V0 : B == 1 ? lds2_V1 : lds2_V2; }
   static __device__ __forceinline__ float* vec() { return B == 0 ? lds2_vec0 : B == 1 ? lds2_vec1 : lds2_vec2; }
-  static __device__ __forceinline__ _Float16* S16(int wave) { return lds2_S16[wave]; }
   static __device__ __forceinline__ unsigned* touch(int loader) { return lds2_touch[loader]; }
 };
 template <int B> struct ScanBuf<4, B> {
@@ -316,7 +313,6 @@ template <int B> struct ScanBuf<4, B> {
   static __device__ __forceinline__ _Float16* P() { return B == 0 ? lds4_P0 : lds4_P1; }
   static __device__ __forceinline__ _Float16* V() { return B == 0 ? lds4_V0 : lds4_V1; }
   static __device__ __forceinline__ float* vec() { return B == 0 ? lds4_vec0 : lds4_vec1; }
-  static __device__ __forceinline__ _Float16* S16(int wave) { return lds4_S16[wave]; }
   static __device__ __forceinline__ unsigned* touch(int loader) { return lds4_touch[loader]; }
 };
 
@@ -473,12 +469,20 @@ __device__ __forceinline__ void store_out(const ScanCtx& x, const float4_t (&O)[
   }
 }
 
+// State tiles. The wave's 16 x 128 state slice is kept transposed in 8 MFMA
+// accumulator tiles ST[mb]; lane (l16, q) element e of tile mb holds
+// S[dv = l16][dk_tile(mb, q) + e]. Tiles 2 ks and 2 ks + 1 thus hold, in lane
+// group q, dk 32 ks + 8 q .. 32 ks + 8 q + 7: converted to fp16 and concatenated
+// they are the state operand of the 32-wide k step ks, in the plain fragment
+// order, with no trip through LDS. The row order is set by the transposing reads
+// of K^T in the state update, whose output row j = 4 m + i is dk_tile(mb, m) + i.
+__device__ __forceinline__ constexpr int dk_tile(int mb, int m) { return 32 * (mb >> 1) + 8 * m + 4 * (mb & 1); }
+
 // Per-lane LDS byte offsets that do not change from chunk to chunk; every
 // access adds only compile-time constants to one of them.
 struct LaneOffsets {
-  int row[4];     // K / Q / S16 row-fragment reads, per 32-wide k step: row l16, unit (4 ks + q) ^ sw
-  int s16w[8];    // S16 writes, per 16-wide dk block mb: unit (2 mb + q / 2) ^ sw, half q % 2
-  int tr[8];      // K^T transposing reads, per dk block mb (token 4q + l16/4 of the first block)
+  int row[4];     // K / Q row-fragment reads, per 32-wide k step: row l16, unit (4 ks + q) ^ sw
+  int tr[8];      // K^T transposing reads, per state tile mb (token 4q + l16/4 of the first block)
   int v;          // V transposing reads
   int frag;       // T' / P fragment reads
 };
@@ -490,13 +494,15 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wave, int lane) {
   const int sw = kv_swizzle(l16);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) o.row[ks] = l16 * (D * 2) + 16 * ((4 * ks + q) ^ sw);
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) o.s16w[mb] = l16 * (D * 2) + 16 * ((2 * mb + (q >> 1)) ^ sw) + 8 * (q & 1);
-  // token r0 = 32 s + 4 q + l16 / 4 (+16): kv_swizzle depends on r0 % 16 = 4 q + l16 / 4 only
+  // token r0 = 32 s + 4 q + l16 / 4 (+16): kv_swizzle depends on r0 % 16 = 4 q + l16 / 4 only.
+  // The lane reads dk_tile(mb, l16 & 3) .. +3, the four state rows that its transposed
+  // data becomes (see dk_tile)
   const int r0 = 4 * q + (l16 >> 2), swt = kv_swizzle(r0);
-  const int unit = (l16 & 3) >> 1;
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) o.tr[mb] = r0 * (D * 2) + 16 * ((2 * mb + unit) ^ swt) + 8 * (l16 & 1);
+  for (int mb = 0; mb < 8; ++mb) {
+    const int dk = dk_tile(mb, l16 & 3);
+    o.tr[mb] = r0 * (D * 2) + 16 * ((dk >> 3) ^ swt) + 2 * (dk & 7);
+  }
   // V: row 16 mb + rv, rv = 4 q + l16 / 4; v_swizzle depends on the row mod 8 only
   const int rv = 4 * q + (l16 >> 2);
   const int col8 = kRowsPerWave * 2 * wave + 8 * (l16 & 3);
@@ -575,14 +581,8 @@ __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& l
   const LaneOffsets& lo = lo_in;
   typedef ScanBuf<NW, B> Buf;
   const float* vec = Buf::vec();
-  _Float16* const S16w = Buf::S16(x.wave);
   compute_barrier();                                   // chunk c is in LDS buffer B
   store_out(x, O, o_t0, o_L);
-
-  // ---- fp16 copy of the state rows, [dv][dk] (wave-private)
-  char* const S16 = reinterpret_cast<char*>(S16w);
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<half4_t*>(S16 + lo.s16w[mb]) = to_half4(ST[mb]);
 
   // ---- X = K S0^T (X[mb]: tokens 16 mb + 4q + e, column dv = l16) and Y^T = S0 Q^T
   // (Yt[nb]: dv 4q + e, token 16 nb + l16); operands of step ks + 1 are read
@@ -595,7 +595,7 @@ __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& l
   }
   half8_t s8[2], k8[2][4], q8[2][4];
   auto load_xy = [&](int ks, int slot) {
-    s8[slot] = lds_b128(S16w, lo.row[ks]);
+    s8[slot] = cat8(to_half4(ST[2 * ks]), to_half4(ST[2 * ks + 1]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       k8[slot][i] = lds_b128(Buf::K(), lo.row[ks] + 16 * D * 2 * i);
@@ -671,8 +671,9 @@ __device__ __forceinline__ void scan_step(const ScanCtx& x, const LaneOffsets& l
   o_t0 = t0;
   o_L = min(C, x.end - t0);
 
-  // ---- S^T = gamma S^T + K^T W, W = uf U; K^T rows dk = 16 mb + i by transposing reads
-  // of tokens 32 s + 4 q + i / 4 (first half) and 16 tokens later (second half)
+  // ---- S^T = gamma S^T + K^T W, W = uf U; K^T rows dk = dk_tile(mb, i / 4) + i % 4 by
+  // transposing reads of tokens 32 s + 4 q + i / 4 (first half) and 16 tokens later
+  // (second half)
   const float gamma = vec[kVecGamma * C];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) ST[mb] *= gamma;
@@ -774,7 +775,7 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
     return;
   }
 
-  // ---- state rows of this wave, transposed: ST[mb] = S[dv][dk = 16 mb + 4 q + e], dv = dvw + l16
+  // ---- state rows of this wave, transposed: ST[mb] = S[dv][dk = dk_tile(mb, q) + e], dv = dvw + l16
   const int dvw = d0 + kRowsPerWave * wave;
   float4_t ST[8];
   const size_t head_off = ((size_t)req * p.Hv + h) * D * D;
@@ -783,7 +784,7 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
     ST[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
     if (p.initial_state != nullptr)
       ST[mb] = *reinterpret_cast<const float4_t*>(p.initial_state + head_off + (size_t)(dvw + l16) * D +
-                                                  16 * mb + 4 * q);
+                                                  dk_tile(mb, q));
   }
 
   ScanCtx x{p, w, h, g, d0, dvw, wave, lane, beg, end, slot0, nch};
@@ -817,7 +818,7 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
   if (p.final_state != nullptr) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
-      *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)(dvw + l16) * D + 16 * mb + 4 * q) = ST[mb];
+      *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)(dvw + l16) * D + dk_tile(mb, q)) = ST[mb];
   }
 }
 
