@@ -823,23 +823,33 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
 }
 
 // ----------------------------------------------------------------------------
-// gdn_chunk_prep: one workgroup per (chunk slot, value head h); key head g = h / G
+// gdn_chunk_prep: one workgroup per (chunk slot, key head g), for the G value
+// heads h = g G .. g G + G - 1 that share g's keys and queries
 //
-//   K, Q tiles -> LDS (direct loads, the scan's swizzled layout); gates of h
-//   Gram tiles on fp16 MFMA, wave w = row block w, taken transposed:
+//   K, Q tiles -> LDS (direct loads, the scan's swizzled layout); the raw gates of
+//   up to four heads are loaded meanwhile (wave w: head w of each batch of four)
+//   Gram tiles on fp16 MFMA, once for all G heads; wave w = row block w, taken
+//   transposed:
 //     K_nb K_w^T and K_nb Q_w^T (nb <= w), Q_w Q_w^T
 //   so that lane (l16, q) of tile nb holds row r = 16 w + l16, columns
 //   i = 16 nb + 4 q + e of K K^T and Q K^T: P's MFMA fragment layout (frag_col),
 //   and one decay factor e^{g_r - g_i} serves both A and P
-//   norms from the Gram diagonals: rk_t = (k_t.k_t + eps)^-1/2, rq_t likewise times the scale
-//   T = (I + A)^-1 blockwise from 16x16 blocks: the diagonal blocks by forward
-//   substitution, the blocks below the diagonal column by column,
-//     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj,
-//   on fp32 MFMA (waves 0, 1, 2 take block columns 0, 1, 2); T' = T diag(beta).
+//   norms from the Gram diagonals: rk_t = (k_t.k_t + eps)^-1/2, rq_t likewise times
+//   the scale; the normalized, masked Gram values stay in registers:
+//     kn = rk_r rk_i (K K^T)_ri (i < r),  pn = rq_r rk_i (Q K^T)_ri (i <= r)
+//   per value head h:
+//     cumulative log decay g and beta of h; the per-token factors
+//     P = e^{g_r - g_i} pn (MFMA fragments, straight from registers)
+//     A = beta_r e^{g_r - g_i} kn
+//     T = (I + A)^-1 blockwise from 16x16 blocks: the diagonal blocks by forward
+//     substitution, the blocks below the diagonal column by column,
+//       T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj,
+//     on fp32 MFMA (waves 0, 1, 2 take block columns 0, 1, 2); T' = T diag(beta).
 // The K, Q tiles are dead once the Gram tiles are in registers; A and T reuse
 // their LDS, which keeps a workgroup at 40 KiB (four per CU).
 // ----------------------------------------------------------------------------
 constexpr int kPrepThreads = 256;
+constexpr int kPrepWaves = kPrepThreads / 64;
 
 struct PrepSmem {
   union {
@@ -850,24 +860,54 @@ struct PrepSmem {
     } m;
   } u;
   float wtmp[4][16 * 17];         // per-wave 16x16 staging for MFMA operands
-  float g[C], beta[C], rk[C], rq[C];
+  float g[2][C], beta[2][C];      // gates of the current head (alternate buffers)
+  float rk[C], rq[C];
 };
 
 // row block of the Gram/P tiles -> fragment indices (kFragRow / kFragStep order)
 __device__ __forceinline__ int frag_index(int rb, int s) { return rb == 3 ? 4 + s : rb == 2 ? 2 + s : rb; }
 
+// Raw gates of head h at token t (rows >= L read as zero).
+struct RawGates {
+  float a, b;
+};
+__device__ __forceinline__ RawGates load_gates(const ChunkArgs& p, int t0, int L, int h, int t) {
+  const int gate_bytes = ((L - 1) * p.Hv + 1) * 4;
+  RawGates r;
+  r.a = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
+  r.b = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
+  return r;
+}
+
+// Cumulative log decay (inclusive prefix sum over the 64 lanes = tokens) and beta
+// of head h; tokens >= L get log decay 0 and beta 0.
+__device__ __forceinline__ void gates_of(const ChunkArgs& p, int h, int L, int t, RawGates r, float* g,
+                                         float* beta) {
+  float la = 0.f, be = 0.f;
+  if (t < L) {
+    la = -expf(p.A_log[h]) * softplus_f(r.a + p.dt_bias[h]);
+    be = sigmoid_f(r.b);
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(la, d, 64);
+    if (t >= d) la += y;
+  }
+  g[t] = la;
+  beta[t] = be;
+}
+
 __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w, int n_items) {
   __shared__ PrepSmem sm;
-  // XCD-aware order: the value heads of one chunk and key head share an XCD's L2
-  const int per_xcd = (int)(gridDim.x / 8);
-  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int item = (int)blockIdx.x;
   if (item >= n_items) return;
-  const int slot = item / p.Hv, h = item % p.Hv, g = h / p.group;
+  const int slot = item / p.Hk, g = item % p.Hk;
   int req, t0, L;
   if (!locate_chunk(p, w, slot, &req, &t0, &L)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q = lane >> 4;
+  const int G = p.group, h0 = g * G;
 
   // ---- K, Q tiles into LDS (rows >= L read as zero): wave w copies rows 16 w .. 16 w + 15
   {
@@ -885,55 +925,40 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
       load_lds16(rq, sm.u.kq[1] + 4 * blk * D, off, 16 * wave * krow * 2);
     }
   }
-
-  // ---- gates of head h (wave 0, while the loads are in flight): cumulative log decay, beta
-  if (wave == 0) {
-    const int t = lane;
-    const int gate_bytes = ((L - 1) * p.Hv + 1) * 4;      // tokens >= L read as zero
-    const float a = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
-    const float b = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
-    float la = 0.f, be = 0.f;
-    if (t < L) {
-      la = -expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]);
-      be = sigmoid_f(b);
-    }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {            // inclusive prefix sum over the 64 lanes
-      const float y = __shfl_up(la, d, 64);
-      if (t >= d) la += y;
-    }
-    sm.g[t] = la;
-    sm.beta[t] = be;
-  }
+  // raw gates of the first batch of heads (wave w: head h0 + w), in flight with the tiles
+  RawGates raw = {0.f, 0.f};
+  if (wave < G) raw = load_gates(p, t0, L, h0 + wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
 
   // ---- Gram tiles of row block wave
-  const _Float16* Kt = sm.u.kq[0];
-  const _Float16* Qt = sm.u.kq[1];
   float4_t kk[4], kq[4], qq = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    kk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    kq[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  const int sw = kv_swizzle(l16);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int uoff = 16 * ((4 * ks + q) ^ sw);
-    const half8_t kw = lds_b128(Kt, (16 * wave + l16) * (D * 2) + uoff);
-    const half8_t qw = lds_b128(Qt, (16 * wave + l16) * (D * 2) + uoff);
-    half8_t kn[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) kn[nb] = lds_b128(Kt, (16 * nb + l16) * (D * 2) + uoff);
+  {
+    const _Float16* Kt = sm.u.kq[0];
+    const _Float16* Qt = sm.u.kq[1];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      if (nb <= wave) {
-        kk[nb] = mfma_f16(kn[nb], kw, kk[nb]);    // KK[16 w + l16][16 nb + 4q + e]
-        kq[nb] = mfma_f16(kn[nb], qw, kq[nb]);    // QK[16 w + l16][16 nb + 4q + e]
-      }
+      kk[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      kq[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-    qq = mfma_f16(qw, qw, qq);
+    const int sw = kv_swizzle(l16);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int uoff = 16 * ((4 * ks + q) ^ sw);
+      const half8_t kw = lds_b128(Kt, (16 * wave + l16) * (D * 2) + uoff);
+      const half8_t qw = lds_b128(Qt, (16 * wave + l16) * (D * 2) + uoff);
+      half8_t kn[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) kn[nb] = lds_b128(Kt, (16 * nb + l16) * (D * 2) + uoff);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (nb <= wave) {
+          kk[nb] = mfma_f16(kn[nb], kw, kk[nb]);    // KK[16 w + l16][16 nb + 4q + e]
+          kq[nb] = mfma_f16(kn[nb], qw, kq[nb]);    // QK[16 w + l16][16 nb + 4q + e]
+        }
+      }
+      qq = mfma_f16(qw, qw, qq);
+    }
   }
   // norms: the diagonal element of row 16 w + l16 sits in lane group q = l16 / 4, element e = l16 % 4
   {
@@ -951,96 +976,125 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
   }
   lds_barrier();                                   // K, Q tiles dead from here; their LDS becomes A, T
 
-  // ---- per-token factors, one row per wave:
-  //   kVecZ e^{g_t} rk_t, kVecO e^{g_t} rq_t, kVecU e^{g_L - g_t} rk_t, kVecGamma e^{g_L}
+  // ---- normalized, masked Gram values of row r = 16 w + l16, columns i = 16 nb + 4 q + e
+  const int r = 16 * wave + l16;
   {
-    const int t = lane;
-    const float gt = sm.g[t], gL = sm.g[C - 1];
-    const float v = wave == kVecZ ? expf(gt) * sm.rk[t]
-                  : wave == kVecO ? expf(gt) * sm.rq[t]
-                  : wave == kVecU ? expf(gL - gt) * sm.rk[t]
-                                  : expf(gL);
-    w.vec[((size_t)slot * p.Hv + h) * kVecRows * C + wave * C + t] = v;
-  }
-
-  // ---- A (rows 16 w + l16 of the fp32 LDS matrix; the blocks above the diagonal
-  // are never read) and the P fragments of row block w, from one decay factor
-  // per element: row r = 16 w + l16, columns i = 16 nb + 4q + e
-  {
-    const int r = 16 * wave + l16;
-    const float gr = sm.g[r], rqr = sm.rq[r], brk = sm.beta[r] * sm.rk[r];
-    half4_t ph[4];
+    const float rkr = sm.rk[r], rqr = sm.rq[r];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const float4_t gi = *reinterpret_cast<const float4_t*>(&sm.g[16 * nb + 4 * q]);
       const float4_t ki = *reinterpret_cast<const float4_t*>(&sm.rk[16 * nb + 4 * q]);
-      float4_t av;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * nb + 4 * q + e;
-        const float dec = nb <= wave ? fast_exp(fminf(gr - gi[e], 0.f)) * ki[e] : 0.f;
-        av[e] = i < r ? brk * dec * kk[nb][e] : 0.f;
-        ph[nb][e] = (_Float16)(i <= r ? rqr * dec * kq[nb][e] : 0.f);
+        kk[nb][e] = i < r ? rkr * ki[e] * kk[nb][e] : 0.f;
+        kq[nb][e] = i <= r ? rqr * ki[e] * kq[nb][e] : 0.f;
       }
-      if (nb <= wave) *reinterpret_cast<float4_t*>(&sm.u.m.A[r * AS + 16 * nb + 4 * q]) = av;
     }
-    _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * kFragHalves;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      if (2 * s <= wave)
-        *reinterpret_cast<half8_t*>(Pw + frag_index(wave, s) * 512 + lane * 8) = cat8(ph[2 * s], ph[2 * s + 1]);
   }
-  lds_barrier();
-
-  // ---- T, step 1: the four diagonal 16x16 blocks (wave 0, lane = 16 block + column)
   float* const A = sm.u.m.A;
   float* const T = sm.u.m.T;
-  if (wave == 0) {
-    const int blk = lane >> 4, j = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float* arow = &A[(16 * blk + r) * AS + 16 * blk];
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-      for (int i = 0; i < r; i += 4) {
-        const float4_t a4 = *reinterpret_cast<const float4_t*>(&arow[i]);
-        s0 = fmaf(a4.x, x[i], s0);
-        s1 = fmaf(a4.y, x[i + 1], s1);
-        s2 = fmaf(a4.z, x[i + 2], s2);
-        s3 = fmaf(a4.w, x[i + 3], s3);
+
+  for (int hb = 0; hb < G; hb += kPrepWaves) {
+    if (hb > 0 && wave < G - hb) raw = load_gates(p, t0, L, h0 + hb + wave, lane);
+    for (int hh = 0; hh < min(kPrepWaves, G - hb); ++hh) {
+      const int h = h0 + hb + hh;
+      const int gb = (hb + hh) & 1;                // gate buffer of this head
+      float* const gs = sm.g[gb];
+      float* const bs = sm.beta[gb];
+      if (wave == hh) gates_of(p, h, L, lane, raw, gs, bs);
+      lds_barrier();
+
+      // ---- per-token factors, one row per wave:
+      //   kVecZ e^{g_t} rk_t, kVecO e^{g_t} rq_t, kVecU e^{g_L - g_t} rk_t, kVecGamma e^{g_L}
+      {
+        const int t = lane;
+        const float gt = gs[t], gL = gs[C - 1];
+        const float v = wave == kVecZ ? expf(gt) * sm.rk[t]
+                      : wave == kVecO ? expf(gt) * sm.rq[t]
+                      : wave == kVecU ? expf(gL - gt) * sm.rk[t]
+                                      : expf(gL);
+        w.vec[((size_t)slot * p.Hv + h) * kVecRows * C + wave * C + t] = v;
       }
-      x[r] = (r == j ? 1.f : 0.f) - ((s0 + s1) + (s2 + s3));
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) T[(16 * blk + r) * AS + 16 * blk + j] = x[r];
-  }
-  lds_barrier();
 
-  // ---- T, step 2: blocks below the diagonal; wave j sweeps block column j
-  if (wave < 3) {
-    float* wt = sm.wtmp[wave];
-    for (int ib = wave + 1; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, wave, lane);
-  }
-  lds_barrier();
-
-  // ---- T' = T diag(beta) fragments of row block w (blocks above the diagonal are zero)
-  {
-    _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * kFragHalves;
-    const int r = 16 * wave + l16;
+      // ---- A (rows 16 w + l16 of the fp32 LDS matrix; the blocks above the diagonal
+      // are never read) and the P fragments of row block w, from one decay factor
+      // per element
+      {
+        const float gr = gs[r], br = bs[r];
+        half4_t ph[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (2 * s <= wave) {
-        half8_t x;
+        for (int nb = 0; nb < 4; ++nb) {
+          ph[nb] = half4_t{0, 0, 0, 0};                 // blocks above the diagonal
+          if (nb <= wave) {
+            const float4_t gi = *reinterpret_cast<const float4_t*>(&gs[16 * nb + 4 * q]);
+            float4_t av;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = frag_col(s, q, j);
-          x[j] = (c >> 4) <= wave ? (_Float16)(T[r * AS + c] * sm.beta[c]) : (_Float16)0.f;
+            for (int e = 0; e < 4; ++e) {
+              const float dec = fast_exp(fminf(gr - gi[e], 0.f));
+              av[e] = br * dec * kk[nb][e];
+              ph[nb][e] = (_Float16)(dec * kq[nb][e]);
+            }
+            *reinterpret_cast<float4_t*>(&A[r * AS + 16 * nb + 4 * q]) = av;
+          }
         }
-        *reinterpret_cast<half8_t*>(Tw + frag_index(wave, s) * 512 + lane * 8) = x;
+        _Float16* Pw = w.P + ((size_t)slot * p.Hv + h) * kFragHalves;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (2 * s <= wave)
+            *reinterpret_cast<half8_t*>(Pw + frag_index(wave, s) * 512 + lane * 8) = cat8(ph[2 * s], ph[2 * s + 1]);
       }
+      lds_barrier();
+
+      // ---- T, step 1: the four diagonal 16x16 blocks (wave 0, lane = 16 block + column)
+      if (wave == 0) {
+        const int blk = lane >> 4, j = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) x[rr] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float* arow = &A[(16 * blk + rr) * AS + 16 * blk];
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+          for (int i = 0; i < rr; i += 4) {
+            const float4_t a4 = *reinterpret_cast<const float4_t*>(&arow[i]);
+            s0 = fmaf(a4.x, x[i], s0);
+            s1 = fmaf(a4.y, x[i + 1], s1);
+            s2 = fmaf(a4.z, x[i + 2], s2);
+            s3 = fmaf(a4.w, x[i + 3], s3);
+          }
+          x[rr] = (rr == j ? 1.f : 0.f) - ((s0 + s1) + (s2 + s3));
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) T[(16 * blk + rr) * AS + 16 * blk + j] = x[rr];
+      }
+      lds_barrier();
+
+      // ---- T, step 2: blocks below the diagonal; wave j sweeps block column j
+      if (wave < 3) {
+        float* wt = sm.wtmp[wave];
+        for (int ib = wave + 1; ib < 4; ++ib) t_offdiag_block(A, T, wt, ib, wave, lane);
+      }
+      lds_barrier();
+
+      // ---- T' = T diag(beta) fragments of row block w (blocks above the diagonal are zero)
+      {
+        _Float16* Tw = w.T + ((size_t)slot * p.Hv + h) * kFragHalves;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (2 * s <= wave) {
+            half8_t x;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int c = frag_col(s, q, j);
+              x[j] = (c >> 4) <= wave ? (_Float16)(T[r * AS + c] * bs[c]) : (_Float16)0.f;
+            }
+            *reinterpret_cast<half8_t*>(Tw + frag_index(wave, s) * 512 + lane * 8) = x;
+          }
+        }
+      }
+      // the next head's gates go to the other buffer, and its first LDS writes
+      // come after one more barrier
     }
   }
 }
@@ -1055,9 +1109,8 @@ hipError_t launch_chunk(const ChunkArgs& p, int io_dtype, hipStream_t stream) {
   const Ws w = ws_layout(p.workspace, p.max_chunks, p.R, p.Hk, p.Hv);
   hipLaunchKernelGGL(gdn_chunk_index, dim3(1), dim3(kThreads), 0, stream, p, w);
   if (p.max_chunks > 0) {
-    const int n_prep = p.max_chunks * p.Hv;
-    const int grid_prep = (n_prep + 7) / 8 * 8;
-    hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)grid_prep), dim3(kPrepThreads), 0, stream, p, w, n_prep);
+    const int n_prep = p.max_chunks * p.Hk;
+    hipLaunchKernelGGL(gdn_chunk_prep, dim3((unsigned)n_prep), dim3(kPrepThreads), 0, stream, p, w, n_prep);
   }
   // Both scan configurations hold one workgroup per CU. 64-row tiles move half the
   // k, q, T', P bytes per state row; they are taken when their workgroups fill

@@ -79,7 +79,8 @@ def test_chunk_packing_invariance_bitwise():
         assert np.array_equal(alone["final_state"][0], packed["final_state"][r])
 
 
-# 8 requests x 16 key heads x group 2: enough workgroups for the 64-row scan tiles
+# 16 key heads x group 2: 4 or more requests give enough workgroups for the
+# 64-row scan tiles
 WIDE = dict(Hk=16, Hv=32)
 
 
@@ -91,15 +92,25 @@ def test_chunk_wide_tiles_vs_oracle():
     assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "chunk 64-row tiles")
 
 
-def test_chunk_tile_width_invariance_bitwise():
-    # the batch runs the 64-row scan tiles, a request alone the 32-row ones; each
-    # wave does the same arithmetic on its 16 state rows in both
-    lengths = [130, 64, 1, 200, 65, 9, 128, 70]
+def test_chunk_wide_tiles_few_requests_vs_oracle():
+    lengths = [200, 1, 64, 97]                      # 4 x 16 x 2 heads x 2 tiles = 256 workgroups
+    inp = make_inputs(lengths, WIDE["Hk"], WIDE["Hv"], 128, 128, "f16", seed=48)
+    _case(f"chunk 64-row tiles Hk={WIDE['Hk']} Hv={WIDE['Hv']} lengths={lengths}")
+    res = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK)
+    ref_o, ref_s, _ = oracle_forward(inp, O)
+    assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "chunk 64-row tiles, 4 requests")
+
+
+@pytest.mark.parametrize("lengths", [[130, 64, 1, 200, 65, 9, 128, 70], [300, 2, 129, 64]])
+def test_chunk_tile_width_invariance_bitwise(lengths):
+    # with 16 key heads x group 2 the batch runs the 64-row scan tiles, a request
+    # alone the 32-row ones; each 16-row block of the state goes through the same
+    # arithmetic in both
     inp = make_inputs(lengths, WIDE["Hk"], WIDE["Hv"], 128, 128, "f16", seed=47)
     _case(f"chunk tile width invariance {lengths}")
     packed = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK)
     cu = inp["cu_seqlens"]
-    for r in (0, 3, 5):
+    for r in sorted({0, len(lengths) // 2, len(lengths) - 1}):
         sub = dict(inp)
         for n in ("q", "k", "v", "a", "b"):
             sub[n] = inp[n][cu[r]:cu[r + 1]]
