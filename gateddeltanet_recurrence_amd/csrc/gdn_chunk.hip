@@ -893,8 +893,8 @@ __device__ __forceinline__ void gates_of(const ChunkArgs& p, int h, int L, int t
     const float y = __shfl_up(la, d, 64);
     if (t >= d) la += y;
   }
-  g[t] = la;
-  beta[t] = be;
+  *g = la;
+  *beta = be;
 }
 
 __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w, int n_items) {
@@ -925,9 +925,9 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
       load_lds16(rq, sm.u.kq[1] + 4 * blk * D, off, 16 * wave * krow * 2);
     }
   }
-  // raw gates of the first batch of heads (wave w: head h0 + w), in flight with the tiles
-  RawGates raw = {0.f, 0.f};
-  if (wave < G) raw = load_gates(p, t0, L, h0 + wave, lane);
+  // gates of the first batch of heads (wave w: head h0 + w) while the tiles are in flight
+  float gw = 0.f, bw = 0.f;
+  if (wave < G) gates_of(p, h0 + wave, L, lane, load_gates(p, t0, L, h0 + wave, lane), &gw, &bw);
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
 
@@ -995,13 +995,16 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
   float* const T = sm.u.m.T;
 
   for (int hb = 0; hb < G; hb += kPrepWaves) {
-    if (hb > 0 && wave < G - hb) raw = load_gates(p, t0, L, h0 + hb + wave, lane);
+    if (hb > 0 && wave < G - hb) gates_of(p, h0 + hb + wave, L, lane, load_gates(p, t0, L, h0 + hb + wave, lane), &gw, &bw);
     for (int hh = 0; hh < min(kPrepWaves, G - hb); ++hh) {
       const int h = h0 + hb + hh;
       const int gb = (hb + hh) & 1;                // gate buffer of this head
       float* const gs = sm.g[gb];
       float* const bs = sm.beta[gb];
-      if (wave == hh) gates_of(p, h, L, lane, raw, gs, bs);
+      if (wave == hh) {
+        gs[lane] = gw;
+        bs[lane] = bw;
+      }
       lds_barrier();
 
       // ---- per-token factors, one row per wave:
