@@ -439,11 +439,12 @@ __device__ __forceinline__ void loader_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Compute waves: the same barrier; the acquire fence keeps this chunk's LDS reads
-// below it. The reads of the buffer that the loaders refill next returned their
-// data before this wave got here, and the wave-private state copy is never read
-// by another wave, so no release fence is needed.
+// Compute waves: the same barrier. The release fence makes this wave's reads of
+// the previous chunk (whose buffer the loaders refill next) complete before it:
+// the compiler may otherwise leave the last of them in flight across the barrier.
+// The acquire fence keeps this chunk's reads below it.
 __device__ __forceinline__ void compute_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
