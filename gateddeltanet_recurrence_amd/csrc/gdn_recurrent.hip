@@ -310,10 +310,11 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
 
   for (int ts = t0; ts < t1; ts += kStageTokens) {
     const int nt = min(kStageTokens, t1 - ts);
-    // ---- stage: 16 threads per token normalise k and q and form the gates
-    {
-      const int j = tid / TPT, part = tid % TPT;
-      if (j < nt) {
+    // ---- stage: 16 threads per token normalise k and q and form the gates (a
+    // workgroup of fewer than four waves takes several passes)
+    for (int j = tid / TPT; j < nt; j += (int)blockDim.x / TPT) {
+      const int part = tid % TPT;
+      {
         const int t = ts + j;
         const IO* krow = kp + ((size_t)t * p.Hk + g) * DK + part * EPT;
         const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK + part * EPT;
@@ -346,12 +347,12 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
           sm.kq[j] = skq * rk * rq;
         }
       }   // a token's 16 lanes are one aligned DPP row group: active or idle together
-      // this block's value rows of every staged token
-      for (int idx = tid; idx < nt * block_rows; idx += blockDim.x) {
-        const int jj = idx / block_rows, rr = idx % block_rows;
-        const int row = block_row0 + rr;
-        sm.v[jj][rr] = row < Dv ? IoOps<IO>::load1(vp + ((size_t)(ts + jj) * p.Hv + h) * Dv + row) : 0.f;
-      }
+    }
+    // this block's value rows of every staged token
+    for (int idx = tid; idx < nt * block_rows; idx += blockDim.x) {
+      const int jj = idx / block_rows, rr = idx % block_rows;
+      const int row = block_row0 + rr;
+      sm.v[jj][rr] = row < Dv ? IoOps<IO>::load1(vp + ((size_t)(ts + jj) * p.Hv + h) * Dv + row) : 0.f;
     }
     __syncthreads();
 

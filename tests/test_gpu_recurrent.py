@@ -169,6 +169,22 @@ def test_capture_count_and_untouched_rows():
             assert rel_max(got[r, :n], ref_cap[r, :n]) <= TOL_F32_REL
 
 
+@pytest.mark.parametrize("Dk,Dv,lengths", [(16, 16, [16]), (16, 16, [21, 6]), (32, 16, [40])])
+def test_capsule_small_heads_vs_oracle(Dk, Dv, lengths):
+    # one-wave workgroups (small Dv) stage a group of up to 16 tokens in several
+    # passes; every captured value and every output is checked, not just coverage
+    cap = max(lengths)
+    inp = make_inputs(lengths, 2, 2, Dk, Dv, "f32", seed=16, capacity=cap)
+    _case(f"capsule Dk={Dk} Dv={Dv} lengths={lengths}")
+    res = run_forward(inp, torch, gdn, capacity=cap, poison=-7.0)
+    ref_o, ref_s, ref_cap = oracle_forward(inp, O, capacity=cap, poison=-7.0)
+    assert_parity("f32", res["output"], ref_o, res["final_state"], ref_s, "capsule small heads")
+    got = res["state_update"]
+    for r, L in enumerate(lengths):
+        assert np.all(got[r, L:] == -7.0)
+        assert rel_max(got[r, :L], ref_cap[r, :L]) <= TOL_F32_REL
+
+
 def test_capture_count_clamped_to_capacity():
     inp = make_inputs([6, 6], 1, 1, 16, 16, "f32", seed=14, capacity=3)
     cc = np.array([99, -5], np.int32)
