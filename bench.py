@@ -14,8 +14,9 @@ Prints one JSON line: tokens/s, ms per step, the dominant kernel's roofline
 stream, against the 8 TB/s HBM peak) and the float64 oracle timed on this
 host's cores on a bounded sample of the same workload. The line also carries,
 under "workloads", the same measurements for the operator's other workloads:
-speculative verify + replay (HBM roofline) and the ragged and long prefills
-(fp16 MFMA roofline); --workload NAME times just one of them.
+speculative verify + replay (HBM roofline), the ragged and long prefills
+(fp16 MFMA roofline) and the decode step with precomputed effective gates in the
+dense rank-4 layout; --workload NAME times just one of them.
 """
 from __future__ import annotations
 
@@ -134,6 +135,44 @@ def run_decode(args, torch, gdn):
                      "avg_kernel_us": ms_step * 1e3},
     }
     return line, inp
+
+
+def run_decode_effective_dense(args, torch, gdn):
+    """The batched decode step in the operator's other input forms: precomputed
+    effective gates (activation none; alpha in [0.5, 1), beta in [0, 1), synthetic)
+    and the dense rank-4 layout [R, 1, H, D] (no cu_seqlens). Same kernel and
+    state traffic as the batched decode; A_log, dt_bias and cu_seqlens are not read."""
+    import numpy as np
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs("batched_decode")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R = len(inp["cu_seqlens"]) - 1
+    rng = np.random.default_rng(7)
+    alpha = torch.from_numpy(rng.uniform(0.5, 1.0, (N, Hv)).astype(np.float32)).cuda()
+    beta = torch.from_numpy(rng.uniform(0.0, 1.0, (N, Hv)).astype(np.float32)).cuda()
+    q, k, v = (_dev(inp[n], torch).reshape(R, N // R, *inp[n].shape[1:]) for n in ("q", "k", "v"))
+    state_bytes = R * Hv * Dv * Dk * 4
+    n_banks = max(2, -(-BANK_TARGET_BYTES // state_bytes))
+    banks = [_dev(inp["initial_state"], torch) for _ in range(n_banks)]
+    out = torch.empty_like(v)
+    a4, b4 = alpha.reshape(R, N // R, Hv), beta.reshape(R, N // R, Hv)
+
+    def step(i):
+        s = banks[i % n_banks]
+        gdn.gdn_forward(q, k, v, a4, b4, None, None, None, out, initial_state=s, final_state=s,
+                        gate_activation=gdn.GATE_NONE, plan=gdn.PLAN_RECURRENT)
+
+    _log(f"decode, effective gates, dense layout: R={R} Hv={Hv} banks={n_banks}")
+    ms = _time_steps(torch, step, args.steps, args.warmup)
+    nbytes = decode_bytes(inp) - 2 * Hv * 4 - (R + 1) * 4
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"tokens": N, "requests": R, "layout": "dense [R, 1, H, D]",
+                       "gates": "effective (activation none)", "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv},
+            "roofline": {"bound": "hbm", "kernel": "gdn_decode", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_step": nbytes}}
 
 
 def _time_steps(torch, step, steps, warmup):
@@ -298,7 +337,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="all",
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
-                             "hbm_copy"],
+                             "decode_effective_dense", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="length of the oracle CPU-baseline sample (0 skips it)")
@@ -319,6 +358,7 @@ def main():
         fn = {"spec_verify_replay": lambda: run_verify_replay(args, torch, gdn),
               "ragged_prefill": lambda: run_prefill(args, torch, gdn, "ragged_prefill"),
               "long_prefill": lambda: run_prefill(args, torch, gdn, "long_prefill"),
+              "decode_effective_dense": lambda: run_decode_effective_dense(args, torch, gdn),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
         print(json.dumps({"metric": METRIC, "workload": args.workload, **res}), flush=True)
@@ -329,6 +369,7 @@ def main():
             "spec_verify_replay": run_verify_replay(args, torch, gdn),
             "ragged_prefill": run_prefill(args, torch, gdn, "ragged_prefill"),
             "long_prefill": run_prefill(args, torch, gdn, "long_prefill"),
+            "decode_effective_dense": run_decode_effective_dense(args, torch, gdn),
         }
     if args.cpu_seconds > 0:
         _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")

@@ -18,6 +18,8 @@ GDN_ERR_CAPACITY, GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP = 5
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA = 0
+GATE_RAW, GATE_NONE = 0, 1
+ABI_VERSION = 2          # the struct layouts below match this version of include/gdn.h
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -37,7 +39,7 @@ class GdnParams(ctypes.Structure):
         ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
         ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("chunk", ctypes.c_int32),
         ("state_update_capacity", ctypes.c_int32), ("plan", ctypes.c_int32),
-        ("update_rule", ctypes.c_int32),
+        ("update_rule", ctypes.c_int32), ("gate_activation", ctypes.c_int32),
     ]
 
 
@@ -79,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_strerror.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         L.gdn_abi_version.restype = ctypes.c_int
+        if L.gdn_abi_version() != ABI_VERSION:
+            raise LibraryNotBuilt(f"{path} has ABI version {L.gdn_abi_version()}, this binding "
+                                  f"needs {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -97,9 +102,10 @@ def capsule_width(Hk: int, Hv: int, Dk: int, Dv: int) -> int:
 
 
 def make_params(N, R, Hk, Hv, Dk, Dv, io_dtype, *, scale=0.0, chunk=0, capacity=0,
-                plan=PLAN_AUTO, update_rule=RULE_GATED_DELTA) -> GdnParams:
+                plan=PLAN_AUTO, update_rule=RULE_GATED_DELTA, gate_activation=GATE_RAW) -> GdnParams:
     return GdnParams(int(N), int(R), int(Hk), int(Hv), int(Dk), int(Dv), int(io_dtype),
-                     float(scale), int(chunk), int(capacity), int(plan), int(update_rule))
+                     float(scale), int(chunk), int(capacity), int(plan), int(update_rule),
+                     int(gate_activation))
 
 
 # ------------------------------------------------------------------ helpers
@@ -161,19 +167,34 @@ def _host_i32(arr):
 def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state=None,
                 final_state=None, state_update=None, capture_count=None, cu_seqlens_host=None,
                 scale: float = 0.0, chunk: int = 0, state_update_capacity: int = 0,
-                plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA, workspace=None,
+                plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA,
+                gate_activation: int = GATE_RAW, num_reqs: Optional[int] = None, workspace=None,
                 stream=None, check: bool = True) -> int:
     """gdn_forward of include/gdn.h on torch tensors; returns the status code.
 
-    q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32; a, b
-    [N, Hv] float32; A_log, dt_bias [Hv] float32; cu_seqlens [R+1] int32;
-    states [R, Hv, Dv, Dk] float32; state_update [R, capacity, W] float32;
-    capture_count [R] int32; workspace a uint8 GPU tensor (CHUNK plan).
+    q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32 (for the
+    dense rank-4 layout, cu_seqlens None: [R, S, H, D] tensors, or the same
+    flattened; R from num_reqs or the leading dim); a, b [N, Hv] float32 (raw
+    gate inputs, or alpha and beta with gate_activation GATE_NONE, when A_log
+    and dt_bias may be None); A_log, dt_bias [Hv] float32; cu_seqlens [R+1]
+    int32 or None; states [R, Hv, Dv, Dk] float32; state_update
+    [R, capacity, W] float32; capture_count [R] int32; workspace a uint8 GPU
+    tensor (CHUNK plan).
     """
     torch = _torch()
+    if cu_seqlens is None and q.dim() == 4:
+        if num_reqs is None:
+            num_reqs = q.shape[0]
+        q, k, v, output = (x.reshape(-1, x.shape[2], x.shape[3]) for x in (q, k, v, output))
+        a, b = (x.reshape(-1, x.shape[-1]) for x in (a, b))
     N, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
-    R = cu_seqlens.shape[0] - 1
+    if cu_seqlens is None:
+        if num_reqs is None:
+            raise ValueError("the dense layout (cu_seqlens None) needs num_reqs or [R, S, H, D] inputs")
+        R = int(num_reqs)
+    else:
+        R = cu_seqlens.shape[0] - 1
     io = q.dtype
     _need(q, "q", (N, Hk, Dk))
     _need(k, "k", (N, Hk, Dk), io)
@@ -199,7 +220,8 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_st
             raise ValueError("workspace must be a contiguous GPU tensor")
         ws_ptr, ws_bytes = int(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     params = make_params(N, R, Hk, Hv, Dk, Dv, _io_code(io), scale=scale, chunk=chunk,
-                         capacity=state_update_capacity, plan=plan, update_rule=update_rule)
+                         capacity=state_update_capacity, plan=plan, update_rule=update_rule,
+                         gate_activation=gate_activation)
     tens = GdnTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                       _ptr(cu_seqlens), host_cu_ptr, _ptr(initial_state), _ptr(final_state),
                       _ptr(output), _ptr(state_update), _ptr(capture_count))

@@ -44,6 +44,7 @@ struct Resolved {
 int check_params(const gdn_params* p, Resolved* out) {
   if (p == nullptr) return GDN_ERR_NULL;
   if (p->update_rule != GDN_RULE_GATED_DELTA) return GDN_ERR_RULE;
+  if (p->gate_activation != GDN_GATE_RAW && p->gate_activation != GDN_GATE_NONE) return GDN_ERR_RULE;
   if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_F16) return GDN_ERR_DTYPE;
   if (p->num_tokens < 0 || p->num_reqs < 0 || p->num_k_heads <= 0 || p->num_v_heads <= 0)
     return GDN_ERR_SHAPE;
@@ -83,10 +84,15 @@ int check_cu_host(const int32_t* cu, int64_t R, int64_t N, int64_t* max_len, int
   return GDN_OK;
 }
 
-// Resolves the plan and the chunk-slot count. `capsule` says a capsule is written.
-int resolve_plan(const gdn_params* p, const int32_t* cu_host, bool capsule, Resolved* rv) {
+// Resolves the plan and the chunk-slot count. `capsule` says a capsule is written;
+// `dense` says every request holds N / R tokens (no cu_seqlens).
+int resolve_plan(const gdn_params* p, const int32_t* cu_host, bool capsule, Resolved* rv,
+                 bool dense = false) {
   int64_t max_len = 0, slots = 0;
-  if (cu_host != nullptr) {
+  if (dense) {
+    max_len = rv->R > 0 ? rv->N / rv->R : 0;
+    slots = rv->R * ((max_len + gdn::kChunk - 1) / gdn::kChunk);
+  } else if (cu_host != nullptr) {
     int st = check_cu_host(cu_host, rv->R, rv->N, &max_len, &slots);
     if (st != GDN_OK) return st;
   } else {
@@ -129,7 +135,7 @@ const char* gdn_strerror(int status) {
     case GDN_ERR_CAPACITY: return "capacity is negative or an accepted/captured count exceeds it";
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_PLAN: return "the forced plan cannot run these arguments";
-    case GDN_ERR_RULE: return "only the gated delta update rule is implemented";
+    case GDN_ERR_RULE: return "only the gated delta update rule, with raw or effective gates, is implemented";
     case GDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     default: return "unknown status";
   }
@@ -167,8 +173,12 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
   if (capsule && rv.cap == 0) return GDN_ERR_CAPACITY;   // a capsule needs rows
   if (rv.R == 0) return rv.N == 0 ? GDN_OK : GDN_ERR_SHAPE;
 
-  // required pointers
-  if (t->cu_seqlens == nullptr || t->A_log == nullptr || t->dt_bias == nullptr) return GDN_ERR_NULL;
+  // required pointers; without cu_seqlens every request holds N / R tokens (dense
+  // rank-4 layout), and the effective gates need no A_log, dt_bias
+  const bool dense = t->cu_seqlens == nullptr;
+  if (dense && (t->cu_seqlens_host != nullptr || rv.N % rv.R != 0)) return GDN_ERR_SHAPE;
+  const bool gate_none = p->gate_activation == GDN_GATE_NONE;
+  if (!gate_none && (t->A_log == nullptr || t->dt_bias == nullptr)) return GDN_ERR_NULL;
   if (rv.N > 0 && (t->q == nullptr || t->k == nullptr || t->v == nullptr || t->a == nullptr ||
                    t->b == nullptr || t->output == nullptr))
     return GDN_ERR_NULL;
@@ -178,8 +188,9 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
   for (const void* ptr : vec_ptrs)
     if (ptr != nullptr && !aligned16(ptr)) return GDN_ERR_SHAPE;
 
-  st = resolve_plan(p, t->cu_seqlens_host, capsule, &rv);
+  st = resolve_plan(p, t->cu_seqlens_host, capsule, &rv, dense);
   if (st != GDN_OK) return st;
+  const int32_t dense_len = dense ? (int32_t)(rv.N / rv.R) : 0;
 
   // overlap rules
   const size_t io = io_bytes(p->io_dtype);
@@ -224,6 +235,7 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
     a.N = (int32_t)rv.N; a.R = (int32_t)rv.R; a.Hk = (int32_t)rv.Hk; a.Hv = (int32_t)rv.Hv;
     a.Dk = (int32_t)rv.Dk; a.Dv = (int32_t)rv.Dv; a.group = (int32_t)(rv.Hv / rv.Hk);
     a.capacity = rv.cap; a.capsule_width = (int32_t)W; a.scale = rv.scale;
+    a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
     err = gdn::launch_recurrent(a, p->io_dtype, s);
   } else {
     gdn::ChunkArgs a{};
@@ -233,6 +245,7 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
     a.workspace = workspace;
     a.N = (int32_t)rv.N; a.R = (int32_t)rv.R; a.Hk = (int32_t)rv.Hk; a.Hv = (int32_t)rv.Hv;
     a.group = (int32_t)(rv.Hv / rv.Hk); a.max_chunks = (int32_t)rv.chunk_slots; a.scale = rv.scale;
+    a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
     err = gdn::launch_chunk(a, p->io_dtype, s);
   }
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;

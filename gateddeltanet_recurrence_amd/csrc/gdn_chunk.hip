@@ -104,10 +104,6 @@ __host__ inline size_t ws_bytes(int64_t slots, int R, int Hk, int Hv) {
          align256((size_t)slots * Hv * kVecRows * C * 4);
 }
 
-__device__ __forceinline__ int clamp_cu(const int32_t* cu, int i, int N) {
-  return min(max(cu[i], 0), N);
-}
-
 }  // namespace
 
 // ----------------------------------------------------------------------------
@@ -122,10 +118,10 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_index(ChunkArgs p, Ws w) {
   const int tid = threadIdx.x;
   const int per = (p.R + kThreads - 1) / kThreads;
   const int r0 = min(tid * per, p.R), r1 = min(r0 + per, p.R);
-  int prev = clamp_cu(p.cu_seqlens, r0, p.N);
+  int prev = seq_start(p, r0);
   int sum = 0;
   for (int r = r0; r < r1; ++r) {
-    const int nxt = max(clamp_cu(p.cu_seqlens, r + 1, p.N), prev);
+    const int nxt = max(seq_start(p, r + 1), prev);
     sum += (nxt - prev + C - 1) / C;
     prev = nxt;
   }
@@ -139,10 +135,10 @@ __global__ void __launch_bounds__(kThreads) gdn_chunk_index(ChunkArgs p, Ws w) {
     __syncthreads();
   }
   int run = tid > 0 ? part[tid - 1] : 0;
-  prev = clamp_cu(p.cu_seqlens, r0, p.N);
+  prev = seq_start(p, r0);
   for (int r = r0; r < r1; ++r) {
     w.chunk_start[r] = run;
-    const int nxt = max(clamp_cu(p.cu_seqlens, r + 1, p.N), prev);
+    const int nxt = max(seq_start(p, r + 1), prev);
     run += (nxt - prev + C - 1) / C;
     prev = nxt;
   }
@@ -172,8 +168,8 @@ __device__ __forceinline__ bool locate_chunk(const ChunkArgs& p, const Ws& w, in
     const int mid = (lo + hi + 1) >> 1;
     if (w.chunk_start[mid] <= slot) lo = mid; else hi = mid - 1;
   }
-  const int beg = clamp_cu(p.cu_seqlens, lo, p.N);
-  const int end = max(clamp_cu(p.cu_seqlens, lo + 1, p.N), beg);
+  const int beg = seq_start(p, lo);
+  const int end = max(seq_start(p, lo + 1), beg);
   *req = lo;
   *t0 = beg + C * (slot - w.chunk_start[lo]);
   *len = min(C, end - *t0);
@@ -727,8 +723,8 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, q = lane >> 4;
 
-  const int beg = clamp_cu(p.cu_seqlens, req, p.N);
-  const int end = max(clamp_cu(p.cu_seqlens, req + 1, p.N), beg);
+  const int beg = seq_start(p, req);
+  const int end = max(seq_start(p, req + 1), beg);
   const int slot0 = w.chunk_start[req];
   int nch = (end - beg + C - 1) / C;
   nch = max(0, min(nch, p.max_chunks - slot0));
@@ -886,8 +882,9 @@ __device__ __forceinline__ void gates_of(const ChunkArgs& p, int h, int L, int t
                                          float* beta) {
   float la = 0.f, be = 0.f;
   if (t < L) {
-    la = -expf(p.A_log[h]) * softplus_f(r.a + p.dt_bias[h]);
-    be = sigmoid_f(r.b);
+    const bool gnone = p.gate_none != 0;           // A_log, dt_bias may be null then
+    la = gate_log_alpha(r.a, gnone, gnone ? 0.f : expf(p.A_log[h]), gnone ? 0.f : p.dt_bias[h]);
+    be = gate_beta(r.b, gnone);
   }
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {

@@ -68,6 +68,24 @@ __device__ __forceinline__ float decay_from_raw(float a, float expA, float dt_bi
 
 __device__ __forceinline__ float sigmoid_f(float b) { return 1.0f / (1.0f + expf(-b)); }
 
+// Precomputed effective decay (gate activation none), clamped to [0, 1], the
+// range of the raw form.
+__device__ __forceinline__ float effective_decay(float a) { return fminf(fmaxf(a, 0.f), 1.f); }
+
+// alpha and beta of a token from its two gate inputs: raw (fused activations) or
+// effective (activation none).
+__device__ __forceinline__ float gate_alpha(float a, bool none, float expA, float dt_bias) {
+  return none ? effective_decay(a) : decay_from_raw(a, expA, dt_bias);
+}
+__device__ __forceinline__ float gate_beta(float b, bool none) { return none ? b : sigmoid_f(b); }
+
+// log alpha for the chunked form. An effective decay of 0 is taken as the
+// smallest normal float (log -87.3): the state is then reset up to a factor
+// 1.2e-38 instead of exactly.
+__device__ __forceinline__ float gate_log_alpha(float a, bool none, float expA, float dt_bias) {
+  return none ? logf(fmaxf(effective_decay(a), 1.17549435e-38f)) : -expA * softplus_f(a + dt_bias);
+}
+
 }  // namespace gdn
 
 namespace gdn {

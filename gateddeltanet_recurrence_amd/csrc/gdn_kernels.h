@@ -17,7 +17,7 @@ struct RecurrentArgs {
   const float* b;
   const float* A_log;
   const float* dt_bias;
-  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens;    // null: dense layout, dense_len tokens per request
   const float* initial_state;   // may be null (zero state)
   float* final_state;           // may be null; may equal initial_state
   void* output;
@@ -29,6 +29,8 @@ struct RecurrentArgs {
   int32_t capacity;
   int32_t capsule_width;        // Hv + Hk*Dk + Hv*Dv
   float scale;
+  int32_t dense_len;            // tokens per request when cu_seqlens is null
+  int32_t gate_none;            // a, b are the effective alpha, beta (no activation)
 };
 
 struct ReplayArgs {
@@ -51,7 +53,7 @@ struct ChunkArgs {
   const float* b;
   const float* A_log;
   const float* dt_bias;
-  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens;    // null: dense layout, dense_len tokens per request
   const float* initial_state;
   float* final_state;
   void* output;
@@ -59,7 +61,17 @@ struct ChunkArgs {
   int32_t N, R, Hk, Hv, group;
   int32_t max_chunks;           // chunk slots the workspace holds
   float scale;
+  int32_t dense_len;            // tokens per request when cu_seqlens is null
+  int32_t gate_none;            // a, b are the effective alpha, beta (no activation)
 };
+
+// First token of request i (i = R: the end of the last request), clamped to
+// [0, N]; from cu_seqlens, or i * dense_len for the dense layout.
+template <typename Args>
+__host__ __device__ inline int seq_start(const Args& p, int i) {
+  const int64_t x = p.cu_seqlens != nullptr ? (int64_t)p.cu_seqlens[i] : (int64_t)i * p.dense_len;
+  return (int)(x < 0 ? 0 : x > p.N ? p.N : x);
+}
 
 constexpr int kChunk = 64;
 

@@ -87,8 +87,8 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   const int row_base = (blk * waves_per_block + wave) * RW;
 
   // segment of this request; clamped so a malformed device array cannot index out of range
-  const int t0 = min(max(p.cu_seqlens[r], 0), p.N);
-  const int t1 = min(max(p.cu_seqlens[r + 1], t0), p.N);
+  const int t0 = seq_start(p, r);
+  const int t1 = max(seq_start(p, r + 1), t0);
 
   const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
 
@@ -111,8 +111,9 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     }
   }
 
-  const float expA = expf(p.A_log[h]);
-  const float dtb = p.dt_bias[h];
+  const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
+  const float expA = gnone ? 0.f : expf(p.A_log[h]);
+  const float dtb = gnone ? 0.f : p.dt_bias[h];
   const IO* __restrict__ qp = static_cast<const IO*>(p.q);
   const IO* __restrict__ kp = static_cast<const IO*>(p.k);
   const IO* __restrict__ vp = static_cast<const IO*>(p.v);
@@ -157,8 +158,8 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     skq = group_sum<LPR>(skq);
     const float rk = rsqrtf(ssk + kNormEps);
     const float rq = rsqrtf(ssq + kNormEps) * p.scale;
-    const float alpha = decay_from_raw(at, expA, dtb);
-    const float beta = sigmoid_f(bt);
+    const float alpha = gate_alpha(at, gnone, expA, dtb);
+    const float beta = gate_beta(bt, gnone);
     const float kq = skq * rk * rq;               // k^ . q^
 #pragma unroll
     for (int e = 0; e < E; ++e) kv[e] *= rk;      // k^
@@ -270,8 +271,8 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   const int block_rows = waves_per_block * RW;
   const int row_base = block_row0 + wave * RW;
 
-  const int t0 = min(max(p.cu_seqlens[r], 0), p.N);
-  const int t1 = min(max(p.cu_seqlens[r + 1], t0), p.N);
+  const int t0 = seq_start(p, r);
+  const int t1 = max(seq_start(p, r + 1), t0);
   const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
 
   // ---- state rows into registers (issued before any staging)
@@ -293,8 +294,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
     }
   }
 
-  const float expA = expf(p.A_log[h]);
-  const float dtb = p.dt_bias[h];
+  const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
+  const float expA = gnone ? 0.f : expf(p.A_log[h]);
+  const float dtb = gnone ? 0.f : p.dt_bias[h];
   const IO* __restrict__ qp = static_cast<const IO*>(p.q);
   const IO* __restrict__ kp = static_cast<const IO*>(p.k);
   const IO* __restrict__ vp = static_cast<const IO*>(p.v);
@@ -342,8 +344,8 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
           sm.qh[j][part * EPT + e] = qv[e] * rq;
         }
         if (part == 0) {
-          sm.alpha[j] = decay_from_raw(p.a[(size_t)t * p.Hv + h], expA, dtb);
-          sm.beta[j] = sigmoid_f(p.b[(size_t)t * p.Hv + h]);
+          sm.alpha[j] = gate_alpha(p.a[(size_t)t * p.Hv + h], gnone, expA, dtb);
+          sm.beta[j] = gate_beta(p.b[(size_t)t * p.Hv + h], gnone);
           sm.kq[j] = skq * rk * rq;
         }
       }   // a token's 16 lanes are one aligned DPP row group: active or idle together

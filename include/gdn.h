@@ -53,8 +53,9 @@
 extern "C" {
 #endif
 
-/* Version of this ABI: structs, entry points and the capsule layout. */
-#define GDN_ABI_VERSION 1
+/* Version of this ABI: structs, entry points and the capsule layout.
+ * 2: gdn_params.gate_activation; cu_seqlens may be NULL (dense rank-4 layout). */
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -83,6 +84,18 @@ typedef enum gdn_plan { GDN_PLAN_AUTO = 0, GDN_PLAN_RECURRENT = 1, GDN_PLAN_CHUN
  * first page, Dependency). */
 typedef enum gdn_rule { GDN_RULE_GATED_DELTA = 0 } gdn_rule;
 
+/* What a and b hold.
+ *  GDN_GATE_RAW:  the raw gate inputs; the operator forms
+ *                 alpha = exp(-exp(A_log) softplus(a + dt_bias)) and beta = sigmoid(b)
+ *                 ("[CUDA] Add compact GatedDeltaNet operator", Description: gate
+ *                 normalization fused from raw A_log).
+ *  GDN_GATE_NONE: precomputed effective gates, activation none: alpha = a and
+ *                 beta = b, in FP32 ("Add GatedDeltaNet evaluation export for Qwen
+ *                 hybrid models", What changed). alpha is taken clamped to [0, 1],
+ *                 the range of the raw form. A_log and dt_bias are not read and may
+ *                 be NULL. */
+typedef enum gdn_gate_activation { GDN_GATE_RAW = 0, GDN_GATE_NONE = 1 } gdn_gate_activation;
+
 typedef struct gdn_params {
   int32_t num_tokens;            /* N: packed tokens over all requests, >= 0      */
   int32_t num_reqs;              /* R: requests (state batch), >= 0               */
@@ -97,6 +110,7 @@ typedef struct gdn_params {
   int32_t state_update_capacity; /* capsule rows per request; 0: no capsule        */
   int32_t plan;                  /* gdn_plan                                       */
   int32_t update_rule;           /* gdn_rule; must be GDN_RULE_GATED_DELTA         */
+  int32_t gate_activation;       /* gdn_gate_activation of a and b                 */
 } gdn_params;
 
 /* Tensors of one forward call. Layouts are dense row-major with the last
@@ -105,14 +119,23 @@ typedef struct gdn_tensors {
   const void* q;                 /* device, io  [N, Hk, Dk]                        */
   const void* k;                 /* device, io  [N, Hk, Dk]                        */
   const void* v;                 /* device, io  [N, Hv, Dv]                        */
-  const float* a;                /* device, f32 [N, Hv]  raw decay input           */
-  const float* b;                /* device, f32 [N, Hv]  raw beta input            */
-  const float* A_log;            /* device, f32 [Hv]                               */
-  const float* dt_bias;          /* device, f32 [Hv]  one scalar per value head    */
+  const float* a;                /* device, f32 [N, Hv]  decay input (see
+                                    gdn_gate_activation)                           */
+  const float* b;                /* device, f32 [N, Hv]  beta input                */
+  const float* A_log;            /* device, f32 [Hv]; may be NULL with GDN_GATE_NONE */
+  const float* dt_bias;          /* device, f32 [Hv]  one scalar per value head;
+                                    may be NULL with GDN_GATE_NONE                 */
   const int32_t* cu_seqlens;     /* device, i32 [R + 1]: 0 = cu[0] <= ... <= cu[R] = N;
-                                    request r owns tokens cu[r] .. cu[r+1]-1       */
+                                    request r owns tokens cu[r] .. cu[r+1]-1.
+                                    NULL selects the dense rank-4 layout ("ragged
+                                    and rank-4 inputs", third page, Description):
+                                    every request holds S = N / R tokens (N must be
+                                    a multiple of R), i.e. q is [R, S, Hk, Dk] and
+                                    v, output [R, S, Hv, Dv] - the same bytes as
+                                    the packed layout with equal lengths.          */
   const int32_t* cu_seqlens_host;/* host mirror of cu_seqlens, or NULL. When given
-                                    it is validated and used for planning.         */
+                                    it is validated and used for planning. Must be
+                                    NULL when cu_seqlens is NULL.                  */
   const float* initial_state;    /* device, f32 [R, Hv, Dv, Dk], or NULL for zeros */
   float* final_state;            /* device, f32 [R, Hv, Dv, Dk], or NULL (not
                                     written). May equal initial_state exactly

@@ -62,15 +62,32 @@ def log_decay(a, A_log, dt_bias):
     return -np.exp(np.asarray(A_log, np.float64)) * softplus(a + np.asarray(dt_bias, np.float64))
 
 
-def gates(a, b, A_log, dt_bias):
-    """(alpha, beta) from the raw gate inputs, both float64 [..., Hv].
+def gates(a, b, A_log, dt_bias, activation="raw"):
+    """(alpha, beta), both float64 [..., Hv].
 
-    Fused native gate arithmetic from raw A_log and per-head dt_bias
+    "raw": fused native gate arithmetic from raw A_log and per-head dt_bias
     ("[CUDA] Add compact GatedDeltaNet operator", Description).
+    "none": precomputed effective gates passed with activation none ("Add
+    GatedDeltaNet evaluation export for Qwen hybrid models", What changed):
+    alpha = a, beta = b. alpha is clamped to [0, 1], the range of the raw form
+    (a reading: the pages only say the gates arrive precomputed).
     """
+    if activation == "none":
+        return (np.clip(np.asarray(a, np.float64), 0.0, 1.0), np.array(b, np.float64, copy=True))
+    if activation != "raw":
+        raise ValueError(f"gate activation {activation!r}")
     alpha = np.exp(log_decay(a, A_log, dt_bias))
     beta = 1.0 / (1.0 + np.exp(-np.asarray(b, dtype=np.float64)))
     return alpha, beta
+
+
+def dense_cu_seqlens(num_tokens: int, num_reqs: int) -> np.ndarray:
+    """Sequence offsets of the dense rank-4 layout [R, S, ...]: R requests of
+    S = N / R tokens each ("[CUDA] Add compact GatedDeltaNet operator",
+    Description: ragged and rank-4 inputs)."""
+    if num_reqs <= 0 or num_tokens % num_reqs:
+        raise ValueError("the dense layout needs N divisible by R")
+    return np.arange(num_reqs + 1, dtype=np.int64) * (num_tokens // num_reqs)
 
 
 def l2normalize(x, eps=L2NORM_EPS):
@@ -145,13 +162,15 @@ def recurrence(qh, kh, v, alpha, beta, S0):
 
 def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
                 scale=None, state_update_capacity=0, capture_count=None,
-                state_update_init=None):
+                state_update_init=None, gate_activation="raw", num_reqs=None):
     """Packed ragged forward by the token recurrence.
 
     Inputs as the operator takes them (q, k [N, Hk, Dk]; v [N, Hv, Dv]; a, b
-    [N, Hv]; A_log, dt_bias [Hv]; cu_seqlens [R + 1]; initial_state
-    [R, Hv, Dv, Dk] or None for zeros). Returns (output [N, Hv, Dv],
-    final_state [R, Hv, Dv, Dk], state_update [R, capacity, W] or None).
+    [N, Hv]; A_log, dt_bias [Hv]; cu_seqlens [R + 1], or None with num_reqs for
+    the dense layout; initial_state [R, Hv, Dv, Dk] or None for zeros). a and b
+    are raw gate inputs or, with gate_activation "none", alpha and beta.
+    Returns (output [N, Hv, Dv], final_state [R, Hv, Dv, Dk], state_update
+    [R, capacity, W] or None).
 
     With a capacity, request r captures its leading
     n_r = min(len_r, capture_count[r] if given else capacity) tokens; capsule
@@ -160,11 +179,12 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    cu = np.asarray(cu_seqlens, np.int64)
+    cu = (dense_cu_seqlens(q.shape[0], num_reqs) if cu_seqlens is None
+          else np.asarray(cu_seqlens, np.int64))
     N, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     R = cu.shape[0] - 1
-    alpha, beta = gates(a, b, A_log, dt_bias)
+    alpha, beta = gates(a, b, A_log, dt_bias, gate_activation)
     out = np.zeros((N, Hv, Dv))
     final = np.zeros((R, Hv, Dv, Dk))
     cap = int(state_update_capacity)

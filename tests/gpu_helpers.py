@@ -47,9 +47,14 @@ def device_inputs(inp, torch):
 
 def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0,
                 capture_count=None, poison=None, plan=None, host_cu=True, workspace=True,
-                scale=0.0):
-    """One gdn_forward call on fresh device copies; returns numpy results."""
+                scale=0.0, gate="raw", dense=False):
+    """One gdn_forward call on fresh device copies; returns numpy results.
+
+    gate "none": a, b are passed as effective gates without A_log, dt_bias.
+    dense: no cu_seqlens (every request holds N / R tokens)."""
     d = device_inputs(inp, torch)
+    if gate == "none":
+        d["A_log"] = d["dt_bias"] = None
     N, Hv, Dv = inp["v"].shape
     R = len(inp["cu_seqlens"]) - 1
     Hk, Dk = inp["Hk"], inp["Dk"]
@@ -70,7 +75,7 @@ def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0
                         dtype=torch.float32, device="cuda")
     cc = dev(capture_count, torch) if capture_count is not None else None
     plan_code = gdn.PLAN_AUTO if plan is None else plan
-    cu_host = inp["cu_seqlens"] if host_cu else None
+    cu_host = inp["cu_seqlens"] if host_cu and not dense else None
     ws = None
     if workspace:
         nbytes = gdn.gdn_forward_workspace_bytes(N, R, Hk, Hv, Dk, Dv,
@@ -80,9 +85,11 @@ def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0
         if nbytes:
             ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     gdn.gdn_forward(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                    d["cu_seqlens"], out, initial_state=init, final_state=fin, state_update=su,
-                    capture_count=cc, cu_seqlens_host=cu_host, state_update_capacity=capacity,
-                    plan=plan_code, workspace=ws, scale=scale)
+                    None if dense else d["cu_seqlens"], out, initial_state=init, final_state=fin,
+                    state_update=su, capture_count=cc, cu_seqlens_host=cu_host,
+                    state_update_capacity=capacity, plan=plan_code, workspace=ws, scale=scale,
+                    gate_activation=gdn.GATE_NONE if gate == "none" else gdn.GATE_RAW,
+                    num_reqs=R if dense else None)
     torch.cuda.synchronize()
     res = {"output": out.float().cpu().numpy(),
            "final_state": None if fin is None else fin.cpu().numpy(),
@@ -91,7 +98,7 @@ def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0
     return res
 
 
-def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=None):
+def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=None, gate="raw"):
     init = None
     if capacity > 0:
         W = O.capsule_width(inp["Hk"], inp["Hv"], inp["Dk"], inp["Dv"])
@@ -100,7 +107,8 @@ def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=No
     return O.gdn_forward(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
                          inp["dt_bias"], inp["cu_seqlens"], inp["initial_state"],
                          scale=scale, state_update_capacity=capacity,
-                         capture_count=capture_count, state_update_init=init)
+                         capture_count=capture_count, state_update_init=init,
+                         gate_activation=gate)
 
 
 def sample_heads_inputs(inp, heads):
@@ -137,3 +145,20 @@ def assert_parity(io_dtype, out, ref_out, fin=None, ref_fin=None, what=""):
         if fin is not None:
             e_s = rel_l2(fin, ref_fin)
             assert e_s <= TOL_F16_STATE_RL2, f"{what} final-state rel-L2 {e_s:.3e}"
+
+
+def effective_gate_inputs(inp, seed):
+    """The inputs with a, b replaced by effective gates (activation none): alpha
+    mostly in [0.5, 1), with exact 1s, exact 0s (a state reset) and values past
+    either end of [0, 1] (clamped by the operator and the oracle alike), and
+    beta in [0, 1)."""
+    rng = np.random.default_rng(seed)
+    e = dict(inp)
+    alpha = rng.uniform(0.5, 1.0, inp["a"].shape)
+    alpha.flat[::7] = 1.0
+    alpha.flat[3::11] = 0.0
+    alpha.flat[5::13] = 1.3
+    alpha.flat[6::17] = -0.2
+    e["a"] = alpha.astype(np.float32)
+    e["b"] = rng.uniform(0.0, 1.0, inp["b"].shape).astype(np.float32)
+    return e

@@ -58,7 +58,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 2
     assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
     assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
     assert gdn.gdn_strerror(12345) == "unknown status"
@@ -104,6 +104,7 @@ def test_null_structs():
     ("io_dtype", gdn.GDN_BF16, gdn.GDN_ERR_DTYPE),
     ("io_dtype", 7, gdn.GDN_ERR_DTYPE),
     ("update_rule", 1, gdn.GDN_ERR_RULE),
+    ("gate_activation", 2, gdn.GDN_ERR_RULE),
     ("num_v_heads", 3, gdn.GDN_ERR_SHAPE),          # Hk = 2 does not divide 3
     ("head_k_dim", 48, gdn.GDN_ERR_SHAPE),
     ("head_v_dim", 256, gdn.GDN_ERR_SHAPE),
@@ -124,9 +125,28 @@ def test_param_validation(field, value, code):
 
 
 def test_missing_required_pointers():
-    for name in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens", "output"):
+    for name in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "output"):
         t, _ = _tensors(8, 2, 2, 4, 16, 16, **{name: None})
         assert _forward(_p(), t) == gdn.GDN_ERR_NULL, name
+
+
+def test_dense_layout_checks():
+    # no cu_seqlens: every request holds N / R tokens
+    t, _ = _tensors(7, 2, 2, 4, 16, 16, cu_seqlens=None)
+    assert _forward(_p(N=7), t) == gdn.GDN_ERR_SHAPE             # 7 tokens do not split into 2
+    t, _ = _tensors(8, 2, 2, 4, 16, 16, cu_seqlens=None)
+    host = np.asarray([0, 4, 8], np.int32)
+    t.cu_seqlens_host = host.ctypes.data
+    assert _forward(_p(), t) == gdn.GDN_ERR_SHAPE                # a mirror of a missing array
+
+
+def test_effective_gates_need_no_gate_parameters():
+    # raw gates need A_log and dt_bias; effective gates (activation none) do not:
+    # with them missing the call gets past the pointer checks to the next error
+    t, _ = _tensors(8, 2, 2, 4, 16, 16, A_log=None, dt_bias=None)
+    assert _forward(_p(), t) == gdn.GDN_ERR_NULL
+    t.initial_state = t.initial_state + 4
+    assert _forward(_p(gate_activation=gdn.GATE_NONE), t) == gdn.GDN_ERR_SHAPE
 
 
 def test_tokens_without_requests_is_a_shape_error():

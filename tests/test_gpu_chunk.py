@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 from gdn_workloads import cu_from_lengths, make_inputs, workload_inputs
-from gpu_helpers import (assert_parity, max_abs, oracle_forward, rel_l2, run_forward,
-                         sample_heads_inputs)
+from gpu_helpers import (assert_parity, effective_gate_inputs, max_abs, oracle_forward, rel_l2,
+                         run_forward, sample_heads_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,25 @@ def test_chunk_tile_width_invariance_bitwise(lengths):
         alone = run_forward(sub, torch, gdn, plan=gdn.PLAN_CHUNK)
         assert np.array_equal(alone["output"], packed["output"][cu[r]:cu[r + 1]])
         assert np.array_equal(alone["final_state"][0], packed["final_state"][r])
+
+
+def test_chunk_effective_gates_vs_oracle():
+    # effective gates with exact state resets (alpha = 0) inside chunks, and
+    # values past [0, 1] that both sides clamp
+    inp = effective_gate_inputs(make_inputs(RAGGED, 2, 4, 128, 128, "f16", seed=49), seed=50)
+    _case(f"chunk effective gates lengths={RAGGED}")
+    res = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK, gate="none")
+    ref_o, ref_s, _ = oracle_forward(inp, O, gate="none")
+    assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "chunk effective gates")
+
+
+def test_chunk_dense_layout_equals_packed_bitwise():
+    inp = make_inputs([130, 130, 130], 2, 4, 128, 128, "f16", seed=51)
+    _case("chunk dense layout")
+    packed = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK)
+    dense = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK, dense=True)
+    assert np.array_equal(dense["output"], packed["output"])
+    assert np.array_equal(dense["final_state"], packed["final_state"])
 
 
 def test_chunk_without_host_mirror_is_identical():

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 from gdn_workloads import cu_from_lengths, make_inputs, workload_inputs
-from gpu_helpers import (TOL_F32_REL, TOL_REPLAY_REL, assert_parity, dev, oracle_forward,
+from gpu_helpers import (TOL_F32_REL, TOL_REPLAY_REL, assert_parity, dev, effective_gate_inputs,
+                         oracle_forward,
                          rel_max, run_forward)
 
 pytestmark = pytest.mark.gpu
@@ -183,6 +184,59 @@ def test_capsule_small_heads_vs_oracle(Dk, Dv, lengths):
     for r, L in enumerate(lengths):
         assert np.all(got[r, L:] == -7.0)
         assert rel_max(got[r, :L], ref_cap[r, :L]) <= TOL_F32_REL
+
+
+# ------------------------------------------------ gate and layout variants
+@pytest.mark.parametrize("io", ["f32", "f16"])
+def test_effective_gates_vs_oracle(io):
+    inp = effective_gate_inputs(make_inputs([9, 1, 0, 17], 2, 4, 64, 32, io, seed=17), seed=18)
+    _case(f"effective gates {io}")
+    res = run_forward(inp, torch, gdn, gate="none", plan=gdn.PLAN_RECURRENT)
+    ref_o, ref_s, _ = oracle_forward(inp, O, gate="none")
+    assert_parity(io, res["output"], ref_o, res["final_state"], ref_s, f"effective gates {io}")
+
+
+def test_effective_gates_capsule():
+    cap = 4
+    inp = effective_gate_inputs(make_inputs([4, 3, 6], 2, 4, 128, 128, "f16", seed=19, capacity=cap),
+                                seed=20)
+    _case("effective gates capsule")
+    res = run_forward(inp, torch, gdn, gate="none", capacity=cap, poison=-7.0)
+    ref_o, ref_s, ref_cap = oracle_forward(inp, O, gate="none", capacity=cap, poison=-7.0)
+    assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "effective gates capsule")
+    sa, sk, sd = O.capsule_sections(inp["Hk"], inp["Hv"], inp["Dk"], inp["Dv"])
+    got = res["state_update"]
+    assert np.array_equal(got[..., sa], ref_cap[..., sa].astype(np.float32))   # clamped alpha, exact
+    assert rel_max(got[..., sd], ref_cap[..., sd]) <= 1e-3
+
+
+@pytest.mark.parametrize("io,capacity", [("f32", 0), ("f16", 0), ("f16", 4)])
+def test_dense_layout_equals_packed_bitwise(io, capacity):
+    inp = make_inputs([5, 5, 5], 2, 4, 128, 64, io, seed=21, capacity=capacity)
+    _case(f"dense layout {io} capacity={capacity}")
+    packed = run_forward(inp, torch, gdn, capacity=capacity, poison=-7.0)
+    dense = run_forward(inp, torch, gdn, capacity=capacity, poison=-7.0, dense=True)
+    for key in ("output", "final_state") + (("state_update",) if capacity else ()):
+        assert np.array_equal(dense[key], packed[key]), key
+
+
+def test_dense_rank4_tensors_through_the_binding():
+    # [R, S, H, D] tensors straight into the binding (no cu_seqlens)
+    R, S, Hk, Hv, D = 3, 6, 2, 4, 32
+    inp = make_inputs([S] * R, Hk, Hv, D, D, "f32", seed=22)
+    _case("dense rank-4 binding")
+    d = {n: dev(inp[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    q4, k4 = d["q"].reshape(R, S, Hk, D), d["k"].reshape(R, S, Hk, D)
+    v4 = d["v"].reshape(R, S, Hv, D)
+    out4 = torch.empty_like(v4)
+    fin = torch.empty((R, Hv, D, D), dtype=torch.float32, device="cuda")
+    init = dev(inp["initial_state"], torch)
+    gdn.gdn_forward(q4, k4, v4, d["a"].reshape(R, S, Hv), d["b"].reshape(R, S, Hv), d["A_log"],
+                    d["dt_bias"], None, out4, initial_state=init, final_state=fin)
+    torch.cuda.synchronize()
+    ref_o, ref_s, _ = oracle_forward(inp, O)
+    assert_parity("f32", out4.reshape(R * S, Hv, D).cpu().numpy(), ref_o, fin.cpu().numpy(), ref_s,
+                  "dense rank-4")
 
 
 def test_capture_count_clamped_to_capacity():

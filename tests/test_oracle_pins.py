@@ -398,3 +398,83 @@ ALL_CHECKS = [
     check_chunked_equals_recurrent, check_capsule_layout, check_replay_prefix,
     check_packing_invariance, check_gqa,
 ]
+
+
+# ------------------------------------------- effective gates (activation none)
+def _effective(inp, alpha, beta):
+    """The inputs with a, b replaced by effective gates; A_log, dt_bias unused."""
+    e = dict(inp)
+    e["a"] = np.asarray(alpha, np.float32)
+    e["b"] = np.asarray(beta, np.float32)
+    e["A_log"] = e["dt_bias"] = None
+    return e
+
+
+def test_effective_gates_frozen_state():
+    # alpha = 1, beta = 0 passed as effective gates: the state stays frozen and
+    # o_t = S0 q^_t with q^ = q / |q| * Dk^-1/2 written out here
+    inp = _tiny([5, 3], Hk=1, Hv=2, Dk=6, Dv=4)
+    e = _effective(inp, np.ones_like(inp["a"]), np.zeros_like(inp["b"]))
+    out, fin, _ = _forward(e, gate_activation="none")
+    assert np.array_equal(fin, inp["initial_state"].astype(np.float64))
+    q = inp["q"].astype(np.float64)
+    qh = q / np.sqrt((q * q).sum(-1, keepdims=True) + 1e-6) / np.sqrt(6)
+    cu = inp["cu_seqlens"]
+    for r in range(2):
+        for t in range(cu[r], cu[r + 1]):
+            for h in range(2):
+                want = inp["initial_state"][r, h].astype(np.float64) @ qh[t, 0]
+                assert np.allclose(out[t, h], want, rtol=0, atol=1e-12)
+
+
+def test_effective_gates_decay_only():
+    # beta = 0: S_T = prod_t alpha_t * S0 for the given alpha
+    inp = _tiny([7], Hk=1, Hv=2, Dk=5, Dv=4)
+    rng = np.random.default_rng(5)
+    alpha = rng.uniform(0.2, 1.0, inp["a"].shape)
+    e = _effective(inp, alpha, np.zeros_like(inp["b"]))
+    _, fin, _ = _forward(e, gate_activation="none")
+    gamma = np.prod(e["a"].astype(np.float64), axis=0)
+    assert _rel(fin[0], gamma[:, None, None] * inp["initial_state"][0]) < TIGHT
+
+
+def test_effective_gates_exact_write():
+    # alpha = 1, beta = 1, orthonormal keys through the whole forward: S_n k_i = v_i
+    rng = np.random.default_rng(6)
+    Dk, Dv, n = 8, 5, 5
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    inp = _tiny([n], Hk=1, Hv=1, Dk=Dk, Dv=Dv)
+    inp["k"] = Qm[:, :n].T[:, None, :].astype(np.float64)
+    e = _effective(inp, np.ones_like(inp["a"]), np.ones_like(inp["b"]))
+    _, fin, _ = _forward(e, gate_activation="none")
+    # exact up to the norm epsilon: |k^|^2 = 1 / (1 + 1e-6)
+    for i in range(n):
+        assert np.allclose(fin[0, 0] @ Qm[:, i], inp["v"][i, 0], rtol=0, atol=1e-5)
+
+
+def test_effective_decay_is_clamped():
+    # a decay above 1 acts as 1; one below 0 acts as 0, which resets the state:
+    # after it S = beta v k^^T whatever S0 was
+    inp = _tiny([1], Hk=1, Hv=1, Dk=4, Dv=3)
+    beta = np.full_like(inp["b"], 0.5)
+    over = _forward(_effective(inp, np.full_like(inp["a"], 1.7), beta), gate_activation="none")
+    one = _forward(_effective(inp, np.ones_like(inp["a"]), beta), gate_activation="none")
+    assert np.array_equal(over[1], one[1])
+    _, fin, _ = _forward(_effective(inp, np.full_like(inp["a"], -0.3), beta), gate_activation="none")
+    k = inp["k"][0, 0].astype(np.float64)
+    kh = k / np.sqrt(k @ k + 1e-6)
+    want = 0.5 * np.outer(inp["v"][0, 0].astype(np.float64), kh)
+    assert np.allclose(fin[0, 0], want, rtol=0, atol=1e-12)
+
+
+def test_dense_layout_is_uniform_packing():
+    # the rank-4 layout [R, S, H, D] is the packed layout with offsets 0, S, 2S, ...
+    inp = _tiny([4, 4, 4], Hk=1, Hv=2, Dk=4, Dv=3)
+    assert np.array_equal(O.dense_cu_seqlens(12, 3), [0, 4, 8, 12])
+    packed = _forward(inp)
+    dense = O.gdn_forward(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
+                          inp["dt_bias"], None, inp["initial_state"], num_reqs=3)
+    for x, y in zip(packed[:2], dense[:2]):
+        assert np.array_equal(x, y)
+    with pytest.raises(ValueError):
+        O.dense_cu_seqlens(10, 3)
