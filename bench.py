@@ -15,8 +15,10 @@ stream, against the 8 TB/s HBM peak) and the float64 oracle timed on this
 host's cores on a bounded sample of the same workload. The line also carries,
 under "workloads", the same measurements for the operator's other workloads:
 speculative verify + replay (HBM roofline), the ragged and long prefills
-(fp16 MFMA roofline) and the decode step with precomputed effective gates in the
-dense rank-4 layout; --workload NAME times just one of them.
+(fp16 MFMA roofline), the decode step with precomputed effective gates in the
+dense rank-4 layout, and the compact causal convolution upstream of the operator
+on a prefill and a decode batch (HBM roofline); --workload NAME times just one
+of them.
 """
 from __future__ import annotations
 
@@ -289,6 +291,94 @@ def run_prefill(args, torch, gdn, name):
                          "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
+# ------------------------------------------------------- causal convolution
+def conv_bytes(N, R, C, K, io, capture_rows=0) -> int:
+    """Algorithmic HBM bytes of one convolution call: x read and output written
+    once, the carried state read and the final state written once, the filter,
+    bias and cu_seqlens read once, and the captured rows written."""
+    return (2 * N * C * io + 2 * R * C * (K - 1) * 4 + C * K * 4 + C * 4 + (R + 1) * 4
+            + capture_rows * C * 4)
+
+
+def _time_graph(torch, step, steps, warmup, per_graph):
+    """Average ms per step of `step(i)` when `per_graph` consecutive steps are
+    replayed as one HIP graph (a call too short to time launch by launch)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            step(i)
+    replays = max(1, -(-steps // per_graph))
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (replays * per_graph), replays * per_graph
+
+
+def run_conv(args, torch, gdn, name):
+    """The compact causal convolution upstream of the operator, C = 2 Hk Dk + Hv Dv
+    = 8192 channels (Hk=16, Hv=32, D=128), K = 4, fp16 I/O, SiLU. conv_prefill: the
+    ragged prefill lengths, final state to its own buffer; conv_decode: 64 requests x
+    1 token, state updated in place over rotating banks, steps replayed as a HIP graph."""
+    from gdn_workloads.conv import conv_channels, make_conv_inputs
+    C, K = conv_channels(16, 32, 128, 128), 4
+    if name == "conv_prefill":
+        inp = make_conv_inputs(None, C, K, "f16", seed=3, num_drawn=8, max_drawn=4096)
+    else:
+        inp = make_conv_inputs([1] * 64, C, K, "f16", seed=1)
+    N, R = inp["x"].shape[0], len(inp["lengths"])
+    x, w, bias, cu = (_dev(inp[n], torch) for n in ("x", "weight", "bias", "cu_seqlens"))
+    out = torch.empty_like(x)
+    host_cu = inp["cu_seqlens"]
+    state_bytes = R * C * (K - 1) * 4
+    nbytes = conv_bytes(N, R, C, K, 2)
+    if name == "conv_prefill":
+        init = _dev(inp["initial_state"], torch)
+        fin = torch.empty_like(init)
+
+        def step(i):
+            gdn.gdn_conv_forward(x, w, bias, cu, out, initial_state=init, final_state=fin,
+                                 cu_seqlens_host=host_cu)
+
+        _log(f"{name}: N={N} R={R} C={C} K={K}")
+        ms = _time_steps(torch, step, max(20, args.steps // 5), max(5, args.warmup // 5))
+        timing = "HIP events around consecutive calls"
+        banks = 1
+    else:
+        banks = max(2, -(-BANK_TARGET_BYTES // state_bytes))
+        states = [_dev(inp["initial_state"], torch) for _ in range(banks)]
+
+        def step(i):
+            s = states[i % banks]
+            gdn.gdn_conv_forward(x, w, bias, cu, out, initial_state=s, final_state=s,
+                                 cu_seqlens_host=host_cu)
+
+        _log(f"{name}: R={R} C={C} K={K} banks={banks} (graph of {banks} steps)")
+        ms, n = _time_graph(torch, step, args.steps, args.warmup, banks)
+        timing = f"HIP events around graph replays, {n} steps"
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"tokens": N, "requests": R, "channels": C, "kernel_size": K,
+                       "io_dtype": "f16", "activation": "silu", "state_banks": banks,
+                       "timing": timing},
+            "roofline": {"bound": "hbm", "kernel": "gdn_conv_forward", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_step": nbytes}}
+
+
 def run_hbm_copy(args, torch):
     """Reference stream: device-to-device copies of 128 MiB fp32 buffers rotated over
     banks (read 128 MiB + write 128 MiB per step). Its known byte count calibrates
@@ -337,7 +427,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="all",
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
-                             "decode_effective_dense", "hbm_copy"],
+                             "decode_effective_dense", "conv_prefill", "conv_decode", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="length of the oracle CPU-baseline sample (0 skips it)")
@@ -359,6 +449,8 @@ def main():
               "ragged_prefill": lambda: run_prefill(args, torch, gdn, "ragged_prefill"),
               "long_prefill": lambda: run_prefill(args, torch, gdn, "long_prefill"),
               "decode_effective_dense": lambda: run_decode_effective_dense(args, torch, gdn),
+              "conv_prefill": lambda: run_conv(args, torch, gdn, "conv_prefill"),
+              "conv_decode": lambda: run_conv(args, torch, gdn, "conv_decode"),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
         print(json.dumps({"metric": METRIC, "workload": args.workload, **res}), flush=True)
@@ -370,6 +462,8 @@ def main():
             "ragged_prefill": run_prefill(args, torch, gdn, "ragged_prefill"),
             "long_prefill": run_prefill(args, torch, gdn, "long_prefill"),
             "decode_effective_dense": run_decode_effective_dense(args, torch, gdn),
+            "conv_prefill": run_conv(args, torch, gdn, "conv_prefill"),
+            "conv_decode": run_conv(args, torch, gdn, "conv_decode"),
         }
     if args.cpu_seconds > 0:
         _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")

@@ -13,4 +13,5 @@ from .binding import (  # noqa: F401
     GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP, GdnParams, GdnTensors,
     lib, library_path, gdn_abi_version, gdn_strerror, gdn_forward, gdn_forward_workspace_bytes,
     gdn_resolve_plan, gdn_replay, capsule_width, make_params,
+    CONV_SILU, CONV_NONE, GdnConvParams, GdnConvTensors, gdn_conv_forward, gdn_conv_replay,
 )

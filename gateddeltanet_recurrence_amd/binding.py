@@ -1,4 +1,5 @@
-"""ctypes binding of the C ABI in include/gdn.h (same entry-point names).
+"""ctypes binding of the C ABI in include/gdn.h and include/gdn_conv.h (same
+entry-point names).
 
 Tensors are torch tensors on the current HIP device; torch only provides the
 device memory and the stream. Shapes are read from the tensors, checked for
@@ -20,6 +21,7 @@ PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA = 0
 GATE_RAW, GATE_NONE = 0, 1
 ABI_VERSION = 2          # the struct layouts below match this version of include/gdn.h
+CONV_SILU, CONV_NONE = 0, 1
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -47,6 +49,18 @@ class GdnTensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens", "cu_seqlens_host",
         "initial_state", "final_state", "output", "state_update", "capture_count")]
+
+
+class GdnConvParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "num_reqs", "channels", "kernel_size", "io_dtype", "activation",
+        "state_update_capacity")]
+
+
+class GdnConvTensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "weight", "bias", "cu_seqlens", "cu_seqlens_host", "initial_state", "final_state",
+        "output", "state_update", "capture_count")]
 
 
 _lib = None
@@ -77,6 +91,11 @@ def lib() -> ctypes.CDLL:
         L.gdn_resolve_plan.restype = ctypes.c_int
         L.gdn_replay.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.gdn_replay.restype = ctypes.c_int
+        L.gdn_conv_forward.argtypes = [ctypes.POINTER(GdnConvParams),
+                                       ctypes.POINTER(GdnConvTensors), vp]
+        L.gdn_conv_forward.restype = ctypes.c_int
+        L.gdn_conv_replay.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.gdn_conv_replay.restype = ctypes.c_int
         L.gdn_strerror.argtypes = [ctypes.c_int]
         L.gdn_strerror.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -279,4 +298,76 @@ def gdn_replay(src_state, state_update, accepted, dst_state, *, num_k_heads: int
     del host_acc
     if check and st != GDN_OK:
         raise GDNError(st, "gdn_replay")
+    return st
+
+
+def gdn_conv_forward(x, weight, bias, cu_seqlens, output, *, initial_state=None,
+                     final_state=None, state_update=None, capture_count=None,
+                     cu_seqlens_host=None, activation: int = CONV_SILU,
+                     state_update_capacity: int = 0, num_reqs: Optional[int] = None,
+                     stream=None, check: bool = True) -> int:
+    """gdn_conv_forward of include/gdn_conv.h on torch tensors; returns the status.
+
+    x and output [N, C] float16 or float32 (dense layout, cu_seqlens None:
+    [R, S, C] or [N, C] with num_reqs); weight [C, K] and bias [C] float32;
+    cu_seqlens [R + 1] int32; states [R, C, K - 1] float32; state_update
+    [R, capacity, C] float32; capture_count [R] int32.
+    """
+    torch = _torch()
+    if cu_seqlens is None and x.dim() == 3:
+        if num_reqs is None:
+            num_reqs = x.shape[0]
+        x, output = x.reshape(-1, x.shape[2]), output.reshape(-1, output.shape[2])
+    N, C = x.shape
+    K = weight.shape[1]
+    if cu_seqlens is None:
+        if num_reqs is None:
+            raise ValueError("the dense layout (cu_seqlens None) needs num_reqs or [R, S, C] inputs")
+        R = int(num_reqs)
+    else:
+        R = cu_seqlens.shape[0] - 1
+    io = x.dtype
+    _need(x, "x", (N, C))
+    _need(output, "output", (N, C), io)
+    _need(weight, "weight", (C, K), torch.float32)
+    _need(bias, "bias", (C,), torch.float32)
+    _need(cu_seqlens, "cu_seqlens", (R + 1,), torch.int32)
+    _need(initial_state, "initial_state", (R, C, K - 1), torch.float32)
+    _need(final_state, "final_state", (R, C, K - 1), torch.float32)
+    if state_update is not None:
+        _need(state_update, "state_update", (R, state_update_capacity, C), torch.float32)
+    _need(capture_count, "capture_count", (R,), torch.int32)
+    host_cu, host_cu_ptr = _host_i32(cu_seqlens_host)
+    if host_cu is not None and host_cu.shape != (R + 1,):
+        raise ValueError("cu_seqlens_host must have R + 1 entries")
+    params = GdnConvParams(N, R, C, K, _io_code(io), int(activation), int(state_update_capacity))
+    tens = GdnConvTensors(_ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), host_cu_ptr,
+                          _ptr(initial_state), _ptr(final_state), _ptr(output),
+                          _ptr(state_update), _ptr(capture_count))
+    st = lib().gdn_conv_forward(ctypes.byref(params), ctypes.byref(tens), _stream_handle(stream))
+    del host_cu
+    if check and st != GDN_OK:
+        raise GDNError(st, "gdn_conv_forward")
+    return st
+
+
+def gdn_conv_replay(src_state, state_update, accepted, dst_state, *, state_update_capacity: int,
+                    accepted_host=None, stream=None, check: bool = True) -> int:
+    """gdn_conv_replay of include/gdn_conv.h: dst = the last K - 1 of [src, accepted inputs]."""
+    torch = _torch()
+    R, C, Km1 = src_state.shape
+    cap = int(state_update_capacity)
+    _need(src_state, "src_state", (R, C, Km1), torch.float32)
+    _need(dst_state, "dst_state", (R, C, Km1), torch.float32)
+    _need(accepted, "accepted", (R,), torch.int32)
+    if cap > 0:
+        _need(state_update, "state_update", (R, cap, C), torch.float32)
+    host_acc, host_ptr = _host_i32(accepted_host)
+    if host_acc is not None and host_acc.shape != (R,):
+        raise ValueError("accepted_host must have R entries")
+    st = lib().gdn_conv_replay(R, C, Km1 + 1, cap, _ptr(src_state), _ptr(state_update),
+                               _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
+    del host_acc
+    if check and st != GDN_OK:
+        raise GDNError(st, "gdn_conv_replay")
     return st

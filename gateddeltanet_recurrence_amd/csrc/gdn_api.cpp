@@ -5,6 +5,7 @@
 // before the publication boundary: "Replay compact fixed state for hybrid
 // decoding", Key Changes). The library allocates nothing and keeps no state.
 #include "../../include/gdn.h"
+#include "../../include/gdn_conv.h"
 
 #include <hip/hip_runtime.h>
 
@@ -112,6 +113,16 @@ int resolve_plan(const gdn_params* p, const int32_t* cu_host, bool capsule, Reso
   rv->plan = plan;
   rv->chunk_slots = slots;
   return GDN_OK;
+}
+
+bool conv_shape_ok(int64_t C, int64_t K) { return C >= 4 && C % 4 == 0 && K >= 2 && K <= 8; }
+
+// Tokens one convolution workgroup walks: enough workgroups to fill the chip
+// several times over, and at most 64 tokens so the K - 1 re-read inputs at each
+// workgroup's start stay a small fraction of the traffic.
+int conv_tokens_per_block(int64_t N, int64_t C) {
+  const int64_t tb = (N * gdn::conv_channel_groups(C) + 8191) / 8192;
+  return (int)(tb < 1 ? 1 : tb > 64 ? 64 : tb);
 }
 
 size_t workspace_for(const Resolved& rv) {
@@ -277,6 +288,122 @@ int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_
   a.R = R; a.Hk = Hk; a.Hv = Hv; a.Dk = Dk; a.Dv = Dv; a.group = Hv / Hk;
   a.capacity = capacity; a.capsule_width = (int32_t)W64;
   hipError_t err = gdn::launch_replay(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* stream) {
+  if (p == nullptr || t == nullptr) return GDN_ERR_NULL;
+  if (p->activation != GDN_CONV_SILU && p->activation != GDN_CONV_NONE) return GDN_ERR_RULE;
+  if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_F16) return GDN_ERR_DTYPE;
+  const int64_t N = p->num_tokens, R = p->num_reqs, C = p->channels, K = p->kernel_size;
+  if (N < 0 || R < 0 || !conv_shape_ok(C, K)) return GDN_ERR_SHAPE;
+  const int64_t cap = p->state_update_capacity;
+  if (cap < 0) return GDN_ERR_CAPACITY;
+  const bool capture = t->state_update != nullptr;
+  if (capture && cap == 0) return GDN_ERR_CAPACITY;
+  if (R == 0) return N == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  const bool dense = t->cu_seqlens == nullptr;
+  if (dense && (t->cu_seqlens_host != nullptr || N % R != 0)) return GDN_ERR_SHAPE;
+  if (N > 0 && (t->x == nullptr || t->weight == nullptr || t->output == nullptr)) return GDN_ERR_NULL;
+  const void* vec_ptrs[] = {t->x, t->weight, t->initial_state, t->final_state, t->output, t->state_update};
+  for (const void* ptr : vec_ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDN_ERR_SHAPE;
+  if (!dense && t->cu_seqlens_host != nullptr) {
+    int64_t max_len = 0, slots = 0;
+    const int st = check_cu_host(t->cu_seqlens_host, R, N, &max_len, &slots);
+    if (st != GDN_OK) return st;
+  }
+
+  const size_t io = io_bytes(p->io_dtype);
+  const size_t state_bytes = (size_t)(R * C * (K - 1)) * 4;
+  const Span inputs[] = {Span(t->x, (size_t)(N * C) * io), Span(t->weight, (size_t)(C * K) * 4),
+                         Span(t->bias, (size_t)C * 4), Span(t->cu_seqlens, (size_t)(R + 1) * 4),
+                         Span(t->capture_count, capture ? (size_t)R * 4 : 0)};
+  const Span init(t->initial_state, state_bytes);
+  const Span fin(t->final_state, state_bytes);
+  const Span out(t->output, (size_t)(N * C) * io);
+  const Span cap_rows(t->state_update, capture ? (size_t)(R * cap * C) * 4 : 0);
+  const Span outputs[] = {out, fin, cap_rows};
+  for (const Span& o : outputs)
+    for (const Span& i : inputs)
+      if (o.overlaps(i)) return GDN_ERR_ALIAS;
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (outputs[i].overlaps(outputs[j])) return GDN_ERR_ALIAS;
+  if (out.overlaps(init) || cap_rows.overlaps(init)) return GDN_ERR_ALIAS;
+  // final_state may be the very same buffer as initial_state (in-place update)
+  if (fin.overlaps(init) && t->final_state != t->initial_state) return GDN_ERR_ALIAS;
+
+  // packed requests of one common length, as the host mirror shows, are indexed
+  // like the dense layout (cu[r] = r L), which spares the kernel its search
+  int64_t uniform_len = dense ? (N / R) : -1;
+  if (!dense && t->cu_seqlens_host != nullptr && N > 0 && N % R == 0) {
+    uniform_len = N / R;
+    for (int64_t r = 0; r <= R && uniform_len >= 0; ++r)
+      if (t->cu_seqlens_host[r] != r * (N / R)) uniform_len = -1;
+  }
+
+  gdn::ConvArgs a{};
+  a.x = t->x; a.weight = t->weight; a.bias = t->bias;
+  a.cu_seqlens = uniform_len >= 0 ? nullptr : t->cu_seqlens;
+  a.initial_state = t->initial_state; a.final_state = t->final_state; a.output = t->output;
+  a.state_update = capture ? t->state_update : nullptr;
+  a.capture_count = capture ? t->capture_count : nullptr;
+  a.N = (int32_t)N; a.R = (int32_t)R; a.C = (int32_t)C; a.K = (int32_t)K;
+  a.dense_len = uniform_len >= 0 ? (int32_t)uniform_len : 0;
+  a.silu = p->activation == GDN_CONV_SILU ? 1 : 0;
+  a.capacity = (int32_t)cap;
+  a.tokens_per_block = conv_tokens_per_block(N, C);
+  // one-dimensional grids of (token blocks or requests) x channel groups
+  const int64_t groups = gdn::conv_channel_groups(C);
+  if (((N + a.tokens_per_block - 1) / a.tokens_per_block) * groups > std::numeric_limits<int32_t>::max() ||
+      R * groups > std::numeric_limits<int32_t>::max())
+    return GDN_ERR_SHAPE;
+  // the final-state kernel is launched unless the host can see that the forward
+  // kernel writes every request's final state
+  a.final_in_place = t->final_state != nullptr && t->final_state == t->initial_state;
+  const bool in_place = a.final_in_place != 0;
+  a.final_pending = 1;
+  if (uniform_len >= 0) {
+    bool all = true;
+    for (int64_t r = 0; r < R && all; ++r)
+      all = gdn::final_in_forward((int)(r * uniform_len), (int)((r + 1) * uniform_len), a.tokens_per_block,
+                                  in_place);
+    a.final_pending = all ? 0 : 1;
+  } else if (t->cu_seqlens_host != nullptr) {
+    bool all = true;
+    for (int64_t r = 0; r < R && all; ++r)
+      all = gdn::final_in_forward(t->cu_seqlens_host[r], t->cu_seqlens_host[r + 1], a.tokens_per_block,
+                                  in_place);
+    a.final_pending = all ? 0 : 1;
+  }
+  const hipError_t err = gdn::launch_conv(a, p->io_dtype, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_conv_replay(int32_t R, int32_t C, int32_t K, int32_t capacity, const float* src,
+                    const float* capture, const int32_t* accepted, const int32_t* accepted_host,
+                    float* dst, void* stream) {
+  if (R < 0 || !conv_shape_ok(C, K)) return GDN_ERR_SHAPE;
+  if (capacity < 0) return GDN_ERR_CAPACITY;
+  if (R == 0) return GDN_OK;
+  if (src == nullptr || dst == nullptr || accepted == nullptr) return GDN_ERR_NULL;
+  if (capacity > 0 && capture == nullptr) return GDN_ERR_NULL;
+  if ((int64_t)R * gdn::conv_channel_groups(C) > std::numeric_limits<int32_t>::max()) return GDN_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst) || (capture != nullptr && !aligned16(capture))) return GDN_ERR_SHAPE;
+  if (accepted_host != nullptr) {
+    for (int32_t r = 0; r < R; ++r)
+      if (accepted_host[r] < 0 || accepted_host[r] > capacity) return GDN_ERR_CAPACITY;
+  }
+  const size_t state_bytes = (size_t)R * C * (K - 1) * 4;
+  const Span d(dst, state_bytes);
+  if (d.overlaps(Span(src, state_bytes)) || d.overlaps(Span(capture, (size_t)R * capacity * C * 4)) ||
+      d.overlaps(Span(accepted, (size_t)R * 4)))
+    return GDN_ERR_ALIAS;
+  gdn::ConvReplayArgs a{};
+  a.src = src; a.capture = capture; a.accepted = accepted; a.dst = dst;
+  a.R = R; a.C = C; a.K = K; a.capacity = capacity;
+  const hipError_t err = gdn::launch_conv_replay(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -75,10 +75,57 @@ __host__ __device__ inline int seq_start(const Args& p, int i) {
 
 constexpr int kChunk = 64;
 
+// Compact causal convolution (depthwise conv1d + activation with K - 1 carried inputs).
+struct ConvArgs {
+  const void* x;
+  const float* weight;          // [C, K]
+  const float* bias;            // [C] or null
+  const int32_t* cu_seqlens;    // null: dense layout, dense_len tokens per request
+  const float* initial_state;   // [R, C, K - 1] or null
+  float* final_state;           // [R, C, K - 1] or null; may equal initial_state
+  void* output;
+  float* state_update;          // [R, capacity, C] or null
+  const int32_t* capture_count; // [R] or null
+  int32_t N, R, C, K;
+  int32_t dense_len;
+  int32_t silu;                 // 1: SiLU, 0: identity
+  int32_t capacity;
+  int32_t tokens_per_block;
+  int32_t final_in_place;       // final_state == initial_state
+  int32_t final_pending;        // 0: every request's final state is written by the forward kernel
+};
+
+// Convolution workgroups: 256 threads of 4 adjacent channels each.
+constexpr int kConvBlockThreads = 256;
+__host__ __device__ inline int64_t conv_channel_groups(int64_t C) {
+  return (C + 4 * kConvBlockThreads - 1) / (4 * kConvBlockThreads);
+}
+
+// Which kernel writes a request's final state. The workgroup that convolves the
+// request's last token holds the last K - 1 inputs and writes it, unless the
+// update is in place and other workgroups may still read the request's carried
+// inputs: then only a request whose tokens all fall in that one workgroup
+// (tokens_per_block tokens each) is written there. Empty requests, and the
+// in-place requests spanning workgroups, are left to the final-state kernel,
+// which runs after the forward kernel.
+__host__ __device__ inline bool final_in_forward(int start, int end, int tokens_per_block, bool in_place) {
+  return end > start && (!in_place || start / tokens_per_block == (end - 1) / tokens_per_block);
+}
+
+struct ConvReplayArgs {
+  const float* src;
+  const float* capture;
+  const int32_t* accepted;
+  float* dst;
+  int32_t R, C, K, capacity;
+};
+
 // io_dtype: 0 = f32, 1 = f16 (gdn_dtype values).
 hipError_t launch_recurrent(const RecurrentArgs& args, int io_dtype, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& args, hipStream_t stream);
 hipError_t launch_chunk(const ChunkArgs& args, int io_dtype, hipStream_t stream);
+hipError_t launch_conv(const ConvArgs& args, int io_dtype, hipStream_t stream);
+hipError_t launch_conv_replay(const ConvReplayArgs& args, hipStream_t stream);
 
 // Workspace bytes of the chunk path for `chunk_slots` chunks and these heads.
 size_t chunk_workspace_bytes(int64_t chunk_slots, int R, int Hk, int Hv);

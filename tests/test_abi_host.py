@@ -1,4 +1,4 @@
-"""Host-side checks of libgdn.so: it loads, exports what include/gdn.h declares,
+"""Host-side checks of libgdn.so: it loads, exports what include/*.h declare,
 and rejects bad arguments on the host before anything reaches the GPU.
 
 No call here launches a kernel: every forward/replay call is built to fail a
@@ -17,7 +17,8 @@ import pytest
 import gateddeltanet_recurrence_amd as gdn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 
@@ -39,15 +40,17 @@ pytestmark = [
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gdn_forward", "gdn_replay", "gdn_forward_workspace_bytes", "gdn_resolve_plan",
-              "gdn_strerror", "gdn_abi_version"):
+              "gdn_strerror", "gdn_abi_version", "gdn_conv_forward", "gdn_conv_replay"):
         assert n in names
 
 
