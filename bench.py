@@ -16,9 +16,10 @@ host's cores on a bounded sample of the same workload. The line also carries,
 under "workloads", the same measurements for the operator's other workloads:
 speculative verify + replay (HBM roofline), the ragged and long prefills
 (fp16 MFMA roofline), the decode step with precomputed effective gates in the
-dense rank-4 layout, and the compact causal convolution upstream of the operator
-on a prefill and a decode batch (HBM roofline); --workload NAME times just one
-of them.
+dense rank-4 layout, the compact causal convolution upstream of the operator
+on a prefill and a decode batch (HBM roofline), and the speculative step over a
+fixed-state pool (verify, replay, publish); --workload NAME times just one of
+them.
 """
 from __future__ import annotations
 
@@ -240,6 +241,67 @@ def run_verify_replay(args, torch, gdn):
                          "verify_bytes": verify_bytes, "replay_bytes": replay_bytes}}
 
 
+def run_spec_step_pooled(args, torch, gdn):
+    """The speculative step over a fixed-state pool: verify reads each request's
+    committed slot (capsule, no final state), replay writes the accepted prefix into
+    its inactive slot in the same pool, and publication swaps the two slot arrays
+    on the device. Same shapes as spec_verify_replay; the pool holds K disjoint
+    slot sets (one committed/inactive pair of arrays each) rotated over steps so
+    every step reads cold state."""
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs("spec_verify_replay")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R, cap = len(inp["cu_seqlens"]) - 1, inp["capacity"]
+    W = gdn.capsule_width(Hk, Hv, Dk, Dv)
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    acc_host = inp["accepted"]
+    acc = _dev(acc_host, torch)
+    state_bytes = R * Hv * Dv * Dk * 4
+    sets = max(2, -(-(3 * BANK_TARGET_BYTES // 2) // (2 * state_bytes)))
+    P = 2 * R * sets
+    pool = torch.empty((P, Hv, Dv, Dk), dtype=torch.float32, device="cuda")
+    init = _dev(inp["initial_state"], torch)
+    pairs = []
+    for j in range(sets):
+        base = 2 * R * j
+        committed = torch.arange(base, base + R, dtype=torch.int32, device="cuda")
+        inactive = torch.arange(base + R, base + 2 * R, dtype=torch.int32, device="cuda")
+        pool[base:base + R] = init
+        pool[base + R:base + 2 * R] = init
+        pairs.append((committed, inactive))
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    capsule = torch.empty((R, cap, W), dtype=torch.float32, device="cuda")
+    host_cu = inp["cu_seqlens"]
+
+    def step(i):
+        committed, inactive = pairs[i % sets]
+        gdn.gdn_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu, out, num_slots=P, read_slots=committed,
+                               write_slots=None, initial_state=pool, final_state=None,
+                               state_update=capsule, state_update_capacity=cap, cu_seqlens_host=host_cu,
+                               plan=gdn.PLAN_RECURRENT)
+        gdn.gdn_replay_pooled(pool, capsule, acc, pool, num_k_heads=Hk, state_update_capacity=cap,
+                              read_slots=committed, write_slots=inactive, accepted_host=acc_host)
+        gdn.gdn_publish_slots(committed, inactive)
+
+    _log(f"pooled verify+replay+publish: R={R} T=4 Hv={Hv} slots={P}")
+    ms = _time_steps(torch, step, args.steps, args.warmup)
+    io = 2
+    verify_bytes = (state_bytes + R * cap * W * 4 + 2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io
+                    + 2 * N * Hv * 4 + 2 * Hv * 4 + (R + 1) * 4 + R * 4)
+    replay_bytes = 2 * state_bytes + int(acc_host.sum()) * W * 4 + 3 * R * 4
+    nbytes = verify_bytes + replay_bytes + 4 * R * 4
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"requests": R, "draft_tokens": 4, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                       "capacity": cap, "accepted": acc_host.tolist(), "pool_slots": P},
+            "roofline": {"bound": "hbm", "kernel": "gdn_capsule+gdn_replay+gdn_publish",
+                         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_step": nbytes}}
+
+
 def prefill_flops(lengths, Hk, Hv, D, chunk=64):
     """Algorithmic MFMA flops of the chunked prefill: per chunk of L tokens,
     Hk * 4 L^2 D (Q K^T and K K^T per key head) + Hv * (6 L^2 D + 6 L D^2)
@@ -427,7 +489,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="all",
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
-                             "decode_effective_dense", "conv_prefill", "conv_decode", "hbm_copy"],
+                             "decode_effective_dense", "conv_prefill", "conv_decode",
+                             "spec_step_pooled", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="length of the oracle CPU-baseline sample (0 skips it)")
@@ -451,6 +514,7 @@ def main():
               "decode_effective_dense": lambda: run_decode_effective_dense(args, torch, gdn),
               "conv_prefill": lambda: run_conv(args, torch, gdn, "conv_prefill"),
               "conv_decode": lambda: run_conv(args, torch, gdn, "conv_decode"),
+              "spec_step_pooled": lambda: run_spec_step_pooled(args, torch, gdn),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
         print(json.dumps({"metric": METRIC, "workload": args.workload, **res}), flush=True)
@@ -464,6 +528,7 @@ def main():
             "decode_effective_dense": run_decode_effective_dense(args, torch, gdn),
             "conv_prefill": run_conv(args, torch, gdn, "conv_prefill"),
             "conv_decode": run_conv(args, torch, gdn, "conv_decode"),
+            "spec_step_pooled": run_spec_step_pooled(args, torch, gdn),
         }
     if args.cpu_seconds > 0:
         _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")

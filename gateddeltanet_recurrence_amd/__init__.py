@@ -14,4 +14,6 @@ from .binding import (  # noqa: F401
     lib, library_path, gdn_abi_version, gdn_strerror, gdn_forward, gdn_forward_workspace_bytes,
     gdn_resolve_plan, gdn_replay, capsule_width, make_params,
     CONV_SILU, CONV_NONE, GdnConvParams, GdnConvTensors, gdn_conv_forward, gdn_conv_replay,
+    GdnSlots, gdn_forward_pooled, gdn_replay_pooled, gdn_conv_forward_pooled, gdn_conv_replay_pooled,
+    gdn_publish_slots,
 )

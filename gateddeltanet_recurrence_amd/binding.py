@@ -1,5 +1,5 @@
-"""ctypes binding of the C ABI in include/gdn.h and include/gdn_conv.h (same
-entry-point names).
+"""ctypes binding of the C ABI in include/gdn.h, include/gdn_conv.h and
+include/gdn_pool.h (same entry-point names).
 
 Tensors are torch tensors on the current HIP device; torch only provides the
 device memory and the stream. Shapes are read from the tensors, checked for
@@ -20,7 +20,7 @@ GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA = 0
 GATE_RAW, GATE_NONE = 0, 1
-ABI_VERSION = 2          # the struct layouts below match this version of include/gdn.h
+ABI_VERSION = 3          # the struct layouts below match this version of include/gdn.h
 CONV_SILU, CONV_NONE = 0, 1
 
 
@@ -63,6 +63,12 @@ class GdnConvTensors(ctypes.Structure):
         "output", "state_update", "capture_count")]
 
 
+class GdnSlots(ctypes.Structure):
+    _fields_ = [("num_slots", ctypes.c_int32), ("read_slots", ctypes.c_void_p),
+                ("write_slots", ctypes.c_void_p), ("read_slots_host", ctypes.c_void_p),
+                ("write_slots_host", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -96,6 +102,19 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv_forward.restype = ctypes.c_int
         L.gdn_conv_replay.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.gdn_conv_replay.restype = ctypes.c_int
+        sp = ctypes.POINTER(GdnSlots)
+        L.gdn_forward_pooled.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), sp, vp,
+                                         ctypes.c_size_t, vp]
+        L.gdn_forward_pooled.restype = ctypes.c_int
+        L.gdn_replay_pooled.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sp, vp]
+        L.gdn_replay_pooled.restype = ctypes.c_int
+        L.gdn_conv_forward_pooled.argtypes = [ctypes.POINTER(GdnConvParams),
+                                              ctypes.POINTER(GdnConvTensors), sp, vp]
+        L.gdn_conv_forward_pooled.restype = ctypes.c_int
+        L.gdn_conv_replay_pooled.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sp, vp]
+        L.gdn_conv_replay_pooled.restype = ctypes.c_int
+        L.gdn_publish_slots.argtypes = [i32, vp, vp, vp]
+        L.gdn_publish_slots.restype = ctypes.c_int
         L.gdn_strerror.argtypes = [ctypes.c_int]
         L.gdn_strerror.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -182,14 +201,45 @@ def _host_i32(arr):
     return a, a.ctypes.data
 
 
+def _slots(R, num_slots, read_slots, write_slots, read_slots_host, write_slots_host):
+    """GdnSlots for R requests plus the host arrays it points to (kept alive by the caller)."""
+    torch = _torch()
+    _need(read_slots, "read_slots", (R,), torch.int32)
+    _need(write_slots, "write_slots", (R,), torch.int32)
+    rh, rh_ptr = _host_i32(read_slots_host)
+    wh, wh_ptr = _host_i32(write_slots_host)
+    for h, name in ((rh, "read_slots_host"), (wh, "write_slots_host")):
+        if h is not None and h.shape != (R,):
+            raise ValueError(f"{name} must have R entries")
+    sl = GdnSlots(int(num_slots), _ptr(read_slots), _ptr(write_slots), rh_ptr, wh_ptr)
+    return sl, (rh, wh)
+
+
 # ------------------------------------------------------------- entry points
-def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state=None,
-                final_state=None, state_update=None, capture_count=None, cu_seqlens_host=None,
-                scale: float = 0.0, chunk: int = 0, state_update_capacity: int = 0,
-                plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA,
-                gate_activation: int = GATE_RAW, num_reqs: Optional[int] = None, workspace=None,
-                stream=None, check: bool = True) -> int:
+def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, **kw) -> int:
     """gdn_forward of include/gdn.h on torch tensors; returns the status code.
+    Keywords as _forward."""
+    return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, **kw)
+
+
+def gdn_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, num_slots: int,
+                       read_slots=None, write_slots=None, read_slots_host=None,
+                       write_slots_host=None, **kw) -> int:
+    """gdn_forward_pooled of include/gdn_pool.h: initial_state and final_state are
+    pools [P, Hv, Dv, Dk]; request r reads slot read_slots[r] and writes slot
+    write_slots[r] (int32 GPU tensors [R], None for slot r)."""
+    pool = dict(num_slots=num_slots, read_slots=read_slots, write_slots=write_slots,
+                read_slots_host=read_slots_host, write_slots_host=write_slots_host)
+    return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, pool=pool, **kw)
+
+
+def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state=None,
+             final_state=None, state_update=None, capture_count=None, cu_seqlens_host=None,
+             scale: float = 0.0, chunk: int = 0, state_update_capacity: int = 0,
+             plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA,
+             gate_activation: int = GATE_RAW, num_reqs: Optional[int] = None, workspace=None,
+             stream=None, check: bool = True, pool=None) -> int:
+    """One forward call on torch tensors; returns the status code.
 
     q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32 (for the
     dense rank-4 layout, cu_seqlens None: [R, S, H, D] tensors, or the same
@@ -224,8 +274,9 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_st
     _need(A_log, "A_log", (Hv,), torch.float32)
     _need(dt_bias, "dt_bias", (Hv,), torch.float32)
     _need(cu_seqlens, "cu_seqlens", (R + 1,), torch.int32)
-    _need(initial_state, "initial_state", (R, Hv, Dv, Dk), torch.float32)
-    _need(final_state, "final_state", (R, Hv, Dv, Dk), torch.float32)
+    S = int(pool["num_slots"]) if pool is not None else R
+    _need(initial_state, "initial_state", (S, Hv, Dv, Dk), torch.float32)
+    _need(final_state, "final_state", (S, Hv, Dv, Dk), torch.float32)
     if state_update is not None:
         _need(state_update, "state_update",
               (R, state_update_capacity, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
@@ -244,11 +295,17 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_st
     tens = GdnTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                       _ptr(cu_seqlens), host_cu_ptr, _ptr(initial_state), _ptr(final_state),
                       _ptr(output), _ptr(state_update), _ptr(capture_count))
-    st = lib().gdn_forward(ctypes.byref(params), ctypes.byref(tens), ws_ptr,
-                           ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    if pool is None:
+        st = lib().gdn_forward(ctypes.byref(params), ctypes.byref(tens), ws_ptr,
+                               ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    else:
+        sl, keep = _slots(R, **pool)
+        st = lib().gdn_forward_pooled(ctypes.byref(params), ctypes.byref(tens), ctypes.byref(sl), ws_ptr,
+                                      ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+        del keep
     del host_cu
     if check and st != GDN_OK:
-        raise GDNError(st, "gdn_forward")
+        raise GDNError(st, "gdn_forward_pooled" if pool is not None else "gdn_forward")
     return st
 
 
@@ -281,32 +338,75 @@ def gdn_replay(src_state, state_update, accepted, dst_state, *, num_k_heads: int
                state_update_capacity: int, accepted_host=None, stream=None,
                check: bool = True) -> int:
     """gdn_replay of include/gdn.h: dst = src advanced by the accepted capsule prefix."""
+    return _replay(src_state, state_update, accepted, dst_state, num_k_heads=num_k_heads,
+                   state_update_capacity=state_update_capacity, accepted_host=accepted_host,
+                   stream=stream, check=check)
+
+
+def gdn_replay_pooled(src_pool, state_update, accepted, dst_pool, *, num_k_heads: int,
+                      state_update_capacity: int, read_slots=None, write_slots=None,
+                      read_slots_host=None, write_slots_host=None, accepted_host=None,
+                      stream=None, check: bool = True) -> int:
+    """gdn_replay_pooled of include/gdn_pool.h: pools [P, Hv, Dv, Dk]; the request
+    count is accepted's length."""
+    pool = dict(num_slots=src_pool.shape[0], read_slots=read_slots, write_slots=write_slots,
+                read_slots_host=read_slots_host, write_slots_host=write_slots_host)
+    return _replay(src_pool, state_update, accepted, dst_pool, num_k_heads=num_k_heads,
+                   state_update_capacity=state_update_capacity, accepted_host=accepted_host,
+                   stream=stream, check=check, pool=pool)
+
+
+def _replay(src_state, state_update, accepted, dst_state, *, num_k_heads, state_update_capacity,
+            accepted_host, stream, check, pool=None):
     torch = _torch()
-    R, Hv, Dv, Dk = src_state.shape
+    S, Hv, Dv, Dk = src_state.shape
+    R = accepted.shape[0] if pool is not None else S
     Hk = int(num_k_heads)
     cap = int(state_update_capacity)
-    _need(src_state, "src_state", (R, Hv, Dv, Dk), torch.float32)
-    _need(dst_state, "dst_state", (R, Hv, Dv, Dk), torch.float32)
+    _need(src_state, "src_state", (S, Hv, Dv, Dk), torch.float32)
+    _need(dst_state, "dst_state", (S, Hv, Dv, Dk), torch.float32)
     _need(accepted, "accepted", (R,), torch.int32)
     if cap > 0:
         _need(state_update, "state_update", (R, cap, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
     host_acc, host_ptr = _host_i32(accepted_host)
     if host_acc is not None and host_acc.shape != (R,):
         raise ValueError("accepted_host must have R entries")
-    st = lib().gdn_replay(R, Hk, Hv, Dk, Dv, cap, _ptr(src_state), _ptr(state_update),
-                          _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
+    if pool is None:
+        st = lib().gdn_replay(R, Hk, Hv, Dk, Dv, cap, _ptr(src_state), _ptr(state_update),
+                              _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
+    else:
+        sl, keep = _slots(R, **pool)
+        st = lib().gdn_replay_pooled(R, Hk, Hv, Dk, Dv, cap, _ptr(src_state), _ptr(state_update),
+                                     _ptr(accepted), host_ptr, _ptr(dst_state), ctypes.byref(sl),
+                                     _stream_handle(stream))
+        del keep
     del host_acc
     if check and st != GDN_OK:
-        raise GDNError(st, "gdn_replay")
+        raise GDNError(st, "gdn_replay_pooled" if pool is not None else "gdn_replay")
     return st
 
 
-def gdn_conv_forward(x, weight, bias, cu_seqlens, output, *, initial_state=None,
-                     final_state=None, state_update=None, capture_count=None,
-                     cu_seqlens_host=None, activation: int = CONV_SILU,
-                     state_update_capacity: int = 0, num_reqs: Optional[int] = None,
-                     stream=None, check: bool = True) -> int:
+def gdn_conv_forward(x, weight, bias, cu_seqlens, output, **kw) -> int:
     """gdn_conv_forward of include/gdn_conv.h on torch tensors; returns the status.
+    Keywords as _conv_forward."""
+    return _conv_forward(x, weight, bias, cu_seqlens, output, **kw)
+
+
+def gdn_conv_forward_pooled(x, weight, bias, cu_seqlens, output, *, num_slots: int, read_slots=None,
+                            write_slots=None, read_slots_host=None, write_slots_host=None,
+                            **kw) -> int:
+    """gdn_conv_forward_pooled of include/gdn_pool.h: states are pools [P, C, K - 1]."""
+    pool = dict(num_slots=num_slots, read_slots=read_slots, write_slots=write_slots,
+                read_slots_host=read_slots_host, write_slots_host=write_slots_host)
+    return _conv_forward(x, weight, bias, cu_seqlens, output, pool=pool, **kw)
+
+
+def _conv_forward(x, weight, bias, cu_seqlens, output, *, initial_state=None,
+                  final_state=None, state_update=None, capture_count=None,
+                  cu_seqlens_host=None, activation: int = CONV_SILU,
+                  state_update_capacity: int = 0, num_reqs: Optional[int] = None,
+                  stream=None, check: bool = True, pool=None) -> int:
+    """One convolution forward call on torch tensors; returns the status.
 
     x and output [N, C] float16 or float32 (dense layout, cu_seqlens None:
     [R, S, C] or [N, C] with num_reqs); weight [C, K] and bias [C] float32;
@@ -332,8 +432,9 @@ def gdn_conv_forward(x, weight, bias, cu_seqlens, output, *, initial_state=None,
     _need(weight, "weight", (C, K), torch.float32)
     _need(bias, "bias", (C,), torch.float32)
     _need(cu_seqlens, "cu_seqlens", (R + 1,), torch.int32)
-    _need(initial_state, "initial_state", (R, C, K - 1), torch.float32)
-    _need(final_state, "final_state", (R, C, K - 1), torch.float32)
+    S = int(pool["num_slots"]) if pool is not None else R
+    _need(initial_state, "initial_state", (S, C, K - 1), torch.float32)
+    _need(final_state, "final_state", (S, C, K - 1), torch.float32)
     if state_update is not None:
         _need(state_update, "state_update", (R, state_update_capacity, C), torch.float32)
     _need(capture_count, "capture_count", (R,), torch.int32)
@@ -344,30 +445,75 @@ def gdn_conv_forward(x, weight, bias, cu_seqlens, output, *, initial_state=None,
     tens = GdnConvTensors(_ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), host_cu_ptr,
                           _ptr(initial_state), _ptr(final_state), _ptr(output),
                           _ptr(state_update), _ptr(capture_count))
-    st = lib().gdn_conv_forward(ctypes.byref(params), ctypes.byref(tens), _stream_handle(stream))
+    if pool is None:
+        st = lib().gdn_conv_forward(ctypes.byref(params), ctypes.byref(tens), _stream_handle(stream))
+    else:
+        sl, keep = _slots(R, **pool)
+        st = lib().gdn_conv_forward_pooled(ctypes.byref(params), ctypes.byref(tens), ctypes.byref(sl),
+                                           _stream_handle(stream))
+        del keep
     del host_cu
     if check and st != GDN_OK:
-        raise GDNError(st, "gdn_conv_forward")
+        raise GDNError(st, "gdn_conv_forward_pooled" if pool is not None else "gdn_conv_forward")
     return st
 
 
 def gdn_conv_replay(src_state, state_update, accepted, dst_state, *, state_update_capacity: int,
                     accepted_host=None, stream=None, check: bool = True) -> int:
     """gdn_conv_replay of include/gdn_conv.h: dst = the last K - 1 of [src, accepted inputs]."""
+    return _conv_replay(src_state, state_update, accepted, dst_state,
+                        state_update_capacity=state_update_capacity, accepted_host=accepted_host,
+                        stream=stream, check=check)
+
+
+def gdn_conv_replay_pooled(src_pool, state_update, accepted, dst_pool, *, state_update_capacity: int,
+                           read_slots=None, write_slots=None, read_slots_host=None,
+                           write_slots_host=None, accepted_host=None, stream=None,
+                           check: bool = True) -> int:
+    """gdn_conv_replay_pooled of include/gdn_pool.h: pools [P, C, K - 1]."""
+    pool = dict(num_slots=src_pool.shape[0], read_slots=read_slots, write_slots=write_slots,
+                read_slots_host=read_slots_host, write_slots_host=write_slots_host)
+    return _conv_replay(src_pool, state_update, accepted, dst_pool,
+                        state_update_capacity=state_update_capacity, accepted_host=accepted_host,
+                        stream=stream, check=check, pool=pool)
+
+
+def _conv_replay(src_state, state_update, accepted, dst_state, *, state_update_capacity,
+                 accepted_host, stream, check, pool=None):
     torch = _torch()
-    R, C, Km1 = src_state.shape
+    S, C, Km1 = src_state.shape
+    R = accepted.shape[0] if pool is not None else S
     cap = int(state_update_capacity)
-    _need(src_state, "src_state", (R, C, Km1), torch.float32)
-    _need(dst_state, "dst_state", (R, C, Km1), torch.float32)
+    _need(src_state, "src_state", (S, C, Km1), torch.float32)
+    _need(dst_state, "dst_state", (S, C, Km1), torch.float32)
     _need(accepted, "accepted", (R,), torch.int32)
     if cap > 0:
         _need(state_update, "state_update", (R, cap, C), torch.float32)
     host_acc, host_ptr = _host_i32(accepted_host)
     if host_acc is not None and host_acc.shape != (R,):
         raise ValueError("accepted_host must have R entries")
-    st = lib().gdn_conv_replay(R, C, Km1 + 1, cap, _ptr(src_state), _ptr(state_update),
-                               _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
+    if pool is None:
+        st = lib().gdn_conv_replay(R, C, Km1 + 1, cap, _ptr(src_state), _ptr(state_update),
+                                   _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
+    else:
+        sl, keep = _slots(R, **pool)
+        st = lib().gdn_conv_replay_pooled(R, C, Km1 + 1, cap, _ptr(src_state), _ptr(state_update),
+                                          _ptr(accepted), host_ptr, _ptr(dst_state), ctypes.byref(sl),
+                                          _stream_handle(stream))
+        del keep
     del host_acc
     if check and st != GDN_OK:
-        raise GDNError(st, "gdn_conv_replay")
+        raise GDNError(st, "gdn_conv_replay_pooled" if pool is not None else "gdn_conv_replay")
+    return st
+
+
+def gdn_publish_slots(committed_slots, inactive_slots, *, stream=None, check: bool = True) -> int:
+    """gdn_publish_slots of include/gdn_pool.h: exchanges the two int32 GPU slot arrays."""
+    torch = _torch()
+    R = committed_slots.shape[0]
+    _need(committed_slots, "committed_slots", (R,), torch.int32)
+    _need(inactive_slots, "inactive_slots", (R,), torch.int32)
+    st = lib().gdn_publish_slots(R, _ptr(committed_slots), _ptr(inactive_slots), _stream_handle(stream))
+    if check and st != GDN_OK:
+        raise GDNError(st, "gdn_publish_slots")
     return st

@@ -6,12 +6,16 @@
 // decoding", Key Changes). The library allocates nothing and keeps no state.
 #include "../../include/gdn.h"
 #include "../../include/gdn_conv.h"
+#include "../../include/gdn_pool.h"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <utility>
+#include <vector>
 
 #include "gdn_kernels.h"
 
@@ -125,6 +129,62 @@ int conv_tokens_per_block(int64_t N, int64_t C) {
   return (int)(tb < 1 ? 1 : tb > 64 ? 64 : tb);
 }
 
+// Slots of one call: P = 0 for states indexed by request.
+struct SlotPlan {
+  int64_t P = 0;
+  const int32_t* rd = nullptr;
+  const int32_t* wr = nullptr;
+};
+
+// Validates a slot description for R requests (gdn_pool.h, slot rules).
+// `same_pool`: the read and write pools are one buffer. Collisions are checked
+// where the host knows the slots (a mirror, or the identity of a NULL array).
+int plan_slots(const gdn_slots* s, int64_t R, bool same_pool, SlotPlan* out) {
+  *out = SlotPlan{};
+  if (s == nullptr) return GDN_OK;
+  const int64_t P = s->num_slots;
+  if (P < 1) return GDN_ERR_SHAPE;
+  if ((s->read_slots == nullptr && s->read_slots_host != nullptr) ||
+      (s->write_slots == nullptr && s->write_slots_host != nullptr))
+    return GDN_ERR_SHAPE;
+  if ((s->read_slots == nullptr || s->write_slots == nullptr) && R > P) return GDN_ERR_SHAPE;
+  const bool rd_known = s->read_slots == nullptr || s->read_slots_host != nullptr;
+  const bool wr_known = s->write_slots == nullptr || s->write_slots_host != nullptr;
+  auto rd = [&](int64_t r) -> int64_t { return s->read_slots == nullptr ? r : s->read_slots_host[r]; };
+  auto wr = [&](int64_t r) -> int64_t { return s->write_slots == nullptr ? r : s->write_slots_host[r]; };
+  for (int64_t r = 0; r < R; ++r) {
+    if (rd_known && (rd(r) < -1 || rd(r) >= P)) return GDN_ERR_SHAPE;
+    if (wr_known && (wr(r) < -1 || wr(r) >= P)) return GDN_ERR_SHAPE;
+  }
+  if (wr_known) {
+    // (slot, request) of every write, sorted: equal neighbours are a double write
+    std::vector<std::pair<int64_t, int64_t>> writes;
+    writes.reserve((size_t)R);
+    for (int64_t r = 0; r < R; ++r)
+      if (wr(r) >= 0) writes.emplace_back(wr(r), r);
+    std::sort(writes.begin(), writes.end());
+    for (size_t i = 1; i < writes.size(); ++i)
+      if (writes[i].first == writes[i - 1].first) return GDN_ERR_ALIAS;
+    if (same_pool && rd_known) {
+      // a slot written by one request and read by another
+      std::vector<std::pair<int64_t, int64_t>> reads;
+      reads.reserve((size_t)R);
+      for (int64_t r = 0; r < R; ++r)
+        if (rd(r) >= 0) reads.emplace_back(rd(r), r);
+      std::sort(reads.begin(), reads.end());
+      for (const auto& w : writes) {
+        auto it = std::lower_bound(reads.begin(), reads.end(), std::make_pair(w.first, int64_t{-1}));
+        for (; it != reads.end() && it->first == w.first; ++it)
+          if (it->second != w.second) return GDN_ERR_ALIAS;
+      }
+    }
+  }
+  out->P = P;
+  out->rd = s->read_slots;
+  out->wr = s->write_slots;
+  return GDN_OK;
+}
+
 size_t workspace_for(const Resolved& rv) {
   if (rv.plan != GDN_PLAN_CHUNK) return 0;
   return gdn::chunk_workspace_bytes(rv.chunk_slots, (int)rv.R, (int)rv.Hk, (int)rv.Hv);
@@ -174,8 +234,8 @@ int gdn_forward_workspace_bytes(const gdn_params* p, const int32_t* cu_host, siz
   return GDN_OK;
 }
 
-int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
-                size_t workspace_bytes, void* stream) {
+static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slots* slots,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   Resolved rv;
   int st = check_params(p, &rv);
   if (st != GDN_OK) return st;
@@ -208,12 +268,16 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
   const size_t N = (size_t)rv.N, R = (size_t)rv.R, Hk = (size_t)rv.Hk, Hv = (size_t)rv.Hv;
   const size_t Dk = (size_t)rv.Dk, Dv = (size_t)rv.Dv;
   const size_t W = Hv + Hk * Dk + Hv * Dv;
-  const size_t state_bytes = R * Hv * Dv * Dk * 4;
+  SlotPlan sp;
+  st = plan_slots(slots, rv.R, t->initial_state != nullptr && t->initial_state == t->final_state, &sp);
+  if (st != GDN_OK) return st;
+  const size_t state_bytes = (sp.P > 0 ? (size_t)sp.P : R) * Hv * Dv * Dk * 4;
   const Span inputs[] = {
       Span(t->q, N * Hk * Dk * io), Span(t->k, N * Hk * Dk * io), Span(t->v, N * Hv * Dv * io),
       Span(t->a, N * Hv * 4),       Span(t->b, N * Hv * 4),       Span(t->A_log, Hv * 4),
       Span(t->dt_bias, Hv * 4),     Span(t->cu_seqlens, (R + 1) * 4),
-      Span(t->capture_count, capsule ? R * 4 : 0)};
+      Span(t->capture_count, capsule ? R * 4 : 0), Span(sp.rd, sp.rd ? R * 4 : 0),
+      Span(sp.wr, sp.wr ? R * 4 : 0)};
   const Span init(t->initial_state, state_bytes);
   const Span fin(t->final_state, state_bytes);
   const Span out(t->output, N * Hv * Dv * io);
@@ -247,6 +311,7 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
     a.Dk = (int32_t)rv.Dk; a.Dv = (int32_t)rv.Dv; a.group = (int32_t)(rv.Hv / rv.Hk);
     a.capacity = rv.cap; a.capsule_width = (int32_t)W; a.scale = rv.scale;
     a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
+    a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
     err = gdn::launch_recurrent(a, p->io_dtype, s);
   } else {
     gdn::ChunkArgs a{};
@@ -257,14 +322,16 @@ int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace,
     a.N = (int32_t)rv.N; a.R = (int32_t)rv.R; a.Hk = (int32_t)rv.Hk; a.Hv = (int32_t)rv.Hv;
     a.group = (int32_t)(rv.Hv / rv.Hk); a.max_chunks = (int32_t)rv.chunk_slots; a.scale = rv.scale;
     a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
+    a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
     err = gdn::launch_chunk(a, p->io_dtype, s);
   }
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
-               const float* src, const float* capsule, const int32_t* accepted,
-               const int32_t* accepted_host, float* dst, void* stream) {
+static int replay_impl(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
+                       const float* src, const float* capsule, const int32_t* accepted,
+                       const int32_t* accepted_host, float* dst, const gdn_slots* slots,
+                       void* stream) {
   if (R < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return GDN_ERR_SHAPE;
   if (!supported_dim(Dk) || !supported_dim(Dv)) return GDN_ERR_SHAPE;
   if (capacity < 0) return GDN_ERR_CAPACITY;
@@ -278,20 +345,27 @@ int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_
     for (int32_t r = 0; r < R; ++r)
       if (accepted_host[r] < 0 || accepted_host[r] > capacity) return GDN_ERR_CAPACITY;
   }
-  const size_t state_bytes = (size_t)R * Hv * Dv * Dk * 4;
+  SlotPlan sp;
+  const int sst = plan_slots(slots, R, src == dst, &sp);
+  if (sst != GDN_OK) return sst;
+  const size_t state_bytes = (sp.P > 0 ? (size_t)sp.P : (size_t)R) * Hv * Dv * Dk * 4;
   const Span d(dst, state_bytes);
-  if (d.overlaps(Span(src, state_bytes)) || d.overlaps(Span(capsule, (size_t)R * capacity * W64 * 4)) ||
-      d.overlaps(Span(accepted, (size_t)R * 4)))
+  // a pooled replay may read and write one pool (distinct slots); otherwise the banks are disjoint
+  if ((d.overlaps(Span(src, state_bytes)) && !(sp.P > 0 && src == dst)) ||
+      d.overlaps(Span(capsule, (size_t)R * capacity * W64 * 4)) || d.overlaps(Span(accepted, (size_t)R * 4)) ||
+      d.overlaps(Span(sp.rd, sp.rd ? (size_t)R * 4 : 0)) || d.overlaps(Span(sp.wr, sp.wr ? (size_t)R * 4 : 0)))
     return GDN_ERR_ALIAS;
   gdn::ReplayArgs a{};
   a.src = src; a.capsule = capsule; a.accepted = accepted; a.dst = dst;
+  a.src_slots = sp.rd; a.dst_slots = sp.wr; a.num_slots = (int32_t)sp.P;
   a.R = R; a.Hk = Hk; a.Hv = Hv; a.Dk = Dk; a.Dv = Dv; a.group = Hv / Hk;
   a.capacity = capacity; a.capsule_width = (int32_t)W64;
   hipError_t err = gdn::launch_replay(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* stream) {
+static int conv_forward_impl(const gdn_conv_params* p, const gdn_conv_tensors* t, const gdn_slots* slots,
+                             void* stream) {
   if (p == nullptr || t == nullptr) return GDN_ERR_NULL;
   if (p->activation != GDN_CONV_SILU && p->activation != GDN_CONV_NONE) return GDN_ERR_RULE;
   if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_F16) return GDN_ERR_DTYPE;
@@ -314,11 +388,15 @@ int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* 
     if (st != GDN_OK) return st;
   }
 
+  SlotPlan sp;
+  const int sst = plan_slots(slots, R, t->initial_state != nullptr && t->initial_state == t->final_state, &sp);
+  if (sst != GDN_OK) return sst;
   const size_t io = io_bytes(p->io_dtype);
-  const size_t state_bytes = (size_t)(R * C * (K - 1)) * 4;
+  const size_t state_bytes = (size_t)((sp.P > 0 ? sp.P : R) * C * (K - 1)) * 4;
   const Span inputs[] = {Span(t->x, (size_t)(N * C) * io), Span(t->weight, (size_t)(C * K) * 4),
                          Span(t->bias, (size_t)C * 4), Span(t->cu_seqlens, (size_t)(R + 1) * 4),
-                         Span(t->capture_count, capture ? (size_t)R * 4 : 0)};
+                         Span(t->capture_count, capture ? (size_t)R * 4 : 0),
+                         Span(sp.rd, sp.rd ? (size_t)R * 4 : 0), Span(sp.wr, sp.wr ? (size_t)R * 4 : 0)};
   const Span init(t->initial_state, state_bytes);
   const Span fin(t->final_state, state_bytes);
   const Span out(t->output, (size_t)(N * C) * io);
@@ -353,6 +431,7 @@ int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* 
   a.dense_len = uniform_len >= 0 ? (int32_t)uniform_len : 0;
   a.silu = p->activation == GDN_CONV_SILU ? 1 : 0;
   a.capacity = (int32_t)cap;
+  a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
   a.tokens_per_block = conv_tokens_per_block(N, C);
   // one-dimensional grids of (token blocks or requests) x channel groups
   const int64_t groups = gdn::conv_channel_groups(C);
@@ -381,9 +460,9 @@ int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* 
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int gdn_conv_replay(int32_t R, int32_t C, int32_t K, int32_t capacity, const float* src,
-                    const float* capture, const int32_t* accepted, const int32_t* accepted_host,
-                    float* dst, void* stream) {
+static int conv_replay_impl(int32_t R, int32_t C, int32_t K, int32_t capacity, const float* src,
+                            const float* capture, const int32_t* accepted, const int32_t* accepted_host,
+                            float* dst, const gdn_slots* slots, void* stream) {
   if (R < 0 || !conv_shape_ok(C, K)) return GDN_ERR_SHAPE;
   if (capacity < 0) return GDN_ERR_CAPACITY;
   if (R == 0) return GDN_OK;
@@ -395,15 +474,78 @@ int gdn_conv_replay(int32_t R, int32_t C, int32_t K, int32_t capacity, const flo
     for (int32_t r = 0; r < R; ++r)
       if (accepted_host[r] < 0 || accepted_host[r] > capacity) return GDN_ERR_CAPACITY;
   }
-  const size_t state_bytes = (size_t)R * C * (K - 1) * 4;
+  SlotPlan sp;
+  const int sst = plan_slots(slots, R, src == dst, &sp);
+  if (sst != GDN_OK) return sst;
+  const size_t state_bytes = (sp.P > 0 ? (size_t)sp.P : (size_t)R) * C * (K - 1) * 4;
   const Span d(dst, state_bytes);
-  if (d.overlaps(Span(src, state_bytes)) || d.overlaps(Span(capture, (size_t)R * capacity * C * 4)) ||
-      d.overlaps(Span(accepted, (size_t)R * 4)))
+  if ((d.overlaps(Span(src, state_bytes)) && !(sp.P > 0 && src == dst)) ||
+      d.overlaps(Span(capture, (size_t)R * capacity * C * 4)) || d.overlaps(Span(accepted, (size_t)R * 4)) ||
+      d.overlaps(Span(sp.rd, sp.rd ? (size_t)R * 4 : 0)) || d.overlaps(Span(sp.wr, sp.wr ? (size_t)R * 4 : 0)))
     return GDN_ERR_ALIAS;
   gdn::ConvReplayArgs a{};
   a.src = src; a.capture = capture; a.accepted = accepted; a.dst = dst;
+  a.src_slots = sp.rd; a.dst_slots = sp.wr; a.num_slots = (int32_t)sp.P;
   a.R = R; a.C = C; a.K = K; a.capacity = capacity;
   const hipError_t err = gdn::launch_conv_replay(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_forward(const gdn_params* p, const gdn_tensors* t, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return forward_impl(p, t, nullptr, workspace, workspace_bytes, stream);
+}
+
+int gdn_forward_pooled(const gdn_params* p, const gdn_tensors* t, const gdn_slots* slots, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (slots == nullptr) return GDN_ERR_NULL;
+  return forward_impl(p, t, slots, workspace, workspace_bytes, stream);
+}
+
+int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
+               const float* src, const float* capsule, const int32_t* accepted,
+               const int32_t* accepted_host, float* dst, void* stream) {
+  return replay_impl(R, Hk, Hv, Dk, Dv, capacity, src, capsule, accepted, accepted_host, dst, nullptr, stream);
+}
+
+int gdn_replay_pooled(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
+                      const float* src_pool, const float* capsule, const int32_t* accepted,
+                      const int32_t* accepted_host, float* dst_pool, const gdn_slots* slots, void* stream) {
+  if (slots == nullptr) return GDN_ERR_NULL;
+  return replay_impl(R, Hk, Hv, Dk, Dv, capacity, src_pool, capsule, accepted, accepted_host, dst_pool, slots,
+                     stream);
+}
+
+int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* stream) {
+  return conv_forward_impl(p, t, nullptr, stream);
+}
+
+int gdn_conv_forward_pooled(const gdn_conv_params* p, const gdn_conv_tensors* t, const gdn_slots* slots,
+                            void* stream) {
+  if (slots == nullptr) return GDN_ERR_NULL;
+  return conv_forward_impl(p, t, slots, stream);
+}
+
+int gdn_conv_replay(int32_t R, int32_t C, int32_t K, int32_t capacity, const float* src,
+                    const float* capture, const int32_t* accepted, const int32_t* accepted_host,
+                    float* dst, void* stream) {
+  return conv_replay_impl(R, C, K, capacity, src, capture, accepted, accepted_host, dst, nullptr, stream);
+}
+
+int gdn_conv_replay_pooled(int32_t R, int32_t C, int32_t K, int32_t capacity, const float* src_pool,
+                           const float* capture, const int32_t* accepted, const int32_t* accepted_host,
+                           float* dst_pool, const gdn_slots* slots, void* stream) {
+  if (slots == nullptr) return GDN_ERR_NULL;
+  return conv_replay_impl(R, C, K, capacity, src_pool, capture, accepted, accepted_host, dst_pool, slots,
+                          stream);
+}
+
+int gdn_publish_slots(int32_t R, int32_t* committed, int32_t* inactive, void* stream) {
+  if (R < 0) return GDN_ERR_SHAPE;
+  if (R == 0) return GDN_OK;
+  if (committed == nullptr || inactive == nullptr) return GDN_ERR_NULL;
+  if (Span(committed, (size_t)R * 4).overlaps(Span(inactive, (size_t)R * 4))) return GDN_ERR_ALIAS;
+  const hipError_t err = gdn::launch_publish(R, committed, inactive, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

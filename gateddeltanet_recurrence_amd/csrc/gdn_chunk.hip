@@ -775,13 +775,14 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
   // ---- state rows of this wave, transposed: ST[mb] = S[dv][dk = dk_tile(mb, q) + e], dv = dvw + l16
   const int dvw = d0 + kRowsPerWave * wave;
   float4_t ST[8];
-  const size_t head_off = ((size_t)req * p.Hv + h) * D * D;
+  const float* init = state_head(p.initial_state, state_slot(p.initial_slots, req, p.num_slots), p.Hv, h,
+                                (size_t)D * D);
+  float* fin = state_head(p.final_state, state_slot(p.final_slots, req, p.num_slots), p.Hv, h, (size_t)D * D);
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     ST[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (p.initial_state != nullptr)
-      ST[mb] = *reinterpret_cast<const float4_t*>(p.initial_state + head_off + (size_t)(dvw + l16) * D +
-                                                  dk_tile(mb, q));
+    if (init != nullptr)
+      ST[mb] = *reinterpret_cast<const float4_t*>(init + (size_t)(dvw + l16) * D + dk_tile(mb, q));
   }
 
   ScanCtx x{p, w, h, g, d0, dvw, wave, lane, beg, end, slot0, nch};
@@ -812,10 +813,10 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
   // ---- output of the last chunk, final state
   __builtin_amdgcn_s_waitcnt(0);
   store_out(x, O, o_t0, o_L);
-  if (p.final_state != nullptr) {
+  if (fin != nullptr) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
-      *reinterpret_cast<float4_t*>(p.final_state + head_off + (size_t)(dvw + l16) * D + dk_tile(mb, q)) = ST[mb];
+      *reinterpret_cast<float4_t*>(fin + (size_t)(dvw + l16) * D + dk_tile(mb, q)) = ST[mb];
   }
 }
 

@@ -159,8 +159,11 @@ __device__ __forceinline__ void window_at(const IO* x, int C, int c, int start, 
   }
 }
 
-__device__ __forceinline__ const float* state_of(const float* s, int r, int C, int c, int K) {
-  return s != nullptr ? s + ((size_t)r * C + c) * (K - 1) : nullptr;
+// This thread's K - 1 entries of 4 channels in the state of `slot` (see
+// state_slot), or null when there is no state array or no slot.
+template <typename T>
+__device__ __forceinline__ T* state_of(T* s, int slot, int C, int c, int K) {
+  return (s != nullptr && slot >= 0) ? s + ((size_t)slot * C + c) * (K - 1) : nullptr;
 }
 
 // Workgroups are numbered channel group fastest (token block = blockIdx.x /
@@ -190,7 +193,7 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
   int start = seq_start(p, r), end = max(seq_start(p, r + 1), start);
   int ncap = p.state_update != nullptr ? capture_rows(p, r, end - start) : 0;
   float win[K - 1][4];
-  window_at<IO, K>(x, p.C, c, start, max(t_begin - start, 0), state_of(p.initial_state, r, p.C, c, K), win);
+  window_at<IO, K>(x, p.C, c, start, max(t_begin - start, 0), state_of(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
 
   int t = t_begin;
   while (t < t_end) {
@@ -199,7 +202,7 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
       start = seq_start(p, r);
       end = max(seq_start(p, r + 1), start);
       ncap = p.state_update != nullptr ? capture_rows(p, r, end - start) : 0;
-      window_at<IO, K>(x, p.C, c, start, 0, state_of(p.initial_state, r, p.C, c, K), win);
+      window_at<IO, K>(x, p.C, c, start, 0, state_of(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
     }
     const int stop = min(t_end, max(end, t + 1));           // this request's tokens here
     // kConvUnroll tokens' inputs are loaded before any of them is used, so a
@@ -238,8 +241,10 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
     }
     t = stop;
     // the window now holds e[L .. L + K - 2], the request's final state
-    if (t == end && p.final_state != nullptr && final_in_forward(start, end, tb, p.final_in_place))
-      store_channel_major<K - 1>(p.final_state + ((size_t)r * p.C + c) * (K - 1), win);
+    if (t == end && p.final_state != nullptr && final_in_forward(start, end, tb, p.final_in_place)) {
+      float* fin = state_of(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.C, c, K);
+      if (fin != nullptr) store_channel_major<K - 1>(fin, win);
+    }
   }
 }
 
@@ -257,8 +262,9 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_final_k(ConvArgs p) {
   if (final_in_forward(start, end, p.tokens_per_block, p.final_in_place)) return;
   float e[K - 1][4];
   window_at<IO, K>(static_cast<const IO*>(p.x), p.C, c, start, end - start,
-                   state_of(p.initial_state, r, p.C, c, K), e);
-  store_channel_major<K - 1>(p.final_state + ((size_t)r * p.C + c) * (K - 1), e);
+                   state_of(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), e);
+  float* fin = state_of(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.C, c, K);
+  if (fin != nullptr) store_channel_major<K - 1>(fin, e);
 }
 
 // dst[r] = the last K - 1 of [src[r], capture[r, 0 .. m - 1]], 4 channels per thread.
@@ -271,8 +277,11 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_replay_k(ConvReplayArgs
   const int m = min(max(p.accepted[r], 0), p.capacity);
   float e[K - 1][4];
   // the capture rows of request r are its inputs from row 0 on
-  window_at<float, K>(p.capture + (size_t)r * p.capacity * p.C, p.C, c, 0, m, state_of(p.src, r, p.C, c, K), e);
-  store_channel_major<K - 1>(p.dst + ((size_t)r * p.C + c) * (K - 1), e);
+  float* dst = state_of(p.dst, state_slot(p.dst_slots, r, p.num_slots), p.C, c, K);
+  if (dst == nullptr) return;                      // no slot to write
+  window_at<float, K>(p.capture + (size_t)r * p.capacity * p.C, p.C, c, 0, m,
+                      state_of(p.src, state_slot(p.src_slots, r, p.num_slots), p.C, c, K), e);
+  store_channel_major<K - 1>(dst, e);
 }
 
 template <typename IO, int K>

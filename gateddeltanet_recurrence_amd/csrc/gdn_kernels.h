@@ -31,6 +31,9 @@ struct RecurrentArgs {
   float scale;
   int32_t dense_len;            // tokens per request when cu_seqlens is null
   int32_t gate_none;            // a, b are the effective alpha, beta (no activation)
+  const int32_t* initial_slots; // state pools: slot read / written per request
+  const int32_t* final_slots;
+  int32_t num_slots;            // 0: states indexed by request
 };
 
 struct ReplayArgs {
@@ -42,6 +45,9 @@ struct ReplayArgs {
   int32_t group;
   int32_t capacity;
   int32_t capsule_width;
+  const int32_t* src_slots;     // state pools: slot read / written per request
+  const int32_t* dst_slots;
+  int32_t num_slots;            // 0: states indexed by request
 };
 
 // Chunked prefill (Dk = Dv = 128, chunk 64).
@@ -63,7 +69,27 @@ struct ChunkArgs {
   float scale;
   int32_t dense_len;            // tokens per request when cu_seqlens is null
   int32_t gate_none;            // a, b are the effective alpha, beta (no activation)
+  const int32_t* initial_slots; // state pools: slot read / written per request
+  const int32_t* final_slots;
+  int32_t num_slots;            // 0: states indexed by request
 };
+
+// Slot of request r's state. Without a pool (num_slots = 0) or without a slot
+// array it is r; otherwise slots[r] when that lies in [0, num_slots), and -1
+// (no state: read as zeros, not written) for any other value, so no index a
+// device array holds can reach outside the pool.
+__device__ inline int state_slot(const int32_t* slots, int r, int num_slots) {
+  if (num_slots == 0 || slots == nullptr) return r;
+  const int s = slots[r];
+  return (s >= 0 && s < num_slots) ? s : -1;
+}
+
+// Start of (slot, head h) in a state array of per-head blocks of head_elems
+// floats, or null when there is no array or no slot.
+template <typename T>
+__device__ inline T* state_head(T* base, int slot, int Hv, int h, size_t head_elems) {
+  return (base != nullptr && slot >= 0) ? base + ((size_t)slot * Hv + h) * head_elems : nullptr;
+}
 
 // First token of request i (i = R: the end of the last request), clamped to
 // [0, N]; from cu_seqlens, or i * dense_len for the dense layout.
@@ -93,6 +119,9 @@ struct ConvArgs {
   int32_t tokens_per_block;
   int32_t final_in_place;       // final_state == initial_state
   int32_t final_pending;        // 0: every request's final state is written by the forward kernel
+  const int32_t* initial_slots; // state pools: slot read / written per request
+  const int32_t* final_slots;
+  int32_t num_slots;            // 0: states indexed by request
 };
 
 // Convolution workgroups: 256 threads of 4 adjacent channels each.
@@ -118,6 +147,9 @@ struct ConvReplayArgs {
   const int32_t* accepted;
   float* dst;
   int32_t R, C, K, capacity;
+  const int32_t* src_slots;     // state pools: slot read / written per request
+  const int32_t* dst_slots;
+  int32_t num_slots;            // 0: states indexed by request
 };
 
 // io_dtype: 0 = f32, 1 = f16 (gdn_dtype values).
@@ -126,6 +158,7 @@ hipError_t launch_replay(const ReplayArgs& args, hipStream_t stream);
 hipError_t launch_chunk(const ChunkArgs& args, int io_dtype, hipStream_t stream);
 hipError_t launch_conv(const ConvArgs& args, int io_dtype, hipStream_t stream);
 hipError_t launch_conv_replay(const ConvReplayArgs& args, hipStream_t stream);
+hipError_t launch_publish(int32_t R, int32_t* committed, int32_t* inactive, hipStream_t stream);
 
 // Workspace bytes of the chunk path for `chunk_slots` chunks and these heads.
 size_t chunk_workspace_bytes(int64_t chunk_slots, int R, int Hk, int Hv);

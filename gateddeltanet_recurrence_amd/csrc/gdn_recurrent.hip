@@ -90,7 +90,9 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   const int t0 = seq_start(p, r);
   const int t1 = max(seq_start(p, r + 1), t0);
 
-  const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
+  const float* init = state_head(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.Hv, h,
+                                (size_t)Dv * DK);
+  float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
 
   // ---- state rows into registers
   float S[NI][E];
@@ -102,8 +104,8 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
       float4_t x = {0.f, 0.f, 0.f, 0.f};
-      if (p.initial_state != nullptr && valid[i])
-        x = load_state4(p.initial_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j);
+      if (init != nullptr && valid[i])
+        x = load_state4(init + (size_t)row * DK + 4 * c + 4 * LPR * j);
       S[i][4 * j + 0] = x.x;
       S[i][4 * j + 1] = x.y;
       S[i][4 * j + 2] = x.z;
@@ -216,7 +218,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     }
   }
 
-  if (p.final_state != nullptr) {
+  if (fin != nullptr) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (!valid[i]) continue;
@@ -224,7 +226,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
 #pragma unroll
       for (int j = 0; j < V4; ++j) {
         float4_t x = {S[i][4 * j + 0], S[i][4 * j + 1], S[i][4 * j + 2], S[i][4 * j + 3]};
-        store_state4(p.final_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
+        store_state4(fin + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
       }
     }
   }
@@ -273,7 +275,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
 
   const int t0 = seq_start(p, r);
   const int t1 = max(seq_start(p, r + 1), t0);
-  const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
+  const float* init = state_head(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.Hv, h,
+                                (size_t)Dv * DK);
+  float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
 
   // ---- state rows into registers (issued before any staging)
   float S[NI][E];
@@ -285,8 +289,8 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
       float4_t x = {0.f, 0.f, 0.f, 0.f};
-      if (p.initial_state != nullptr && valid[i])
-        x = load_state4(p.initial_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j);
+      if (init != nullptr && valid[i])
+        x = load_state4(init + (size_t)row * DK + 4 * c + 4 * LPR * j);
       S[i][4 * j + 0] = x.x;
       S[i][4 * j + 1] = x.y;
       S[i][4 * j + 2] = x.z;
@@ -423,7 +427,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
     __syncthreads();   // the next group's staging overwrites the staged tokens
   }
 
-  if (p.final_state != nullptr) {
+  if (fin != nullptr) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (!valid[i]) continue;
@@ -431,7 +435,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
 #pragma unroll
       for (int j = 0; j < V4; ++j) {
         float4_t x = {S[i][4 * j + 0], S[i][4 * j + 1], S[i][4 * j + 2], S[i][4 * j + 3]};
-        store_state4(p.final_state + head_off + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
+        store_state4(fin + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
       }
     }
   }

@@ -30,15 +30,17 @@ __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
   const int r = blockIdx.x / p.Hv;
   const int g = h / p.group;
   const int Dv = p.Dv;
-  const size_t head_off = ((size_t)r * p.Hv + h) * (size_t)Dv * DK;
+  const float* src = state_head(p.src, state_slot(p.src_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
+  float* dst = state_head(p.dst, state_slot(p.dst_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
+  if (dst == nullptr) return;                      // no slot to write
 
   float4_t S[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int row = rsub + RPP * it;
     S[it] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (row < Dv)
-      S[it] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(p.src + head_off + (size_t)row * DK + 4 * c4));
+    if (row < Dv && src != nullptr)
+      S[it] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(src + (size_t)row * DK + 4 * c4));
   }
 
   const int m = min(max(p.accepted[r], 0), p.capacity);
@@ -63,8 +65,25 @@ __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
   for (int it = 0; it < ITERS; ++it) {
     const int row = rsub + RPP * it;
     if (row < Dv)
-      __builtin_nontemporal_store(S[it], reinterpret_cast<float4_t*>(p.dst + head_off + (size_t)row * DK + 4 * c4));
+      __builtin_nontemporal_store(S[it], reinterpret_cast<float4_t*>(dst + (size_t)row * DK + 4 * c4));
   }
+}
+
+// Double-buffered publication: after a replay has written every request's
+// inactive slot, the two slot arrays trade places, so the slot just written
+// becomes the committed one and the old committed slot the next inactive one.
+__global__ void __launch_bounds__(256) gdn_publish(int32_t R, int32_t* committed, int32_t* inactive) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  const int32_t c = committed[r];
+  committed[r] = inactive[r];
+  inactive[r] = c;
+}
+
+hipError_t launch_publish(int32_t R, int32_t* committed, int32_t* inactive, hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(gdn_publish, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, stream, R, committed, inactive);
+  return hipGetLastError();
 }
 
 hipError_t launch_replay(const ReplayArgs& p, hipStream_t stream) {

@@ -33,9 +33,10 @@
  *  - Pointers named as device pointers must point to device memory of the
  *    current HIP device; "_host" pointers point to host memory.
  *  - The caller owns every buffer. The library keeps no pointer after a call
- *    returns, allocates no memory and holds no global mutable state: calls on
- *    different streams may run concurrently as long as their buffers do not
- *    overlap.
+ *    returns, allocates no device memory and holds no global mutable state:
+ *    calls on different streams may run concurrently as long as their buffers
+ *    do not overlap. (Host-side checks of slot mirrors, gdn_pool.h, use
+ *    temporary host memory.)
  *  - All device work is enqueued on `stream` (a hipStream_t; NULL is the null
  *    stream) and runs asynchronously; no call blocks on the device.
  *  - Every argument check runs on the host before anything is enqueued. A
@@ -54,8 +55,9 @@ extern "C" {
 #endif
 
 /* Version of this ABI: structs, entry points and the capsule layout.
- * 2: gdn_params.gate_activation; cu_seqlens may be NULL (dense rank-4 layout). */
-#define GDN_ABI_VERSION 2
+ * 2: gdn_params.gate_activation; cu_seqlens may be NULL (dense rank-4 layout).
+ * 3: the causal convolution (gdn_conv.h) and the state pools (gdn_pool.h). */
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,

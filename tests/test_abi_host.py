@@ -61,7 +61,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 2
+    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 3
     assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
     assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
     assert gdn.gdn_strerror(12345) == "unknown status"
