@@ -18,8 +18,8 @@ speculative verify + replay (HBM roofline), the ragged and long prefills
 (fp16 MFMA roofline), the decode step with precomputed effective gates in the
 dense rank-4 layout, the compact causal convolution upstream of the operator
 on a prefill and a decode batch (HBM roofline), and the speculative step over a
-fixed-state pool (verify, replay, publish); --workload NAME times just one of
-them.
+fixed-state pool (verify, replay, publish), and the decode step with a K-major
+state; --workload NAME times just one of them.
 """
 from __future__ import annotations
 
@@ -174,6 +174,40 @@ def run_decode_effective_dense(args, torch, gdn):
             "config": {"tokens": N, "requests": R, "layout": "dense [R, 1, H, D]",
                        "gates": "effective (activation none)", "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv},
             "roofline": {"bound": "hbm", "kernel": "gdn_decode", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_step": nbytes}}
+
+
+def run_decode_kmajor(args, torch, gdn):
+    """The batched decode step with the K-major state layout [R, Hv, Dk, Dv] (the
+    dense LinearAttention layout): the gdn_decode_kmajor kernel, same state traffic."""
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs("batched_decode")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R = len(inp["cu_seqlens"]) - 1
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    state_bytes = R * Hv * Dv * Dk * 4
+    n_banks = max(2, -(-BANK_TARGET_BYTES // state_bytes))
+    km = np.ascontiguousarray(np.swapaxes(inp["initial_state"], -1, -2))
+    banks = [_dev(km, torch) for _ in range(n_banks)]
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    host_cu = inp["cu_seqlens"]
+
+    def step(i):
+        s = banks[i % n_banks]
+        gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=s, final_state=s,
+                        cu_seqlens_host=host_cu, plan=gdn.PLAN_RECURRENT, state_layout=gdn.STATE_K_MAJOR)
+
+    _log(f"decode, K-major state: R={R} Hv={Hv} banks={n_banks}")
+    ms = _time_steps(torch, step, args.steps, args.warmup)
+    nbytes = decode_bytes(inp)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"tokens": N, "requests": R, "state": "fp32 K-major [64,32,128,128], in place",
+                       "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "state_banks": n_banks},
+            "roofline": {"bound": "hbm", "kernel": "gdn_decode_kmajor", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": None, "algorithmic_bytes_per_step": nbytes}}
 
@@ -490,7 +524,7 @@ def main():
     ap.add_argument("--workload", default="all",
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
                              "decode_effective_dense", "conv_prefill", "conv_decode",
-                             "spec_step_pooled", "hbm_copy"],
+                             "spec_step_pooled", "decode_kmajor", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="length of the oracle CPU-baseline sample (0 skips it)")
@@ -515,6 +549,7 @@ def main():
               "conv_prefill": lambda: run_conv(args, torch, gdn, "conv_prefill"),
               "conv_decode": lambda: run_conv(args, torch, gdn, "conv_decode"),
               "spec_step_pooled": lambda: run_spec_step_pooled(args, torch, gdn),
+              "decode_kmajor": lambda: run_decode_kmajor(args, torch, gdn),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
         print(json.dumps({"metric": METRIC, "workload": args.workload, **res}), flush=True)
@@ -529,6 +564,7 @@ def main():
             "conv_prefill": run_conv(args, torch, gdn, "conv_prefill"),
             "conv_decode": run_conv(args, torch, gdn, "conv_decode"),
             "spec_step_pooled": run_spec_step_pooled(args, torch, gdn),
+            "decode_kmajor": run_decode_kmajor(args, torch, gdn),
         }
     if args.cpu_seconds > 0:
         _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")

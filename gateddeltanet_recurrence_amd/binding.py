@@ -20,6 +20,7 @@ GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA = 0
 GATE_RAW, GATE_NONE = 0, 1
+STATE_V_MAJOR, STATE_K_MAJOR = 0, 1
 ABI_VERSION = 3          # the struct layouts below match this version of include/gdn.h
 CONV_SILU, CONV_NONE = 0, 1
 
@@ -42,6 +43,7 @@ class GdnParams(ctypes.Structure):
         ("io_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("chunk", ctypes.c_int32),
         ("state_update_capacity", ctypes.c_int32), ("plan", ctypes.c_int32),
         ("update_rule", ctypes.c_int32), ("gate_activation", ctypes.c_int32),
+        ("state_layout", ctypes.c_int32),
     ]
 
 
@@ -106,7 +108,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_forward_pooled.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), sp, vp,
                                          ctypes.c_size_t, vp]
         L.gdn_forward_pooled.restype = ctypes.c_int
-        L.gdn_replay_pooled.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sp, vp]
+        L.gdn_replay_pooled.argtypes = [ctypes.POINTER(GdnParams), vp, vp, vp, vp, vp, sp, vp]
         L.gdn_replay_pooled.restype = ctypes.c_int
         L.gdn_conv_forward_pooled.argtypes = [ctypes.POINTER(GdnConvParams),
                                               ctypes.POINTER(GdnConvTensors), sp, vp]
@@ -140,10 +142,11 @@ def capsule_width(Hk: int, Hv: int, Dk: int, Dv: int) -> int:
 
 
 def make_params(N, R, Hk, Hv, Dk, Dv, io_dtype, *, scale=0.0, chunk=0, capacity=0,
-                plan=PLAN_AUTO, update_rule=RULE_GATED_DELTA, gate_activation=GATE_RAW) -> GdnParams:
+                plan=PLAN_AUTO, update_rule=RULE_GATED_DELTA, gate_activation=GATE_RAW,
+                state_layout=STATE_V_MAJOR) -> GdnParams:
     return GdnParams(int(N), int(R), int(Hk), int(Hv), int(Dk), int(Dv), int(io_dtype),
                      float(scale), int(chunk), int(capacity), int(plan), int(update_rule),
-                     int(gate_activation))
+                     int(gate_activation), int(state_layout))
 
 
 # ------------------------------------------------------------------ helpers
@@ -238,7 +241,7 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
              scale: float = 0.0, chunk: int = 0, state_update_capacity: int = 0,
              plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA,
              gate_activation: int = GATE_RAW, num_reqs: Optional[int] = None, workspace=None,
-             stream=None, check: bool = True, pool=None) -> int:
+             stream=None, check: bool = True, pool=None, state_layout: int = STATE_V_MAJOR) -> int:
     """One forward call on torch tensors; returns the status code.
 
     q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32 (for the
@@ -275,8 +278,9 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
     _need(dt_bias, "dt_bias", (Hv,), torch.float32)
     _need(cu_seqlens, "cu_seqlens", (R + 1,), torch.int32)
     S = int(pool["num_slots"]) if pool is not None else R
-    _need(initial_state, "initial_state", (S, Hv, Dv, Dk), torch.float32)
-    _need(final_state, "final_state", (S, Hv, Dv, Dk), torch.float32)
+    st_shape = (S, Hv, Dk, Dv) if state_layout == STATE_K_MAJOR else (S, Hv, Dv, Dk)
+    _need(initial_state, "initial_state", st_shape, torch.float32)
+    _need(final_state, "final_state", st_shape, torch.float32)
     if state_update is not None:
         _need(state_update, "state_update",
               (R, state_update_capacity, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
@@ -291,7 +295,8 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
         ws_ptr, ws_bytes = int(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     params = make_params(N, R, Hk, Hv, Dk, Dv, _io_code(io), scale=scale, chunk=chunk,
                          capacity=state_update_capacity, plan=plan, update_rule=update_rule,
-                         gate_activation=gate_activation)
+                         gate_activation=gate_activation,
+                         state_layout=state_layout)
     tens = GdnTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                       _ptr(cu_seqlens), host_cu_ptr, _ptr(initial_state), _ptr(final_state),
                       _ptr(output), _ptr(state_update), _ptr(capture_count))
@@ -346,43 +351,54 @@ def gdn_replay(src_state, state_update, accepted, dst_state, *, num_k_heads: int
 def gdn_replay_pooled(src_pool, state_update, accepted, dst_pool, *, num_k_heads: int,
                       state_update_capacity: int, read_slots=None, write_slots=None,
                       read_slots_host=None, write_slots_host=None, accepted_host=None,
-                      stream=None, check: bool = True) -> int:
-    """gdn_replay_pooled of include/gdn_pool.h: pools [P, Hv, Dv, Dk]; the request
-    count is accepted's length."""
-    pool = dict(num_slots=src_pool.shape[0], read_slots=read_slots, write_slots=write_slots,
-                read_slots_host=read_slots_host, write_slots_host=write_slots_host)
+                      state_layout: int = STATE_V_MAJOR, pooled: bool = True, stream=None,
+                      check: bool = True) -> int:
+    """gdn_replay_pooled of include/gdn_pool.h: pools [P, Hv, Dv, Dk] (K-major
+    [P, Hv, Dk, Dv]); the request count is accepted's length. pooled=False passes
+    no slot description: the states are then [R, ...], indexed by request."""
+    pool = None
+    if pooled:
+        pool = dict(num_slots=src_pool.shape[0], read_slots=read_slots, write_slots=write_slots,
+                    read_slots_host=read_slots_host, write_slots_host=write_slots_host)
     return _replay(src_pool, state_update, accepted, dst_pool, num_k_heads=num_k_heads,
                    state_update_capacity=state_update_capacity, accepted_host=accepted_host,
-                   stream=stream, check=check, pool=pool)
+                   stream=stream, check=check, pool=pool, state_layout=state_layout, via_params=True)
 
 
 def _replay(src_state, state_update, accepted, dst_state, *, num_k_heads, state_update_capacity,
-            accepted_host, stream, check, pool=None):
+            accepted_host, stream, check, pool=None, state_layout=STATE_V_MAJOR, via_params=False):
     torch = _torch()
-    S, Hv, Dv, Dk = src_state.shape
-    R = accepted.shape[0] if pool is not None else S
+    if state_layout == STATE_K_MAJOR:
+        S, Hv, Dk, Dv = src_state.shape
+    else:
+        S, Hv, Dv, Dk = src_state.shape
+    R = accepted.shape[0]
     Hk = int(num_k_heads)
     cap = int(state_update_capacity)
-    _need(src_state, "src_state", (S, Hv, Dv, Dk), torch.float32)
-    _need(dst_state, "dst_state", (S, Hv, Dv, Dk), torch.float32)
+    st_shape = tuple(src_state.shape)
+    _need(dst_state, "dst_state", st_shape, torch.float32)
+    _need(src_state, "src_state", st_shape, torch.float32)
+    if pool is None and S != R:
+        raise ValueError("request-indexed states need one state per request")
     _need(accepted, "accepted", (R,), torch.int32)
     if cap > 0:
         _need(state_update, "state_update", (R, cap, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
     host_acc, host_ptr = _host_i32(accepted_host)
     if host_acc is not None and host_acc.shape != (R,):
         raise ValueError("accepted_host must have R entries")
-    if pool is None:
+    if not via_params:
         st = lib().gdn_replay(R, Hk, Hv, Dk, Dv, cap, _ptr(src_state), _ptr(state_update),
                               _ptr(accepted), host_ptr, _ptr(dst_state), _stream_handle(stream))
     else:
-        sl, keep = _slots(R, **pool)
-        st = lib().gdn_replay_pooled(R, Hk, Hv, Dk, Dv, cap, _ptr(src_state), _ptr(state_update),
-                                     _ptr(accepted), host_ptr, _ptr(dst_state), ctypes.byref(sl),
-                                     _stream_handle(stream))
+        params = make_params(0, R, Hk, Hv, Dk, Dv, GDN_F32, capacity=cap, state_layout=state_layout)
+        sl, keep = _slots(R, **pool) if pool is not None else (None, None)
+        st = lib().gdn_replay_pooled(ctypes.byref(params), _ptr(src_state), _ptr(state_update),
+                                     _ptr(accepted), host_ptr, _ptr(dst_state),
+                                     ctypes.byref(sl) if sl is not None else None, _stream_handle(stream))
         del keep
     del host_acc
     if check and st != GDN_OK:
-        raise GDNError(st, "gdn_replay_pooled" if pool is not None else "gdn_replay")
+        raise GDNError(st, "gdn_replay_pooled" if via_params else "gdn_replay")
     return st
 
 

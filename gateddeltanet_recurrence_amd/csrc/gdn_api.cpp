@@ -50,6 +50,7 @@ int check_params(const gdn_params* p, Resolved* out) {
   if (p == nullptr) return GDN_ERR_NULL;
   if (p->update_rule != GDN_RULE_GATED_DELTA) return GDN_ERR_RULE;
   if (p->gate_activation != GDN_GATE_RAW && p->gate_activation != GDN_GATE_NONE) return GDN_ERR_RULE;
+  if (p->state_layout != GDN_STATE_V_MAJOR && p->state_layout != GDN_STATE_K_MAJOR) return GDN_ERR_SHAPE;
   if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_F16) return GDN_ERR_DTYPE;
   if (p->num_tokens < 0 || p->num_reqs < 0 || p->num_k_heads <= 0 || p->num_v_heads <= 0)
     return GDN_ERR_SHAPE;
@@ -254,8 +255,11 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
                    t->b == nullptr || t->output == nullptr))
     return GDN_ERR_NULL;
 
-  // alignment of vector-accessed buffers
-  const void* vec_ptrs[] = {t->q, t->k, t->initial_state, t->final_state};
+  // alignment of vector-accessed buffers (the K-major kernels move v and the
+  // output in 4-column vectors)
+  const bool k_major = p->state_layout == GDN_STATE_K_MAJOR;
+  const void* vec_ptrs[] = {t->q, t->k, t->initial_state, t->final_state, k_major ? t->v : nullptr,
+                            k_major ? t->output : nullptr};
   for (const void* ptr : vec_ptrs)
     if (ptr != nullptr && !aligned16(ptr)) return GDN_ERR_SHAPE;
 
@@ -312,7 +316,8 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     a.capacity = rv.cap; a.capsule_width = (int32_t)W; a.scale = rv.scale;
     a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
     a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
-    err = gdn::launch_recurrent(a, p->io_dtype, s);
+    a.k_major = k_major ? 1 : 0;
+    err = k_major ? gdn::launch_recurrent_kmajor(a, p->io_dtype, s) : gdn::launch_recurrent(a, p->io_dtype, s);
   } else {
     gdn::ChunkArgs a{};
     a.q = t->q; a.k = t->k; a.v = t->v; a.a = t->a; a.b = t->b;
@@ -323,6 +328,7 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     a.group = (int32_t)(rv.Hv / rv.Hk); a.max_chunks = (int32_t)rv.chunk_slots; a.scale = rv.scale;
     a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
     a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
+    a.k_major = k_major ? 1 : 0;
     err = gdn::launch_chunk(a, p->io_dtype, s);
   }
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -330,7 +336,7 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
 
 static int replay_impl(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
                        const float* src, const float* capsule, const int32_t* accepted,
-                       const int32_t* accepted_host, float* dst, const gdn_slots* slots,
+                       const int32_t* accepted_host, float* dst, const gdn_slots* slots, bool k_major,
                        void* stream) {
   if (R < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return GDN_ERR_SHAPE;
   if (!supported_dim(Dk) || !supported_dim(Dv)) return GDN_ERR_SHAPE;
@@ -360,6 +366,7 @@ static int replay_impl(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv
   a.src_slots = sp.rd; a.dst_slots = sp.wr; a.num_slots = (int32_t)sp.P;
   a.R = R; a.Hk = Hk; a.Hv = Hv; a.Dk = Dk; a.Dv = Dv; a.group = Hv / Hk;
   a.capacity = capacity; a.capsule_width = (int32_t)W64;
+  a.k_major = k_major ? 1 : 0;
   hipError_t err = gdn::launch_replay(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -505,15 +512,17 @@ int gdn_forward_pooled(const gdn_params* p, const gdn_tensors* t, const gdn_slot
 int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
                const float* src, const float* capsule, const int32_t* accepted,
                const int32_t* accepted_host, float* dst, void* stream) {
-  return replay_impl(R, Hk, Hv, Dk, Dv, capacity, src, capsule, accepted, accepted_host, dst, nullptr, stream);
+  return replay_impl(R, Hk, Hv, Dk, Dv, capacity, src, capsule, accepted, accepted_host, dst, nullptr, false,
+                     stream);
 }
 
-int gdn_replay_pooled(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,
-                      const float* src_pool, const float* capsule, const int32_t* accepted,
+int gdn_replay_pooled(const gdn_params* p, const float* src_pool, const float* capsule, const int32_t* accepted,
                       const int32_t* accepted_host, float* dst_pool, const gdn_slots* slots, void* stream) {
-  if (slots == nullptr) return GDN_ERR_NULL;
-  return replay_impl(R, Hk, Hv, Dk, Dv, capacity, src_pool, capsule, accepted, accepted_host, dst_pool, slots,
-                     stream);
+  if (p == nullptr) return GDN_ERR_NULL;
+  if (p->state_layout != GDN_STATE_V_MAJOR && p->state_layout != GDN_STATE_K_MAJOR) return GDN_ERR_SHAPE;
+  return replay_impl(p->num_reqs, p->num_k_heads, p->num_v_heads, p->head_k_dim, p->head_v_dim,
+                     p->state_update_capacity, src_pool, capsule, accepted, accepted_host, dst_pool, slots,
+                     p->state_layout == GDN_STATE_K_MAJOR, stream);
 }
 
 int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* stream) {

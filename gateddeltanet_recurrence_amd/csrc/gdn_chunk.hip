@@ -778,11 +778,18 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
   const float* init = state_head(p.initial_state, state_slot(p.initial_slots, req, p.num_slots), p.Hv, h,
                                 (size_t)D * D);
   float* fin = state_head(p.final_state, state_slot(p.final_slots, req, p.num_slots), p.Hv, h, (size_t)D * D);
+  // V-major: S[dv][dk .. dk+3] is one 16-byte vector; K-major (the transpose,
+  // [Dk, Dv]): four scalars a row apart. Once per workgroup either way.
+  const bool kmaj = p.k_major != 0;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     ST[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (init != nullptr)
+    if (init != nullptr && !kmaj)
       ST[mb] = *reinterpret_cast<const float4_t*>(init + (size_t)(dvw + l16) * D + dk_tile(mb, q));
+    if (init != nullptr && kmaj) {
+      const float* c0 = init + (size_t)dk_tile(mb, q) * D + dvw + l16;
+      ST[mb] = float4_t{c0[0], c0[D], c0[2 * D], c0[3 * D]};
+    }
   }
 
   ScanCtx x{p, w, h, g, d0, dvw, wave, lane, beg, end, slot0, nch};
@@ -813,10 +820,17 @@ __global__ void __launch_bounds__(ScanCfg<NW>::THREADS) gdn_chunk_scan(ChunkArgs
   // ---- output of the last chunk, final state
   __builtin_amdgcn_s_waitcnt(0);
   store_out(x, O, o_t0, o_L);
-  if (fin != nullptr) {
+  if (fin != nullptr && !kmaj) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
       *reinterpret_cast<float4_t*>(fin + (size_t)(dvw + l16) * D + dk_tile(mb, q)) = ST[mb];
+  }
+  if (fin != nullptr && kmaj) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      float* c0 = fin + (size_t)dk_tile(mb, q) * D + dvw + l16;
+      c0[0] = ST[mb].x; c0[D] = ST[mb].y; c0[2 * D] = ST[mb].z; c0[3 * D] = ST[mb].w;
+    }
   }
 }
 

@@ -34,6 +34,7 @@ struct RecurrentArgs {
   const int32_t* initial_slots; // state pools: slot read / written per request
   const int32_t* final_slots;
   int32_t num_slots;            // 0: states indexed by request
+  int32_t k_major;              // states stored [.., Dk, Dv] (else V-major [.., Dv, Dk])
 };
 
 struct ReplayArgs {
@@ -48,6 +49,7 @@ struct ReplayArgs {
   const int32_t* src_slots;     // state pools: slot read / written per request
   const int32_t* dst_slots;
   int32_t num_slots;            // 0: states indexed by request
+  int32_t k_major;              // states stored [.., Dk, Dv] (else V-major [.., Dv, Dk])
 };
 
 // Chunked prefill (Dk = Dv = 128, chunk 64).
@@ -72,6 +74,7 @@ struct ChunkArgs {
   const int32_t* initial_slots; // state pools: slot read / written per request
   const int32_t* final_slots;
   int32_t num_slots;            // 0: states indexed by request
+  int32_t k_major;              // states stored [.., Dk, Dv] (else V-major [.., Dv, Dk])
 };
 
 // Slot of request r's state. Without a pool (num_slots = 0) or without a slot
@@ -154,6 +157,7 @@ struct ConvReplayArgs {
 
 // io_dtype: 0 = f32, 1 = f16 (gdn_dtype values).
 hipError_t launch_recurrent(const RecurrentArgs& args, int io_dtype, hipStream_t stream);
+hipError_t launch_recurrent_kmajor(const RecurrentArgs& args, int io_dtype, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& args, hipStream_t stream);
 hipError_t launch_chunk(const ChunkArgs& args, int io_dtype, hipStream_t stream);
 hipError_t launch_conv(const ConvArgs& args, int io_dtype, hipStream_t stream);

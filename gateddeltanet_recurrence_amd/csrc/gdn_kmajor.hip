@@ -1,0 +1,240 @@
+// Token-recurrent GatedDeltaNet kernels for the K-major state layout:
+// gdn_decode_kmajor and gdn_capsule_kmajor.
+//
+// The dense LinearAttention path keeps its recurrent state K-major,
+// [B, heads, key_dim, value_dim], where the packed GatedDeltaNet path keeps it
+// V-major (first page, Copilot review of the builder). The matrix per head is
+// M = S^T (Dk rows of Dv contiguous floats), and the gated delta rule reads
+//   pk = M^T k^, pq = M^T q^,  u = beta (v - alpha pk),  o = alpha pq + u (k^ . q^),
+//   M = alpha M + k^ u^T.
+//
+// Work decomposition (CDNA4, wave64). A wavefront owns a slice of 4 LK value
+// columns of one (request, value head) and all Dk rows of it, in registers for
+// the whole segment: lane l holds the 4 columns 4 (l mod LK) .. +3 (one 16-byte
+// vector, so LK adjacent lanes read a 16 LK-byte run of a row) in rows
+// dk = l / LK + (64 / LK) i. The contraction over dk is then an in-lane sum over
+// the lane's rows followed by a sum over the lanes of equal l mod LK (DPP
+// rotations within each row of 16 lanes, two cross-row exchanges): nothing
+// leaves the wavefront, and the update M = alpha M + k^ u^T is lane-local.
+// LK = 8 (full 128-byte lines per row segment) took the batched decode from
+// 69 us (LK = 4, 64-byte segments) to 51 us.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+#ifndef GDN_KMAJ_WAVES
+#define GDN_KMAJ_WAVES 4
+#endif
+// Lanes per state row segment: a wavefront owns 4 * GDN_KMAJ_LANES value columns.
+#ifndef GDN_KMAJ_LANES
+#define GDN_KMAJ_LANES 8
+#endif
+
+namespace gdn {
+
+namespace {
+
+constexpr int kDppRowRor4 = 0x124;    // row_ror:4 within a row of 16 lanes
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8
+
+// Sum over the lanes of each class l mod LK (LK = 4 or 8 lanes per row
+// segment); every lane gets its class total. All 64 lanes must be active.
+template <int LK>
+__device__ __forceinline__ float column_sum(float x) {
+  if constexpr (LK == 4) x += dpp<kDppRowRor4>(x);
+  x += dpp<kDppRowRor8>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float4_t load_state4_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(p));
+}
+__device__ __forceinline__ void store_state4_nt(float* p, float4_t x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<float4_t*>(p));
+}
+
+template <typename IO> struct Io4Store;
+template <> struct Io4Store<float> {
+  static __device__ __forceinline__ void store(float* p, float4_t v) { *reinterpret_cast<float4_t*>(p) = v; }
+};
+template <> struct Io4Store<_Float16> {
+  static __device__ __forceinline__ void store(_Float16* p, float4_t v) {
+    *reinterpret_cast<half4_t*>(p) = half4_t{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+  }
+};
+
+template <typename IO, int DK, bool CAPTURE>
+__device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_per_block, int blocks_per_head) {
+  constexpr int LK = GDN_KMAJ_LANES;               // lanes per row segment
+  constexpr int WD = 4 * LK;                       // value columns per wavefront
+  constexpr int RG = 64 / LK;                      // row groups
+  constexpr int NR = DK / RG;                      // rows per lane
+  static_assert(NR >= 1, "Dk must cover the row groups");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cl = lane % LK;                        // column quad within the slice
+  const int rg = lane / LK;                        // row group: rows rg + RG i
+
+  int item = blockIdx.x;
+  const int blk = item % blocks_per_head;
+  item /= blocks_per_head;
+  const int h = item % p.Hv;
+  const int r = item / p.Hv;
+  const int g = h / p.group;
+  const int Dv = p.Dv;
+  const int slice = blk * waves_per_block + wave;
+  if (slice * WD >= Dv) return;                    // no barrier below: idle waves may leave
+  const int col = slice * WD + 4 * cl;             // first of this lane's 4 columns
+  const bool cvalid = col < Dv;                    // Dv is a multiple of 16, maybe not of WD
+
+  const int t0 = seq_start(p, r);
+  const int t1 = max(seq_start(p, r + 1), t0);
+
+  const size_t head_elems = (size_t)Dv * DK;
+  const float* init = state_head(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.Hv, h, head_elems);
+  float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, head_elems);
+
+  float4_t M[NR];
+  if (init != nullptr && cvalid) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) M[i] = load_state4_nt(init + (size_t)(rg + RG * i) * Dv + col);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) M[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const bool gnone = p.gate_none != 0;
+  const float expA = gnone ? 0.f : expf(p.A_log[h]);
+  const float dtb = gnone ? 0.f : p.dt_bias[h];
+  const IO* __restrict__ qp = static_cast<const IO*>(p.q);
+  const IO* __restrict__ kp = static_cast<const IO*>(p.k);
+  const IO* __restrict__ vp = static_cast<const IO*>(p.v);
+  IO* __restrict__ op = static_cast<IO*>(p.output);
+
+  int ncap = 0;
+  if constexpr (CAPTURE) {
+    int cmax = p.capacity;
+    if (p.capture_count != nullptr) cmax = min(max(p.capture_count[r], 0), p.capacity);
+    ncap = min(t1 - t0, cmax);
+  }
+
+  for (int t = t0; t < t1; ++t) {
+    const IO* krow = kp + ((size_t)t * p.Hk + g) * DK;
+    const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK;
+    float kv[NR], qv[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      kv[i] = IoOps<IO>::load1(krow + rg + RG * i);
+      qv[i] = IoOps<IO>::load1(qrow + rg + RG * i);
+    }
+    const float4_t vv = cvalid ? IoOps<IO>::load4(vp + ((size_t)t * p.Hv + h) * Dv + col)
+                               : float4_t{0.f, 0.f, 0.f, 0.f};
+    const float at = p.a[(size_t)t * p.Hv + h];
+    const float bt = p.b[(size_t)t * p.Hv + h];
+
+    float ssk = 0.f, ssq = 0.f, skq = 0.f;
+    float4_t pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      ssk = fmaf(kv[i], kv[i], ssk);
+      ssq = fmaf(qv[i], qv[i], ssq);
+      skq = fmaf(kv[i], qv[i], skq);
+      pk.x = fmaf(M[i].x, kv[i], pk.x); pk.y = fmaf(M[i].y, kv[i], pk.y);
+      pk.z = fmaf(M[i].z, kv[i], pk.z); pk.w = fmaf(M[i].w, kv[i], pk.w);
+      pq.x = fmaf(M[i].x, qv[i], pq.x); pq.y = fmaf(M[i].y, qv[i], pq.y);
+      pq.z = fmaf(M[i].z, qv[i], pq.z); pq.w = fmaf(M[i].w, qv[i], pq.w);
+    }
+    // with the raw k and q: pk = M^T k = |k| M^T k^, so the norms scale afterwards
+    ssk = column_sum<LK>(ssk);
+    ssq = column_sum<LK>(ssq);
+    skq = column_sum<LK>(skq);
+    pk.x = column_sum<LK>(pk.x); pk.y = column_sum<LK>(pk.y); pk.z = column_sum<LK>(pk.z); pk.w = column_sum<LK>(pk.w);
+    pq.x = column_sum<LK>(pq.x); pq.y = column_sum<LK>(pq.y); pq.z = column_sum<LK>(pq.z); pq.w = column_sum<LK>(pq.w);
+    const float rk = rsqrtf(ssk + kNormEps);
+    const float rq = rsqrtf(ssq + kNormEps) * p.scale;
+    const float alpha = gate_alpha(at, gnone, expA, dtb);
+    const float beta = gate_beta(bt, gnone);
+    const float kq = skq * rk * rq;                // k^ . q^
+    const float ak = alpha * rk, aq = alpha * rq;
+
+    float4_t u, o;
+    u.x = beta * fmaf(-ak, pk.x, vv.x); u.y = beta * fmaf(-ak, pk.y, vv.y);
+    u.z = beta * fmaf(-ak, pk.z, vv.z); u.w = beta * fmaf(-ak, pk.w, vv.w);
+    o.x = fmaf(aq, pq.x, u.x * kq); o.y = fmaf(aq, pq.y, u.y * kq);
+    o.z = fmaf(aq, pq.z, u.z * kq); o.w = fmaf(aq, pq.w, u.w * kq);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const float kh = kv[i] * rk;
+      M[i].x = fmaf(alpha, M[i].x, kh * u.x); M[i].y = fmaf(alpha, M[i].y, kh * u.y);
+      M[i].z = fmaf(alpha, M[i].z, kh * u.z); M[i].w = fmaf(alpha, M[i].w, kh * u.w);
+    }
+    if (rg == 0 && cvalid) Io4Store<IO>::store(op + ((size_t)t * p.Hv + h) * Dv + col, o);
+
+    if constexpr (CAPTURE) {
+      const int jcap = t - t0;
+      if (jcap < ncap) {
+        float* caprow = p.state_update + ((size_t)r * p.capacity + jcap) * p.capsule_width;
+        if (rg == 0 && cvalid) {
+          float* d = caprow + p.Hv + p.Hk * DK + h * Dv + col;
+          d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
+        }
+        if (slice == 0) {
+          if (lane == 0) caprow[h] = alpha;
+          // the shared key is written once per key head, by its first value head
+          if (h % p.group == 0 && cl == 0) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) caprow[p.Hv + g * DK + rg + RG * i] = kv[i] * rk;
+          }
+        }
+      }
+    }
+  }
+
+  if (fin != nullptr && cvalid) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) store_state4_nt(fin + (size_t)(rg + RG * i) * Dv + col, M[i]);
+  }
+}
+
+}  // namespace
+
+template <typename IO, int DK>
+__global__ void __launch_bounds__(64 * GDN_KMAJ_WAVES) gdn_decode_kmajor(RecurrentArgs p, int wpb, int bph) {
+  kmajor_body<IO, DK, false>(p, wpb, bph);
+}
+template <typename IO, int DK>
+__global__ void __launch_bounds__(64 * GDN_KMAJ_WAVES) gdn_capsule_kmajor(RecurrentArgs p, int wpb, int bph) {
+  kmajor_body<IO, DK, true>(p, wpb, bph);
+}
+
+template <typename IO, int DK>
+static hipError_t launch_kmajor_dk(const RecurrentArgs& p, hipStream_t stream) {
+  const int slices = (p.Dv + 4 * GDN_KMAJ_LANES - 1) / (4 * GDN_KMAJ_LANES);
+  const int wpb = slices < GDN_KMAJ_WAVES ? slices : GDN_KMAJ_WAVES;
+  const int bph = (slices + wpb - 1) / wpb;
+  const dim3 grid((unsigned)((size_t)p.R * p.Hv * bph)), block((unsigned)(64 * wpb));
+  if (p.state_update != nullptr)
+    hipLaunchKernelGGL((gdn_capsule_kmajor<IO, DK>), grid, block, 0, stream, p, wpb, bph);
+  else
+    hipLaunchKernelGGL((gdn_decode_kmajor<IO, DK>), grid, block, 0, stream, p, wpb, bph);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_kmajor_io(const RecurrentArgs& p, hipStream_t stream) {
+  switch (p.Dk) {
+    case 16: return launch_kmajor_dk<IO, 16>(p, stream);
+    case 32: return launch_kmajor_dk<IO, 32>(p, stream);
+    case 64: return launch_kmajor_dk<IO, 64>(p, stream);
+    case 128: return launch_kmajor_dk<IO, 128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_recurrent_kmajor(const RecurrentArgs& p, int io_dtype, hipStream_t stream) {
+  if (p.R == 0) return hipSuccess;
+  return io_dtype == 1 ? launch_kmajor_io<_Float16>(p, stream) : launch_kmajor_io<float>(p, stream);
+}
+
+}  // namespace gdn

@@ -8,20 +8,24 @@
 // A pure stream: every state element is read once from the committed bank and
 // written once to the inactive bank (nontemporal, so the streams do not evict
 // cached data); the m_r rank-1 updates run in registers.
-// A workgroup owns one (request, value head) slice of Dv x Dk floats; thread t
-// owns the 16-byte column group t % (Dk/4) of rows t / (Dk/4) + (256/(Dk/4)) i,
-// so it needs one key vector and a few delta scalars per capsule row, read
-// through the cache (the capsule is small and shared by a head's threads).
+// A workgroup owns one (request, value head) slice of Dv x Dk floats, in either
+// state layout; the capsule values it needs per row are read through the cache
+// (the capsule is small and shared by a head's threads).
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
 namespace gdn {
 
-template <int DK>
+// ROW is the length of a stored state row: Dk for the V-major layout (rows are
+// dv), Dv for the K-major one (rows are dk). A thread owns one 16-byte group of
+// 4 row elements in rows t / (ROW/4) + (256/(ROW/4)) i. Per capsule row it needs
+// a 4-vector and one scalar per row: V-major the key k^[4 dk] and u[dv = row],
+// K-major u[4 dv] and k^[dk = row].
+template <int ROW, bool KMAJOR>
 __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
-  constexpr int C4 = DK / 4;          // 16-byte column groups per row
+  constexpr int C4 = ROW / 4;         // 16-byte groups per row
   constexpr int RPP = 256 / C4;       // rows per pass of the block
-  constexpr int ITERS = 128 / RPP;    // passes: the block covers 128 rows
+  constexpr int ITERS = 128 / RPP;    // passes: the block covers up to 128 rows
   const int tid = threadIdx.x;
   const int c4 = tid % C4;
   const int rsub = tid / C4;
@@ -29,9 +33,10 @@ __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
   const int h = blockIdx.x % p.Hv;
   const int r = blockIdx.x / p.Hv;
   const int g = h / p.group;
-  const int Dv = p.Dv;
-  const float* src = state_head(p.src, state_slot(p.src_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
-  float* dst = state_head(p.dst, state_slot(p.dst_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
+  const int rows = KMAJOR ? p.Dk : p.Dv;
+  const size_t head_elems = (size_t)p.Dv * p.Dk;
+  const float* src = state_head(p.src, state_slot(p.src_slots, r, p.num_slots), p.Hv, h, head_elems);
+  float* dst = state_head(p.dst, state_slot(p.dst_slots, r, p.num_slots), p.Hv, h, head_elems);
   if (dst == nullptr) return;                      // no slot to write
 
   float4_t S[ITERS];
@@ -39,33 +44,35 @@ __global__ void __launch_bounds__(256) gdn_replay(ReplayArgs p) {
   for (int it = 0; it < ITERS; ++it) {
     const int row = rsub + RPP * it;
     S[it] = float4_t{0.f, 0.f, 0.f, 0.f};
-    if (row < Dv && src != nullptr)
-      S[it] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(src + (size_t)row * DK + 4 * c4));
+    if (row < rows && src != nullptr)
+      S[it] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(src + (size_t)row * ROW + 4 * c4));
   }
 
   const int m = min(max(p.accepted[r], 0), p.capacity);
   const float* caprow = p.capsule + (size_t)r * p.capacity * p.capsule_width;
-  const int key_off = p.Hv + g * DK + 4 * c4;
-  const int delta_off = p.Hv + p.Hk * DK + h * Dv;
+  const int key_off = p.Hv + g * p.Dk;
+  const int delta_off = p.Hv + p.Hk * p.Dk + h * p.Dv;
+  const int vec_off = (KMAJOR ? delta_off : key_off) + 4 * c4;     // the 4-vector of this thread
+  const int row_off = KMAJOR ? key_off : delta_off;                // the per-row scalars
   for (int j = 0; j < m; ++j, caprow += p.capsule_width) {
     const float alpha = caprow[h];
-    const float4_t kk = {caprow[key_off], caprow[key_off + 1], caprow[key_off + 2], caprow[key_off + 3]};
+    const float4_t w = {caprow[vec_off], caprow[vec_off + 1], caprow[vec_off + 2], caprow[vec_off + 3]};
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int row = rsub + RPP * it;
-      const float u = row < Dv ? caprow[delta_off + row] : 0.f;
-      S[it].x = fmaf(alpha, S[it].x, u * kk.x);
-      S[it].y = fmaf(alpha, S[it].y, u * kk.y);
-      S[it].z = fmaf(alpha, S[it].z, u * kk.z);
-      S[it].w = fmaf(alpha, S[it].w, u * kk.w);
+      const float s = row < rows ? caprow[row_off + row] : 0.f;
+      S[it].x = fmaf(alpha, S[it].x, s * w.x);
+      S[it].y = fmaf(alpha, S[it].y, s * w.y);
+      S[it].z = fmaf(alpha, S[it].z, s * w.z);
+      S[it].w = fmaf(alpha, S[it].w, s * w.w);
     }
   }
 
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int row = rsub + RPP * it;
-    if (row < Dv)
-      __builtin_nontemporal_store(S[it], reinterpret_cast<float4_t*>(dst + (size_t)row * DK + 4 * c4));
+    if (row < rows)
+      __builtin_nontemporal_store(S[it], reinterpret_cast<float4_t*>(dst + (size_t)row * ROW + 4 * c4));
   }
 }
 
@@ -90,11 +97,16 @@ hipError_t launch_replay(const ReplayArgs& p, hipStream_t stream) {
   if (p.R == 0) return hipSuccess;
   const dim3 grid((unsigned)((size_t)p.R * p.Hv));
   const dim3 block(256);
-  switch (p.Dk) {
-    case 16: hipLaunchKernelGGL(gdn_replay<16>, grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(gdn_replay<32>, grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(gdn_replay<64>, grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(gdn_replay<128>, grid, block, 0, stream, p); break;
+  const int row = p.k_major ? p.Dv : p.Dk;
+  switch (row * 2 + (p.k_major ? 1 : 0)) {
+    case 32: hipLaunchKernelGGL((gdn_replay<16, false>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((gdn_replay<32, false>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((gdn_replay<64, false>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((gdn_replay<128, false>), grid, block, 0, stream, p); break;
+    case 33: hipLaunchKernelGGL((gdn_replay<16, true>), grid, block, 0, stream, p); break;
+    case 65: hipLaunchKernelGGL((gdn_replay<32, true>), grid, block, 0, stream, p); break;
+    case 129: hipLaunchKernelGGL((gdn_replay<64, true>), grid, block, 0, stream, p); break;
+    case 257: hipLaunchKernelGGL((gdn_replay<128, true>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -56,7 +56,8 @@ extern "C" {
 
 /* Version of this ABI: structs, entry points and the capsule layout.
  * 2: gdn_params.gate_activation; cu_seqlens may be NULL (dense rank-4 layout).
- * 3: the causal convolution (gdn_conv.h) and the state pools (gdn_pool.h). */
+ * 3: gdn_params.state_layout; the causal convolution (gdn_conv.h) and the state
+ *    pools (gdn_pool.h). */
 #define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
@@ -98,6 +99,15 @@ typedef enum gdn_rule { GDN_RULE_GATED_DELTA = 0 } gdn_rule;
  *                 be NULL. */
 typedef enum gdn_gate_activation { GDN_GATE_RAW = 0, GDN_GATE_NONE = 1 } gdn_gate_activation;
 
+/* How the FP32 state of a (request, value head) is stored.
+ *  GDN_STATE_V_MAJOR: [Dv, Dk], each dv row of Dk floats contiguous - the packed
+ *                     GatedDeltaNet contract ("Add GatedDeltaNet evaluation export
+ *                     for Qwen hybrid models", What changed: FP32 V-major state).
+ *  GDN_STATE_K_MAJOR: [Dk, Dv], the transpose - the dense LinearAttention layout
+ *                     [B, heads, key_dim, value_dim] (same page, Copilot review).
+ * The capsule layout does not depend on it. */
+typedef enum gdn_state_layout { GDN_STATE_V_MAJOR = 0, GDN_STATE_K_MAJOR = 1 } gdn_state_layout;
+
 typedef struct gdn_params {
   int32_t num_tokens;            /* N: packed tokens over all requests, >= 0      */
   int32_t num_reqs;              /* R: requests (state batch), >= 0               */
@@ -113,6 +123,7 @@ typedef struct gdn_params {
   int32_t plan;                  /* gdn_plan                                       */
   int32_t update_rule;           /* gdn_rule; must be GDN_RULE_GATED_DELTA         */
   int32_t gate_activation;       /* gdn_gate_activation of a and b                 */
+  int32_t state_layout;          /* gdn_state_layout of initial and final states   */
 } gdn_params;
 
 /* Tensors of one forward call. Layouts are dense row-major with the last
@@ -138,8 +149,10 @@ typedef struct gdn_tensors {
   const int32_t* cu_seqlens_host;/* host mirror of cu_seqlens, or NULL. When given
                                     it is validated and used for planning. Must be
                                     NULL when cu_seqlens is NULL.                  */
-  const float* initial_state;    /* device, f32 [R, Hv, Dv, Dk], or NULL for zeros */
-  float* final_state;            /* device, f32 [R, Hv, Dv, Dk], or NULL (not
+  const float* initial_state;    /* device, f32 [R, Hv, Dv, Dk] (K-major: [R, Hv, Dk,
+                                    Dv]), or NULL for zeros. With the K-major
+                                    layout, v and output must be 16-byte aligned. */
+  float* final_state;            /* device, f32, as initial_state, or NULL (not
                                     written). May equal initial_state exactly
                                     (in-place update); any other overlap is an error */
   void* output;                  /* device, io  [N, Hv, Dv]                        */
@@ -174,8 +187,9 @@ int gdn_forward_workspace_bytes(const gdn_params* params, const int32_t* cu_seql
 int gdn_resolve_plan(const gdn_params* params, const int32_t* cu_seqlens_host, int32_t* plan);
 
 /* Replays the leading accepted[r] capsule rows of every request r onto the
- * committed state and writes the result to an inactive bank ("Replay compact
- * fixed state for hybrid decoding", Summary):
+ * committed V-major state and writes the result to an inactive bank ("Replay
+ * compact fixed state for hybrid decoding", Summary); gdn_replay_pooled
+ * (gdn_pool.h) takes the state layout and pools:
  *   dst[r,h] = src[r,h];  for j < m_r:  dst[r,h] = alpha_j * dst[r,h] + u_j k^_j^T
  * with alpha_j, k^_j (key head h / (Hv/Hk)) and u_j read from capsule row j.
  *   src_state     device, f32 [R, Hv, Dv, Dk]  committed bank, read only

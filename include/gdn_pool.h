@@ -49,20 +49,23 @@ typedef struct gdn_slots {
   const int32_t* write_slots_host;
 } gdn_slots;
 
-/* gdn_forward with initial_state and final_state read as pools [P, Hv, Dv, Dk]:
- * request r starts from initial_state[read_slots[r]] and, when final_state is
- * non-NULL, leaves its state in final_state[write_slots[r]]. */
+/* gdn_forward with initial_state and final_state read as pools [P, Hv, Dv, Dk]
+ * (or [P, Hv, Dk, Dv] K-major): request r starts from initial_state[read_slots[r]]
+ * and, when final_state is non-NULL, leaves its state in
+ * final_state[write_slots[r]]. */
 int gdn_forward_pooled(const gdn_params* params, const gdn_tensors* tensors, const gdn_slots* slots,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* gdn_replay from and into pools: request r's committed state is
  * src_pool[read_slots[r]] and the replayed state goes to
- * dst_pool[write_slots[r]]; state_update and accepted as in gdn_replay. */
-int gdn_replay_pooled(int32_t num_reqs, int32_t num_k_heads, int32_t num_v_heads,
-                      int32_t head_k_dim, int32_t head_v_dim, int32_t state_update_capacity,
-                      const float* src_pool, const float* state_update, const int32_t* accepted,
-                      const int32_t* accepted_host, float* dst_pool, const gdn_slots* slots,
-                      void* stream);
+ * dst_pool[write_slots[r]]; state_update and accepted as in gdn_replay. The
+ * sizes and the state layout come from params (num_reqs, the head counts and
+ * dims, state_update_capacity, state_layout; the other fields are not read).
+ * slots may be NULL: the states are then indexed by request ([R, ...]) as in
+ * gdn_replay, which makes this the replay of a K-major state too. */
+int gdn_replay_pooled(const gdn_params* params, const float* src_pool, const float* state_update,
+                      const int32_t* accepted, const int32_t* accepted_host, float* dst_pool,
+                      const gdn_slots* slots, void* stream);
 
 /* gdn_conv_forward with initial_state and final_state read as pools [P, C, K - 1]. */
 int gdn_conv_forward_pooled(const gdn_conv_params* params, const gdn_conv_tensors* tensors,

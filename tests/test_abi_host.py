@@ -117,6 +117,7 @@ def test_null_structs():
     ("chunk", 32, gdn.GDN_ERR_SHAPE),
     ("plan", 9, gdn.GDN_ERR_PLAN),
     ("scale", float("nan"), gdn.GDN_ERR_SHAPE),
+    ("state_layout", 2, gdn.GDN_ERR_SHAPE),
 ])
 def test_param_validation(field, value, code):
     p = _p()
@@ -162,6 +163,14 @@ def test_misaligned_state_is_rejected():
     t, _ = _tensors(8, 2, 2, 4, 16, 16)
     t.initial_state = t.initial_state + 4
     assert _forward(_p(), t) == gdn.GDN_ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", ["v", "output"])
+def test_k_major_needs_aligned_v_and_output(name):
+    # the K-major kernels move v and the output as 4-column vectors
+    t, _ = _tensors(8, 2, 2, 4, 16, 16)
+    setattr(t, name, getattr(t, name) + 2)
+    assert _forward(_p(state_layout=gdn.STATE_K_MAJOR), t) == gdn.GDN_ERR_SHAPE
 
 
 @pytest.mark.parametrize("cu,code", [

@@ -116,16 +116,21 @@ def test_conv_pooled_rules():
     assert gdn.lib().gdn_conv_forward_pooled(ctypes.byref(p), ctypes.byref(t), None, None) == gdn.GDN_ERR_NULL
 
 
-def _replay(sl, src=FAKE, dst=FAKE):
+def _replay(sl, src=FAKE, dst=FAKE, layout=gdn.STATE_V_MAJOR, params=True):
     cap = 2
     capsule = FAKE + (1 << 36)
     acc = FAKE + (1 << 37)
-    return gdn.lib().gdn_replay_pooled(R, Hk, Hv, D, D, cap, src, capsule, acc, None, dst,
+    p = gdn.make_params(0, R, Hk, Hv, D, D, gdn.GDN_F32, capacity=cap, state_layout=layout)
+    return gdn.lib().gdn_replay_pooled(ctypes.byref(p) if params else None, src, capsule, acc, None, dst,
                                        ctypes.byref(sl) if sl is not None else None, None)
 
 
 def test_replay_pooled_rules():
-    assert _replay(None) == gdn.GDN_ERR_NULL
+    sl, keep = _slots()
+    assert _replay(sl, params=False) == gdn.GDN_ERR_NULL
+    assert _replay(sl, layout=2) == gdn.GDN_ERR_SHAPE
+    # without slots the states are request-indexed: one buffer for both is an overlap
+    assert _replay(None) == gdn.GDN_ERR_ALIAS
     sl, keep = _slots(rd=RD, rd_host=[0, 1, 2], wr=WR, wr_host=[1, 4, 5])
     assert _replay(sl) == gdn.GDN_ERR_ALIAS                           # writes slot 1, read by request 1
     sl, keep = _slots(rd=RD, rd_host=[0, 1, 2], wr=WR, wr_host=[4, 4, 5])
