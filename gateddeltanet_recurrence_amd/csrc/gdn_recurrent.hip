@@ -66,6 +66,42 @@ struct RecLayout {
   static_assert(E % 4 == 0, "row slice must be whole float4 vectors");
 };
 
+// The NI state rows of a lane group (rows row_base + i RI + rg, this lane's E
+// floats of each) into registers, zero without an initial state. The loads are
+// issued back to back with no branch or use between them: a row at or past Dv
+// (valid[i] false) loads row Dv - 1 instead, in bounds; rows are independent
+// (each row's dot products reduce over its own lanes only) and nothing of an
+// invalid row is ever stored, so its values need no clearing. (Per-load
+// conditions had compiled to a branch per load with a full wait after the
+// first ones.)
+template <int DK, int NI>
+__device__ __forceinline__ void load_state_rows(const float* init, int row_base, int rg, int c, int Dv,
+                                                float (&S)[NI][RecLayout<DK>::E], bool (&valid)[NI]) {
+  using L = RecLayout<DK>;
+  constexpr int LPR = L::LPR, V4 = L::V4, RI = L::RI;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) valid[i] = row_base + i * RI + rg < Dv;
+  if (init == nullptr) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int e = 0; e < L::E; ++e) S[i][e] = 0.f;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = min(row_base + i * RI + rg, Dv - 1);
+#pragma unroll
+    for (int j = 0; j < V4; ++j) {
+      const float4_t x = load_state4(init + (size_t)row * DK + 4 * c + 4 * LPR * j);
+      S[i][4 * j + 0] = x.x;
+      S[i][4 * j + 1] = x.y;
+      S[i][4 * j + 2] = x.z;
+      S[i][4 * j + 3] = x.w;
+    }
+  }
+}
+
 template <typename IO, int DK, int NI, bool CAPTURE>
 __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves_per_block,
                                                int blocks_per_head) {
@@ -97,21 +133,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   // ---- state rows into registers
   float S[NI][E];
   bool valid[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row = row_base + i * RI + rg;
-    valid[i] = row < Dv;
-#pragma unroll
-    for (int j = 0; j < V4; ++j) {
-      float4_t x = {0.f, 0.f, 0.f, 0.f};
-      if (init != nullptr && valid[i])
-        x = load_state4(init + (size_t)row * DK + 4 * c + 4 * LPR * j);
-      S[i][4 * j + 0] = x.x;
-      S[i][4 * j + 1] = x.y;
-      S[i][4 * j + 2] = x.z;
-      S[i][4 * j + 3] = x.w;
-    }
-  }
+  load_state_rows<DK, NI>(init, row_base, rg, c, Dv, S, valid);
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
   const float expA = gnone ? 0.f : expf(p.A_log[h]);
@@ -142,8 +164,8 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     float vv[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = row_base + i * RI + rg;
-      vv[i] = valid[i] ? IoOps<IO>::load1(vp + ((size_t)t * p.Hv + h) * Dv + row) : 0.f;
+      const int row = min(row_base + i * RI + rg, Dv - 1);     // in bounds; unused past Dv
+      vv[i] = IoOps<IO>::load1(vp + ((size_t)t * p.Hv + h) * Dv + row);
     }
     const float at = p.a[(size_t)t * p.Hv + h];
     const float bt = p.b[(size_t)t * p.Hv + h];
@@ -282,21 +304,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   // ---- state rows into registers (issued before any staging)
   float S[NI][E];
   bool valid[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row = row_base + i * RI + rg;
-    valid[i] = row < Dv;
-#pragma unroll
-    for (int j = 0; j < V4; ++j) {
-      float4_t x = {0.f, 0.f, 0.f, 0.f};
-      if (init != nullptr && valid[i])
-        x = load_state4(init + (size_t)row * DK + 4 * c + 4 * LPR * j);
-      S[i][4 * j + 0] = x.x;
-      S[i][4 * j + 1] = x.y;
-      S[i][4 * j + 2] = x.z;
-      S[i][4 * j + 3] = x.w;
-    }
-  }
+  load_state_rows<DK, NI>(init, row_base, rg, c, Dv, S, valid);
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
   const float expA = gnone ? 0.f : expf(p.A_log[h]);
