@@ -108,6 +108,7 @@ namespace gdn {
 // the number of memory instructions per loop iteration fixed and lets the
 // compiler wait for just the data it needs).
 constexpr int kBufferWord3 = 0x00020000;   // gfx9-family raw buffer descriptor word 3
+constexpr int kBufferNontemporal = 2;      // cache-policy operand of a buffer access: nt
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 

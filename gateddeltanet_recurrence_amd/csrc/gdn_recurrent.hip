@@ -67,33 +67,30 @@ struct RecLayout {
 };
 
 // The NI state rows of a lane group (rows row_base + i RI + rg, this lane's E
-// floats of each) into registers, zero without an initial state. The loads are
-// issued back to back with no branch or use between them: a row at or past Dv
-// (valid[i] false) loads row Dv - 1 instead, in bounds; rows are independent
-// (each row's dot products reduce over its own lanes only) and nothing of an
-// invalid row is ever stored, so its values need no clearing. (Per-load
-// conditions had compiled to a branch per load with a full wait after the
-// first ones.)
+// floats of each) into registers, zero without an initial state. Raw buffer
+// loads with a range check do it without a single branch: the range is the
+// head's Dv x Dk floats, or empty when there is no initial state, and a load
+// outside it returns zero (rows at or past Dv included). Branches around the
+// loads had compiled to waits for the first loads before the later ones were
+// issued, and to waits that also covered the state where only later loads
+// were needed.
 template <int DK, int NI>
-__device__ __forceinline__ void load_state_rows(const float* init, int row_base, int rg, int c, int Dv,
-                                                float (&S)[NI][RecLayout<DK>::E], bool (&valid)[NI]) {
+__device__ __forceinline__ void load_state_rows(const float* init, const void* any_base, int row_base, int rg,
+                                                int c, int Dv, float (&S)[NI][RecLayout<DK>::E],
+                                                bool (&valid)[NI]) {
   using L = RecLayout<DK>;
   constexpr int LPR = L::LPR, V4 = L::V4, RI = L::RI;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) valid[i] = row_base + i * RI + rg < Dv;
-  if (init == nullptr) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int e = 0; e < L::E; ++e) S[i][e] = 0.f;
-    return;
-  }
+  const rsrc_t rs = make_rsrc(init != nullptr ? static_cast<const void*>(init) : any_base,
+                              init != nullptr ? Dv * DK * 4 : 0);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int row = min(row_base + i * RI + rg, Dv - 1);
+    const int row = row_base + i * RI + rg;
+    valid[i] = row < Dv;
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
-      const float4_t x = load_state4(init + (size_t)row * DK + 4 * c + 4 * LPR * j);
+      const float4_t x = __builtin_bit_cast(
+          float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (row * DK + 4 * c + 4 * LPR * j) * 4, 0,
+                                                          kBufferNontemporal));
       S[i][4 * j + 0] = x.x;
       S[i][4 * j + 1] = x.y;
       S[i][4 * j + 2] = x.z;
@@ -133,7 +130,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   // ---- state rows into registers
   float S[NI][E];
   bool valid[NI];
-  load_state_rows<DK, NI>(init, row_base, rg, c, Dv, S, valid);
+  load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
   const float expA = gnone ? 0.f : expf(p.A_log[h]);
@@ -304,7 +301,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   // ---- state rows into registers (issued before any staging)
   float S[NI][E];
   bool valid[NI];
-  load_state_rows<DK, NI>(init, row_base, rg, c, Dv, S, valid);
+  load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
   const float expA = gnone ? 0.f : expf(p.A_log[h]);
