@@ -47,10 +47,12 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # Keyed by the hash of the kernel's sources: a changed kernel reports null until
 # its counters are taken again.
 MEASURED_TRAFFIC = {
-    "gdn_decode": {"sources": ["gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip",
-                               "gateddeltanet_recurrence_amd/csrc/gdn_common.h"],
-                   "sha256_16": "101c87fee620fe66", "fetch_kib": 66993.0, "write_kib": 131609.5,
-                   "bytes": 271945511},
+    "gdn_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+                   "sha256_16": "c001a7a272e8a100", "fetch_kib": 66995.5, "write_kib": 131601.9,
+                   "bytes": 271939688},
+    "gdn_decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+                          "sha256_16": "3bc85c1b7e7eb4c0", "fetch_kib": 66440.1, "write_kib": 131671.6,
+                          "bytes": 270873829},
 }
 
 
@@ -209,7 +211,8 @@ def run_decode_kmajor(args, torch, gdn):
                        "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "state_banks": n_banks},
             "roofline": {"bound": "hbm", "kernel": "gdn_decode_kmajor", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_step": nbytes}}
+                         "traffic": measured_traffic("gdn_decode_kmajor"),
+                         "algorithmic_bytes_per_step": nbytes}}
 
 
 def _time_steps(torch, step, steps, warmup):
