@@ -119,23 +119,40 @@ __device__ __forceinline__ void load_io4(const IO* p, float (&dst)[4]) {
   dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
 }
 
+// The carried inputs of one request's state slot, seen through a raw buffer
+// resource with a range check: the slot's C x (K - 1) floats, or an empty range
+// when there is no state array or no slot, so that every load from it is
+// unconditional and reads zero in the empty case. `off` is this thread's byte
+// offset (its 4 channels' K - 1 entries each, channel-major).
+struct StateRef {
+  rsrc_t rs;
+  int off;
+};
+
+template <typename T>
+__device__ __forceinline__ StateRef state_ref(T* s, int slot, int C, int c, int K) {
+  const bool any = s != nullptr && slot >= 0;
+  return StateRef{make_rsrc(any ? static_cast<const void*>(s + (size_t)slot * C * (K - 1)) : nullptr,
+                            any ? C * (K - 1) * 4 : 0),
+                  c * (K - 1) * 4};
+}
+
 // e[idx .. idx + K - 2] of one request for 4 channels (e = [carried state, the
-// inputs from token `start` on], idx >= 0). `st` points at this thread's
-// carried inputs ([channel][K - 1]) or is null for zeros. idx is uniform across
-// the workgroup. The two common cases, all from the state (idx = 0) and all from
-// the inputs (idx >= K - 1), issue their loads back to back; the mixed case reads
-// entry by entry. No register array is indexed at run time.
+// inputs from token `start` on], idx >= 0). idx is uniform across the
+// workgroup. The two common cases, all from the state (idx = 0) and all from
+// the inputs (idx >= K - 1), issue their loads back to back; the mixed case
+// reads entry by entry. No register array is indexed at run time.
 template <typename IO, int K>
-__device__ __forceinline__ void window_at(const IO* x, int C, int c, int start, int idx,
-                                          const float* st, float (&win)[K - 1][4]) {
+__device__ __forceinline__ void window_at(const IO* x, int C, int c, int start, int idx, StateRef st,
+                                          float (&win)[K - 1][4]) {
   if (idx == 0) {
-    if (st != nullptr) {
-      load_channel_major<K - 1>(st, win);
-    } else {
+    // float 4 i + j of the thread's run is entry m = (4 i + j) mod (K - 1) of
+    // channel (4 i + j) / (K - 1)
 #pragma unroll
-      for (int m = 0; m < K - 1; ++m)
+    for (int i = 0; i < K - 1; ++i) {
+      const float4_t v = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(st.rs, st.off + 16 * i, 0, 0));
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) win[m][ch] = 0.f;
+      for (int j = 0; j < 4; ++j) win[(4 * i + j) % (K - 1)][(4 * i + j) / (K - 1)] = v[j];
     }
   } else if (idx >= K - 1) {
     const IO* row = x + (size_t)(start + idx - (K - 1)) * C + c;
@@ -153,7 +170,7 @@ __device__ __forceinline__ void window_at(const IO* x, int C, int c, int start, 
         win[m][0] = v.x; win[m][1] = v.y; win[m][2] = v.z; win[m][3] = v.w;
       } else {
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) win[m][ch] = st != nullptr ? st[ch * (K - 1) + e] : 0.f;
+        for (int ch = 0; ch < 4; ++ch) win[m][ch] = buf_load_f32(st.rs, st.off + (ch * (K - 1) + e) * 4);
       }
     }
   }
@@ -186,14 +203,17 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
 
   float w[K][4], bias[4];
   load_channel_major<K>(p.weight + (size_t)c * K, w);
+  {
+    const rsrc_t rb = make_rsrc(p.bias, p.bias != nullptr ? p.C * 4 : 0);   // no bias: zeros
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch) bias[ch] = p.bias != nullptr ? p.bias[c + ch] : 0.f;
+    for (int ch = 0; ch < 4; ++ch) bias[ch] = buf_load_f32(rb, (c + ch) * 4);
+  }
 
   // the K - 1 inputs before token t_begin: e[j .. j + K - 2], j = t_begin - start
   int start = seq_start(p, r), end = max(seq_start(p, r + 1), start);
   int ncap = p.state_update != nullptr ? capture_rows(p, r, end - start) : 0;
   float win[K - 1][4];
-  window_at<IO, K>(x, p.C, c, start, max(t_begin - start, 0), state_of(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
+  window_at<IO, K>(x, p.C, c, start, max(t_begin - start, 0), state_ref(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
 
   int t = t_begin;
   while (t < t_end) {
@@ -202,7 +222,7 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
       start = seq_start(p, r);
       end = max(seq_start(p, r + 1), start);
       ncap = p.state_update != nullptr ? capture_rows(p, r, end - start) : 0;
-      window_at<IO, K>(x, p.C, c, start, 0, state_of(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
+      window_at<IO, K>(x, p.C, c, start, 0, state_ref(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
     }
     const int stop = min(t_end, max(end, t + 1));           // this request's tokens here
     // kConvUnroll tokens' inputs are loaded before any of them is used, so a
@@ -262,7 +282,7 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_final_k(ConvArgs p) {
   if (final_in_forward(start, end, p.tokens_per_block, p.final_in_place)) return;
   float e[K - 1][4];
   window_at<IO, K>(static_cast<const IO*>(p.x), p.C, c, start, end - start,
-                   state_of(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), e);
+                   state_ref(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), e);
   float* fin = state_of(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.C, c, K);
   if (fin != nullptr) store_channel_major<K - 1>(fin, e);
 }
@@ -280,7 +300,7 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_replay_k(ConvReplayArgs
   float* dst = state_of(p.dst, state_slot(p.dst_slots, r, p.num_slots), p.C, c, K);
   if (dst == nullptr) return;                      // no slot to write
   window_at<float, K>(p.capture + (size_t)r * p.capacity * p.C, p.C, c, 0, m,
-                      state_of(p.src, state_slot(p.src_slots, r, p.num_slots), p.C, c, K), e);
+                      state_ref(p.src, state_slot(p.src_slots, r, p.num_slots), p.C, c, K), e);
   store_channel_major<K - 1>(dst, e);
 }
 
