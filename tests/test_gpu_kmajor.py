@@ -88,11 +88,12 @@ def test_kmajor_batched_decode_in_place():
     assert_parity("f16", o, o_ref, M, M_ref, "K-major decode")
 
 
-def test_kmajor_capsule_matches_oracle():
+@pytest.mark.parametrize("Dk,Dv", [(128, 64), (32, 16)])
+def test_kmajor_capsule_matches_oracle(Dk, Dv):
     cap = 4
-    inp = make_inputs([4, 3, 1, 4], 2, 4, 128, 64, "f16", seed=510, capacity=cap)
+    inp = make_inputs([4, 3, 1, 4], 2, 4, Dk, Dv, "f16", seed=510 + Dv, capacity=cap)
     M0 = _m0(inp, 2)
-    _case("K-major capsule fp16 capacity 4")
+    _case(f"K-major capsule fp16 capacity 4 Dk={Dk} Dv={Dv}")
     o, M, su = run_kmajor(inp, M0, plan=gdn.PLAN_RECURRENT, capacity=cap)
     init = np.full(su.shape, -3.0)
     o_ref, M_ref, su_ref = LO.gdn_forward_k_major(*_args(inp), M0.astype(np.float32), state_update_capacity=cap,
@@ -178,5 +179,28 @@ def test_kmajor_pooled_decode():
     o_ref, M_ref, _ = LO.gdn_forward_k_major(*_args(inp), M0)
     got = dpool.cpu().numpy()
     assert_parity("f16", out.float().cpu().numpy(), o_ref, got[wr], M_ref, "K-major pooled")
+    untouched = [s for s in range(P) if s not in set(wr)]
+    assert np.array_equal(got[untouched], pool[untouched])
+
+
+def test_kmajor_pooled_replay():
+    T, R, cap, P = 4, 5, 4, 12
+    inp = make_inputs([T] * R, 2, 4, 64, 32, "f32", seed=560, capacity=cap)
+    rng = np.random.default_rng(8)
+    pool = (rng.standard_normal((P, 4, 64, 32)) * 0.05).astype(np.float32)
+    perm = rng.permutation(P)
+    rd, wr = perm[:R].copy(), perm[R:2 * R].copy()
+    _, _, su = run_kmajor(inp, pool[rd], plan=gdn.PLAN_RECURRENT, capacity=cap, write_final=False)
+    acc_np = np.array([0, 4, 1, 3, 2], np.int32)
+    dpool = dev(pool, torch)
+    _case("K-major pooled replay")
+    gdn.gdn_replay_pooled(dpool, dev(su, torch), dev(acc_np, torch), dpool, num_k_heads=2,
+                          state_update_capacity=cap, read_slots=dev(rd.astype(np.int32), torch),
+                          write_slots=dev(wr.astype(np.int32), torch), read_slots_host=rd, write_slots_host=wr,
+                          accepted_host=acc_np, state_layout=gdn.STATE_K_MAJOR)
+    torch.cuda.synchronize()
+    got = dpool.cpu().numpy()
+    ref = LO.gdn_replay_k_major(pool[rd], su, acc_np, 2, 4, 64, 32)
+    assert rel_max(got[wr], ref) <= 1e-5
     untouched = [s for s in range(P) if s not in set(wr)]
     assert np.array_equal(got[untouched], pool[untouched])
