@@ -257,6 +257,9 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
 // waves' state loads are issued before the staging, so a short segment (the
 // speculative verify) pays one memory latency instead of one per token.
 constexpr int kStageTokens = 16;
+// Smallest decay product the staged recurrence keeps factored out of its
+// registers; below it the product is applied to the state and reset to one.
+constexpr float kMinStateScale = 0x1p-40f;
 
 template <int DK>
 struct StageSmem {
@@ -319,6 +322,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
     ncap = min(t1 - t0, cmax);
   }
 
+  // The registers hold S / gam: a token's decay then folds into gam and the
+  // update is one fused multiply-add per element, S/gam += (u/gam) k^.
+  float gam = 1.f;
   for (int ts = t0; ts < t1; ts += kStageTokens) {
     const int nt = min(kStageTokens, t1 - ts);
     // ---- stage: 16 threads per token normalise k and q and form the gates (a
@@ -377,7 +383,10 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
         kv[4 * jj + 0] = kx.x; kv[4 * jj + 1] = kx.y; kv[4 * jj + 2] = kx.z; kv[4 * jj + 3] = kx.w;
         qv[4 * jj + 0] = qx.x; qv[4 * jj + 1] = qx.y; qv[4 * jj + 2] = qx.z; qv[4 * jj + 3] = qx.w;
       }
-      const float alpha = sm.alpha[j], beta = sm.beta[j], kq = sm.kq[j];
+      const float beta = sm.beta[j], kq = sm.kq[j];
+      // decay of the held state up to and including this token
+      const float gn = gam * sm.alpha[j];
+      const bool keep_scaled = gn >= kMinStateScale;   // uniform over the workgroup
       float pk[NI], pq[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -400,24 +409,41 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
       if constexpr (CAPTURE) {
         if (jcap < ncap) caprow = cap + ((size_t)r * p.capacity + jcap) * p.capsule_width;
       }
+      // the state's scale is reset (one in-place multiply) only when the
+      // product would leave the range where 1/gam is safe
+      const float rgn = keep_scaled ? __builtin_amdgcn_rcpf(gn) : 1.f;
+      float u[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float vv = sm.v[j][row_base + i * RI + rg - block_row0];   // zero past Dv
+        u[i] = beta * (vv - gn * pk[i]);
+      }
+      if (!keep_scaled) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int e = 0; e < E; ++e) S[i][e] *= gn;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float w = u[i] * rgn;
+#pragma unroll
+        for (int e = 0; e < E; ++e) S[i][e] = fmaf(w, kv[e], S[i][e]);
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int row = row_base + i * RI + rg;
-        const float vv = valid[i] ? sm.v[j][row - block_row0] : 0.f;
-        const float u = beta * (vv - alpha * pk[i]);
-        const float o = fmaf(alpha, pq[i], u * kq);
-#pragma unroll
-        for (int e = 0; e < E; ++e) S[i][e] = fmaf(alpha, S[i][e], u * kv[e]);
+        const float o = fmaf(gn, pq[i], u[i] * kq);
         if (valid[i] && c == 0) {
           IoOps<IO>::store1(op + ((size_t)t * p.Hv + h) * Dv + row, o);
           if constexpr (CAPTURE) {
-            if (caprow != nullptr) caprow[p.Hv + p.Hk * DK + h * Dv + row] = u;
+            if (caprow != nullptr) caprow[p.Hv + p.Hk * DK + h * Dv + row] = u[i];
           }
         }
       }
       if constexpr (CAPTURE) {
         if (caprow != nullptr && blk == 0 && wave == 0) {
-          if (lane == 0) caprow[h] = alpha;
+          if (lane == 0) caprow[h] = sm.alpha[j];
           // the shared key is written once per key head, by its first value head
           if (h % p.group == 0 && rg == 0) {
 #pragma unroll
@@ -428,6 +454,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
           }
         }
       }
+      gam = keep_scaled ? gn : 1.f;
     }
     __syncthreads();   // the next group's staging overwrites the staged tokens
   }
@@ -439,7 +466,8 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
       const int row = row_base + i * RI + rg;
 #pragma unroll
       for (int j = 0; j < V4; ++j) {
-        float4_t x = {S[i][4 * j + 0], S[i][4 * j + 1], S[i][4 * j + 2], S[i][4 * j + 3]};
+        float4_t x = {gam * S[i][4 * j + 0], gam * S[i][4 * j + 1], gam * S[i][4 * j + 2],
+                      gam * S[i][4 * j + 3]};
         store_state4(fin + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
       }
     }

@@ -210,6 +210,32 @@ def test_effective_gates_capsule():
     assert rel_max(got[..., sd], ref_cap[..., sd]) <= 1e-3
 
 
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (32, 64)])
+def test_capsule_deep_decay_vs_oracle(Dk, Dv):
+    # decays spread over twelve decades (and exact 0s and 1s) drive the running
+    # product of a segment's decays far below any fixed floor within a few
+    # tokens, so the staged recurrence both keeps it factored out of the state
+    # and folds it back in, many times per segment
+    lengths = [40, 23, 1, 0]
+    cap = max(lengths)
+    inp = make_inputs(lengths, 2, 4, Dk, Dv, "f32", seed=22, capacity=cap)
+    inp = effective_gate_inputs(inp, seed=23)
+    rng = np.random.default_rng(24)
+    alpha = 10.0 ** rng.uniform(-12.0, 0.0, inp["a"].shape)
+    alpha.flat[::7] = 1.0
+    alpha.flat[3::11] = 0.0
+    inp["a"] = alpha.astype(np.float32)
+    _case(f"capsule deep decay Dk={Dk} Dv={Dv} lengths={lengths}")
+    res = run_forward(inp, torch, gdn, gate="none", capacity=cap, poison=-7.0)
+    ref_o, ref_s, ref_cap = oracle_forward(inp, O, gate="none", capacity=cap, poison=-7.0)
+    assert_parity("f32", res["output"], ref_o, res["final_state"], ref_s, "capsule deep decay")
+    got = res["state_update"]
+    for r, L in enumerate(lengths):
+        assert np.all(got[r, L:] == -7.0)
+        if L:
+            assert rel_max(got[r, :L], ref_cap[r, :L]) <= TOL_F32_REL
+
+
 @pytest.mark.parametrize("io,capacity", [("f32", 0), ("f16", 0), ("f16", 4)])
 def test_dense_layout_equals_packed_bitwise(io, capacity):
     inp = make_inputs([5, 5, 5], 2, 4, 128, 64, io, seed=21, capacity=capacity)
