@@ -126,6 +126,11 @@ def run_decode(args, torch, gdn):
     nbytes = decode_bytes(inp)
     achieved = nbytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic("gdn_decode")
+    # context only: single-call times, and one bank reused every step (its 128 MiB
+    # can then stay in the 256 MB Infinity Cache between steps)
+    per_call = _per_call(torch, step, 50, args.warmup + args.steps)
+    hot_ms = _time_steps(torch, lambda i: step(0), 100, 10)
+    hot = {"ms_per_step": hot_ms, "achieved_GBps": nbytes / (hot_ms * 1e-3) / 1e9}
     line = {
         "metric": METRIC, "value": N / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
@@ -138,6 +143,8 @@ def run_decode(args, torch, gdn):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
                      "avg_kernel_us": ms_step * 1e3},
+        "per_call": per_call,
+        "hot_single_bank": hot,
     }
     return line, inp
 
@@ -231,6 +238,24 @@ def _time_steps(torch, step, steps, warmup):
     return ev0.elapsed_time(ev1) / steps
 
 
+def _per_call(torch, step, calls, start):
+    """Distribution of single-call times: `calls` further steps, each bracketed by
+    its own HIP events on the launch stream (after the timed region, not part of it)."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for j, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        step(start + j)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    def quantile(f):
+        return 1e3 * t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]
+
+    return {"calls": calls, "median_us": quantile(0.5), "p10_us": quantile(0.1), "p90_us": quantile(0.9)}
+
+
 def run_verify_replay(args, torch, gdn):
     """Speculative verify (capsule, committed bank read-only) then replay of the
     accepted prefix into the inactive bank, per step."""
@@ -263,13 +288,14 @@ def run_verify_replay(args, torch, gdn):
 
     _log(f"verify+replay: R={R} T=4 Hv={Hv} banks={n_banks}")
     ms = _time_steps(torch, step, args.steps, args.warmup)
+    per_call = _per_call(torch, step, 50, args.warmup + args.steps)   # single-call latency
     io = 2
     verify_bytes = (state_bytes + R * cap * W * 4 + 2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io
                     + 2 * N * Hv * 4 + 2 * Hv * 4 + (R + 1) * 4)
     replay_bytes = 2 * state_bytes + int(acc_host.sum()) * W * 4 + R * 4
     nbytes = verify_bytes + replay_bytes
     achieved = nbytes / (ms * 1e-3) / 1e9
-    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "per_call": per_call,
             "config": {"requests": R, "draft_tokens": 4, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
                        "capacity": cap, "accepted": acc_host.tolist(), "state_banks": n_banks},
             "roofline": {"bound": "hbm", "kernel": "gdn_capsule+gdn_replay", "achieved": achieved,
@@ -324,13 +350,14 @@ def run_spec_step_pooled(args, torch, gdn):
 
     _log(f"pooled verify+replay+publish: R={R} T=4 Hv={Hv} slots={P}")
     ms = _time_steps(torch, step, args.steps, args.warmup)
+    per_call = _per_call(torch, step, 50, args.warmup + args.steps)
     io = 2
     verify_bytes = (state_bytes + R * cap * W * 4 + 2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io
                     + 2 * N * Hv * 4 + 2 * Hv * 4 + (R + 1) * 4 + R * 4)
     replay_bytes = 2 * state_bytes + int(acc_host.sum()) * W * 4 + 3 * R * 4
     nbytes = verify_bytes + replay_bytes + 4 * R * 4
     achieved = nbytes / (ms * 1e-3) / 1e9
-    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "per_call": per_call,
             "config": {"requests": R, "draft_tokens": 4, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
                        "capacity": cap, "accepted": acc_host.tolist(), "pool_slots": P},
             "roofline": {"bound": "hbm", "kernel": "gdn_capsule+gdn_replay+gdn_publish",
@@ -375,12 +402,13 @@ def run_prefill(args, torch, gdn, name):
     warm = max(2, args.warmup // 10)
     _log(f"{name}: N={N} R={R} Hv={Hv} plan={'chunk' if plan == gdn.PLAN_CHUNK else 'recurrent'} steps={steps}")
     ms = _time_steps(torch, step, steps, warm)
+    per_call = _per_call(torch, step, 10, warm + steps)
     flops = prefill_flops(inp["lengths"], Hk, Hv, Dk)
     io = 2
     nbytes = (2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io + 2 * N * Hv * 4 + 2 * Hv * 4
               + (R + 1) * 4 + 2 * R * Hv * Dv * Dk * 4)
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "per_call": per_call,
             "config": {"tokens": N, "requests": R, "lengths": [int(x) for x in inp["lengths"]],
                        "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "chunk": 64, "workspace_bytes": nws},
             "roofline": {"bound": "mfma", "kernel": "gdn_chunk_index+gdn_chunk_prep+gdn_chunk_scan",
