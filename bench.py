@@ -51,8 +51,8 @@ MEASURED_TRAFFIC = {
                    "sha256_16": "cfc0bf9b25b303bd", "fetch_kib": 66995.5, "write_kib": 131599.8,
                    "bytes": 271940698},
     "gdn_decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-                          "sha256_16": "3bc85c1b7e7eb4c0", "fetch_kib": 66440.1, "write_kib": 131675.5,
-                          "bytes": 270880957},
+                          "sha256_16": "94793b2b7224c585", "fetch_kib": 66937.6, "write_kib": 131655.0,
+                          "bytes": 271878664},
 }
 
 

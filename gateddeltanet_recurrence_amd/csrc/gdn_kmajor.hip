@@ -8,16 +8,18 @@
 //   pk = M^T k^, pq = M^T q^,  u = beta (v - alpha pk),  o = alpha pq + u (k^ . q^),
 //   M = alpha M + k^ u^T.
 //
-// Work decomposition (CDNA4, wave64). A wavefront owns a slice of 4 LK value
-// columns of one (request, value head) and all Dk rows of it, in registers for
-// the whole segment: lane l holds the 4 columns 4 (l mod LK) .. +3 (one 16-byte
-// vector, so LK adjacent lanes read a 16 LK-byte run of a row) in rows
-// dk = l / LK + (64 / LK) i. The contraction over dk is then an in-lane sum over
-// the lane's rows followed by a sum over the lanes of equal l mod LK (DPP
-// rotations within each row of 16 lanes, two cross-row exchanges): nothing
-// leaves the wavefront, and the update M = alpha M + k^ u^T is lane-local.
-// LK = 8 (full 128-byte lines per row segment) took the batched decode from
-// 69 us (LK = 4, 64-byte segments) to 51 us.
+// Work decomposition (CDNA4, wave64). A slice of 4 LK value columns of one
+// (request, value head) is held in registers for the whole segment by DKS
+// wavefronts, each with Dk / DKS of its rows: lane l holds the 4 columns
+// 4 (l mod LK) .. +3 (one 16-byte vector, so LK adjacent lanes read a 16 LK-byte
+// run of a row) in rows dk = dk0 + l / LK + (64 / LK) i. The contraction over dk
+// is an in-lane sum over the lane's rows, a sum over the lanes of equal
+// l mod LK (DPP rotations within each row of 16 lanes, two cross-row
+// exchanges), and with DKS = 2 the partner wavefront's partial sums through
+// LDS; the update M = alpha M + k^ u^T is lane-local. LK = 8 (full 128-byte
+// lines per row segment) took the batched decode from 69 us (LK = 4, 64-byte
+// segments) to 51 us; DKS = 2 at Dk = 128 (104 VGPRs, four waves per SIMD,
+// against 150 and three) to 49.5 us.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -64,17 +66,34 @@ template <> struct Io4Store<_Float16> {
   }
 };
 
+// Dk rows of a column slice are split over DKS wavefronts (DKS = 2 at Dk = 128:
+// 32 state floats per lane instead of 64, five waves per SIMD instead of three).
+// The contractions over dk then add the DKS partial sums through LDS, one
+// barrier per token; every wave of a slice forms the same totals (the partner's
+// sum is added to its own, and a + b = b + a exactly).
+template <int DK>
+struct KmajSplit {
+  static constexpr int DKS = DK == 128 ? 2 : 1;
+};
+
 template <typename IO, int DK, bool CAPTURE>
 __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_per_block, int blocks_per_head) {
   constexpr int LK = GDN_KMAJ_LANES;               // lanes per row segment
   constexpr int WD = 4 * LK;                       // value columns per wavefront
   constexpr int RG = 64 / LK;                      // row groups
-  constexpr int NR = DK / RG;                      // rows per lane
+  constexpr int DKS = KmajSplit<DK>::DKS;          // wavefronts per column slice
+  constexpr int NR = DK / DKS / RG;                // rows per lane
+  constexpr int SPB = GDN_KMAJ_WAVES / DKS;        // column slices per workgroup (at most)
   static_assert(NR >= 1, "Dk must cover the row groups");
+  // partial sums pk (4), pq (4), |k|^2, |q|^2, k.q (padded to 12), two token buffers
+  __shared__ float xsum[DKS > 1 ? 2 : 1][SPB][DKS][LK][12];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int cl = lane % LK;                        // column quad within the slice
-  const int rg = lane / LK;                        // row group: rows rg + RG i
+  const int rg = lane / LK;                        // row group: rows rg + RG i of this wave's part
+  const int part = wave % DKS;                     // which dk part of the slice
+  const int sl = wave / DKS;                       // slice within the workgroup
+  const int dk0 = part * (DK / DKS);
 
   int item = blockIdx.x;
   const int blk = item % blocks_per_head;
@@ -83,10 +102,14 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   const int r = item / p.Hv;
   const int g = h / p.group;
   const int Dv = p.Dv;
-  const int slice = blk * waves_per_block + wave;
-  if (slice * WD >= Dv) return;                    // no barrier below: idle waves may leave
+  const int slices_per_block = waves_per_block / DKS;
+  const int slice = blk * slices_per_block + sl;
+  const bool sactive = slice * WD < Dv;            // idle slices still take part in the barriers
+  if constexpr (DKS == 1) {
+    if (!sactive) return;                          // no barrier below: idle waves may leave
+  }
   const int col = slice * WD + 4 * cl;             // first of this lane's 4 columns
-  const bool cvalid = col < Dv;                    // Dv is a multiple of 16, maybe not of WD
+  const bool cvalid = sactive && col < Dv;         // Dv is a multiple of 16, maybe not of WD
 
   const int t0 = seq_start(p, r);
   const int t1 = max(seq_start(p, r + 1), t0);
@@ -98,7 +121,7 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   float4_t M[NR];
   if (init != nullptr && cvalid) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) M[i] = load_state4_nt(init + (size_t)(rg + RG * i) * Dv + col);
+    for (int i = 0; i < NR; ++i) M[i] = load_state4_nt(init + (size_t)(dk0 + rg + RG * i) * Dv + col);
   } else {
 #pragma unroll
     for (int i = 0; i < NR; ++i) M[i] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -120,8 +143,8 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   }
 
   for (int t = t0; t < t1; ++t) {
-    const IO* krow = kp + ((size_t)t * p.Hk + g) * DK;
-    const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK;
+    const IO* krow = kp + ((size_t)t * p.Hk + g) * DK + dk0;
+    const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK + dk0;
     float kv[NR], qv[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -151,6 +174,21 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
     skq = column_sum<LK>(skq);
     pk.x = column_sum<LK>(pk.x); pk.y = column_sum<LK>(pk.y); pk.z = column_sum<LK>(pk.z); pk.w = column_sum<LK>(pk.w);
     pq.x = column_sum<LK>(pq.x); pq.y = column_sum<LK>(pq.y); pq.z = column_sum<LK>(pq.z); pq.w = column_sum<LK>(pq.w);
+    if constexpr (DKS > 1) {
+      static_assert(DKS == 2, "two dk parts");
+      const int buf = (t - t0) & 1;                // the other buffer may still be read by the partner
+      if (rg == 0) {
+        float* d = xsum[buf][sl][part][cl];
+        d[0] = pk.x; d[1] = pk.y; d[2] = pk.z; d[3] = pk.w;
+        d[4] = pq.x; d[5] = pq.y; d[6] = pq.z; d[7] = pq.w;
+        d[8] = ssk; d[9] = ssq; d[10] = skq;
+      }
+      __syncthreads();
+      const float* o = xsum[buf][sl][part ^ 1][cl];
+      pk.x += o[0]; pk.y += o[1]; pk.z += o[2]; pk.w += o[3];
+      pq.x += o[4]; pq.y += o[5]; pq.z += o[6]; pq.w += o[7];
+      ssk += o[8]; ssq += o[9]; skq += o[10];
+    }
     const float rk = rsqrtf(ssk + kNormEps);
     const float rq = rsqrtf(ssq + kNormEps) * p.scale;
     const float alpha = gate_alpha(at, gnone, expA, dtb);
@@ -169,22 +207,22 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
       M[i].x = fmaf(alpha, M[i].x, kh * u.x); M[i].y = fmaf(alpha, M[i].y, kh * u.y);
       M[i].z = fmaf(alpha, M[i].z, kh * u.z); M[i].w = fmaf(alpha, M[i].w, kh * u.w);
     }
-    if (rg == 0 && cvalid) Io4Store<IO>::store(op + ((size_t)t * p.Hv + h) * Dv + col, o);
+    if (part == 0 && rg == 0 && cvalid) Io4Store<IO>::store(op + ((size_t)t * p.Hv + h) * Dv + col, o);
 
     if constexpr (CAPTURE) {
       const int jcap = t - t0;
       if (jcap < ncap) {
         float* caprow = p.state_update + ((size_t)r * p.capacity + jcap) * p.capsule_width;
-        if (rg == 0 && cvalid) {
+        if (part == 0 && rg == 0 && cvalid) {
           float* d = caprow + p.Hv + p.Hk * DK + h * Dv + col;
           d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
         }
         if (slice == 0) {
-          if (lane == 0) caprow[h] = alpha;
+          if (part == 0 && lane == 0) caprow[h] = alpha;
           // the shared key is written once per key head, by its first value head
           if (h % p.group == 0 && cl == 0) {
 #pragma unroll
-            for (int i = 0; i < NR; ++i) caprow[p.Hv + g * DK + rg + RG * i] = kv[i] * rk;
+            for (int i = 0; i < NR; ++i) caprow[p.Hv + g * DK + dk0 + rg + RG * i] = kv[i] * rk;
           }
         }
       }
@@ -193,7 +231,7 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
 
   if (fin != nullptr && cvalid) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) store_state4_nt(fin + (size_t)(rg + RG * i) * Dv + col, M[i]);
+    for (int i = 0; i < NR; ++i) store_state4_nt(fin + (size_t)(dk0 + rg + RG * i) * Dv + col, M[i]);
   }
 }
 
@@ -210,9 +248,12 @@ __global__ void __launch_bounds__(64 * GDN_KMAJ_WAVES) gdn_capsule_kmajor(Recurr
 
 template <typename IO, int DK>
 static hipError_t launch_kmajor_dk(const RecurrentArgs& p, hipStream_t stream) {
+  constexpr int DKS = KmajSplit<DK>::DKS;
+  constexpr int SPB = GDN_KMAJ_WAVES / DKS;
   const int slices = (p.Dv + 4 * GDN_KMAJ_LANES - 1) / (4 * GDN_KMAJ_LANES);
-  const int wpb = slices < GDN_KMAJ_WAVES ? slices : GDN_KMAJ_WAVES;
-  const int bph = (slices + wpb - 1) / wpb;
+  const int spb = slices < SPB ? slices : SPB;
+  const int wpb = spb * DKS;
+  const int bph = (slices + spb - 1) / spb;
   const dim3 grid((unsigned)((size_t)p.R * p.Hv * bph)), block((unsigned)(64 * wpb));
   if (p.state_update != nullptr)
     hipLaunchKernelGGL((gdn_capsule_kmajor<IO, DK>), grid, block, 0, stream, p, wpb, bph);
