@@ -1,0 +1,200 @@
+"""GPU: the hot path captured in HIP graphs (torch.cuda.CUDAGraph) and replayed.
+
+A serving loop captures a decode step, or the speculative step (verify, replay
+of the accepted prefix, publication of the slot arrays), once and replays it.
+Each graph here is replayed several times, with the program's own eager work
+and synchronisations between the replays, and every replay is compared bit for
+bit with the same calls made eagerly from the same starting state (the kernels
+are deterministic: no atomics, fixed reduction order). The calls are given host
+mirrors of cu_seqlens, so nothing in them waits for the device.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gdn_workloads import make_inputs
+from gdn_workloads.conv import make_conv_inputs
+from gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gateddeltanet_recurrence_amd as gdn          # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.lib()                                         # fails loudly if libgdn.so is missing
+
+
+def _case(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+def _i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def _capture(fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _snapshot(tensors):
+    torch.cuda.synchronize()
+    return [t.detach().cpu().clone() for t in tensors]
+
+
+def _same(got, ref, what):
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a, b), f"{what}: tensor {i} differs"
+
+
+def test_decode_steps_graph():
+    # three in-place decode steps per replay over one state bank
+    R, Hk, Hv, D, steps = 8, 4, 8, 128, 3
+    inp = make_inputs([1] * R, Hk, Hv, D, D, "f16", seed=501)
+    d = {n: dev(inp[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    s0 = dev(inp["initial_state"], torch)
+    state = s0.clone()
+    out = torch.empty((R, Hv, D), dtype=torch.float16, device="cuda")
+
+    def run():
+        for _ in range(steps):
+            gdn.gdn_forward(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], d["cu_seqlens"],
+                            out, initial_state=state, final_state=state, cu_seqlens_host=inp["cu_seqlens"],
+                            plan=gdn.PLAN_RECURRENT)
+
+    _case("decode: eager reference")
+    run()
+    ref = _snapshot([state, out])
+    _case("decode: capture")
+    g = _capture(run)
+    for rep in range(3):
+        state.copy_(s0)
+        out.zero_()
+        torch.cuda.synchronize()
+        _case(f"decode: replay {rep}")
+        g.replay()
+        _same(_snapshot([state, out]), ref, f"decode replay {rep}")
+
+
+def test_speculative_step_graph_publishes_on_the_device():
+    # verify from the committed slots, replay the accepted prefix into the
+    # inactive ones, swap the slot arrays: replay k of the graph must equal k
+    # eager steps, since each replay reads the slots the previous one published
+    T, R, cap, Hk, Hv, D = 4, 6, 4, 2, 4, 128
+    inp = make_inputs([T] * R, Hk, Hv, D, D, "f16", seed=502, capacity=cap)
+    P = 2 * R
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(P)
+    committed_np, inactive_np = perm[:R], perm[R:]
+    pool_np = rng.standard_normal((P, Hv, D, D)).astype(np.float32) * 0.05
+    pool_np[committed_np] = inp["initial_state"]
+    accepted = _i32([0, 1, 2, 3, 4, 2])
+    pool0 = dev(pool_np, torch)
+    pool = pool0.clone()
+    committed, inactive = _i32(committed_np), _i32(inactive_np)
+    d = {n: dev(inp[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    out = torch.empty((T * R, Hv, D), dtype=torch.float16, device="cuda")
+    su = torch.zeros((R, cap, gdn.capsule_width(Hk, Hv, D, D)), device="cuda")
+
+    def step():
+        gdn.gdn_forward_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                               d["cu_seqlens"], out, num_slots=P, read_slots=committed, write_slots=None,
+                               initial_state=pool, final_state=None, state_update=su,
+                               state_update_capacity=cap, cu_seqlens_host=inp["cu_seqlens"],
+                               plan=gdn.PLAN_RECURRENT)
+        gdn.gdn_replay_pooled(pool, su, accepted, pool, num_k_heads=Hk, state_update_capacity=cap,
+                              read_slots=committed, write_slots=inactive)
+        gdn.gdn_publish_slots(committed, inactive)
+
+    def reset():
+        pool.copy_(pool0)
+        committed.copy_(_i32(committed_np))
+        inactive.copy_(_i32(inactive_np))
+        out.zero_()
+        su.zero_()
+        torch.cuda.synchronize()
+
+    watched = [pool, committed, inactive, out, su]
+    _case("speculative step: eager reference, 3 steps")
+    refs = []
+    for _ in range(3):
+        step()
+        refs.append(_snapshot(watched))
+    reset()
+    _case("speculative step: capture")
+    g = _capture(step)
+    for trial in range(2):
+        reset()
+        for k in range(3):
+            _case(f"speculative step: trial {trial} replay {k}")
+            g.replay()
+            _same(_snapshot(watched), refs[k], f"trial {trial} replay {k}")
+
+
+def test_chunked_prefill_graph():
+    lengths = [130, 64, 1, 77]
+    Hk, Hv, D = 2, 4, 128
+    inp = make_inputs(lengths, Hk, Hv, D, D, "f16", seed=503)
+    N, R = sum(lengths), len(lengths)
+    d = {n: dev(inp[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    init = dev(inp["initial_state"], torch)
+    fin = torch.empty_like(init)
+    out = torch.empty((N, Hv, D), dtype=torch.float16, device="cuda")
+    nws = gdn.gdn_forward_workspace_bytes(N, R, Hk, Hv, D, D, gdn.GDN_F16, cu_seqlens_host=inp["cu_seqlens"])
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def run():
+        gdn.gdn_forward(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], d["cu_seqlens"], out,
+                        initial_state=init, final_state=fin, cu_seqlens_host=inp["cu_seqlens"], workspace=ws,
+                        plan=gdn.PLAN_CHUNK)
+
+    _case("chunked prefill: eager reference")
+    run()
+    ref = _snapshot([fin, out])
+    _case("chunked prefill: capture")
+    g = _capture(run)
+    for rep in range(3):
+        fin.zero_()
+        out.zero_()
+        ws.zero_()                                     # the workspace carries nothing between calls
+        torch.cuda.synchronize()
+        _case(f"chunked prefill: replay {rep}")
+        g.replay()
+        _same(_snapshot([fin, out]), ref, f"chunked prefill replay {rep}")
+
+
+def test_conv_decode_graph():
+    R, C, K, steps = 16, 2048, 4, 3
+    inp = make_conv_inputs([1] * R, C, K, "f16", seed=504)
+    x = dev(inp["x"], torch)
+    w, b, cu = dev(inp["weight"], torch), dev(inp["bias"], torch), dev(inp["cu_seqlens"], torch)
+    s0 = dev(inp["initial_state"], torch)
+    state = s0.clone()
+    out = torch.empty_like(x)
+
+    def run():
+        for _ in range(steps):
+            gdn.gdn_conv_forward(x, w, b, cu, out, initial_state=state, final_state=state,
+                                 cu_seqlens_host=inp["cu_seqlens"])
+
+    _case("conv decode: eager reference")
+    run()
+    ref = _snapshot([state, out])
+    _case("conv decode: capture")
+    g = _capture(run)
+    for rep in range(3):
+        state.copy_(s0)
+        out.zero_()
+        torch.cuda.synchronize()
+        _case(f"conv decode: replay {rep}")
+        g.replay()
+        _same(_snapshot([state, out]), ref, f"conv decode replay {rep}")
