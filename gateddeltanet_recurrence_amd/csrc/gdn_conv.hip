@@ -27,18 +27,24 @@ constexpr int kConvThreads = kConvBlockThreads;
 constexpr int kConvChannelsPerBlock = 4 * kConvThreads;
 constexpr int kConvUnroll = 8;
 
+// The output is a stream written once: nontemporal stores (ragged prefill
+// 103 -> 86 us). Nontemporal loads of x were slower: a block re-reads the K - 1
+// rows before its first token, which the previous block has just read.
 template <typename IO> struct Io4;
 template <> struct Io4<float> {
   static __device__ __forceinline__ float4_t load(const float* p) { return *reinterpret_cast<const float4_t*>(p); }
-  static __device__ __forceinline__ void store(float* p, float4_t v) { *reinterpret_cast<float4_t*>(p) = v; }
+  static __device__ __forceinline__ void store_stream(float* p, float4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<float4_t*>(p));
+  }
 };
 template <> struct Io4<_Float16> {
   static __device__ __forceinline__ float4_t load(const _Float16* p) {
     const half4_t h = *reinterpret_cast<const half4_t*>(p);
     return float4_t{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
   }
-  static __device__ __forceinline__ void store(_Float16* p, float4_t v) {
-    *reinterpret_cast<half4_t*>(p) = half4_t{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+  static __device__ __forceinline__ void store_stream(_Float16* p, float4_t v) {
+    const half4_t h = half4_t{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    __builtin_nontemporal_store(h, reinterpret_cast<half4_t*>(p));
   }
 };
 
@@ -247,7 +253,7 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
           z = fmaf(w[K - 1][ch], xv[ch], z);
           y[ch] = p.silu ? silu(z) : z;
         }
-        Io4<IO>::store(out + (size_t)(t + u) * p.C + c, float4_t{y[0], y[1], y[2], y[3]});
+        Io4<IO>::store_stream(out + (size_t)(t + u) * p.C + c, float4_t{y[0], y[1], y[2], y[3]});
         const int j = t + u - start;
         if (j >= 0 && j < ncap)
           *reinterpret_cast<float4_t*>(p.state_update + ((size_t)r * p.capacity + j) * p.C + c) = xs[u];
