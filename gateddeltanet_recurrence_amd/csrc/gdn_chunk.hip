@@ -1034,7 +1034,8 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
 
       // ---- A (rows 16 w + l16 of the fp32 LDS matrix; the blocks above the diagonal
       // are never read) and the P fragments of row block w, from one decay factor
-      // per element
+      // per element. T' and P go out by nontemporal stores: the scan reads them
+      // once, well after this workgroup (long prefill 790 -> 778 us)
       {
         const float gr = gs[r], br = bs[r];
         half4_t ph[4];
@@ -1057,7 +1058,7 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (2 * s <= wave)
-            *reinterpret_cast<half8_t*>(Pw + frag_index(wave, s) * 512 + lane * 8) = cat8(ph[2 * s], ph[2 * s + 1]);
+            __builtin_nontemporal_store(cat8(ph[2 * s], ph[2 * s + 1]), reinterpret_cast<half8_t*>(Pw + frag_index(wave, s) * 512 + lane * 8));
       }
       lds_barrier();
 
@@ -1105,7 +1106,7 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
               const int c = frag_col(s, q, j);
               x[j] = (c >> 4) <= wave ? (_Float16)(T[r * AS + c] * bs[c]) : (_Float16)0.f;
             }
-            *reinterpret_cast<half8_t*>(Tw + frag_index(wave, s) * 512 + lane * 8) = x;
+            __builtin_nontemporal_store(x, reinterpret_cast<half8_t*>(Tw + frag_index(wave, s) * 512 + lane * 8));
           }
         }
       }
