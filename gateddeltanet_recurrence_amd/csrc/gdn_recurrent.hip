@@ -418,17 +418,21 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
         const float vv = sm.v[j][row_base + i * RI + rg - block_row0];   // zero past Dv
         u[i] = beta * (vv - gn * pk[i]);
       }
-      if (!keep_scaled) {
+      // the state after the segment's last token is used only as a final state
+      // (the verify asks for none)
+      if (t + 1 < t1 || fin != nullptr) {          // uniform over the workgroup
+        if (!keep_scaled) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
+          for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int e = 0; e < E; ++e) S[i][e] *= gn;
-      }
+            for (int e = 0; e < E; ++e) S[i][e] *= gn;
+        }
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float w = u[i] * rgn;
+        for (int i = 0; i < NI; ++i) {
+          const float w = u[i] * rgn;
 #pragma unroll
-        for (int e = 0; e < E; ++e) S[i][e] = fmaf(w, kv[e], S[i][e]);
+          for (int e = 0; e < E; ++e) S[i][e] = fmaf(w, kv[e], S[i][e]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
