@@ -28,7 +28,7 @@ constexpr int kConvChannelsPerBlock = 4 * kConvThreads;
 constexpr int kConvUnroll = 8;
 
 // The output is a stream written once: nontemporal stores (ragged prefill
-// 103 -> 86 us). Nontemporal loads of x were slower: a block re-reads the K - 1
+// 103 -> 83..90 us). Nontemporal loads of x were slower: a block re-reads the K - 1
 // rows before its first token, which the previous block has just read.
 template <typename IO> struct Io4;
 template <> struct Io4<float> {
