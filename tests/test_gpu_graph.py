@@ -6,7 +6,8 @@ Each graph here is replayed several times, with the program's own eager work
 and synchronisations between the replays, and every replay is compared bit for
 bit with the same calls made eagerly from the same starting state (the kernels
 are deterministic: no atomics, fixed reduction order). The calls are given host
-mirrors of cu_seqlens, so nothing in them waits for the device.
+mirrors of cu_seqlens, so nothing in them waits for the device. The last test
+runs two independent calls on two streams at once.
 """
 from __future__ import annotations
 
@@ -198,3 +199,49 @@ def test_conv_decode_graph():
         _case(f"conv decode: replay {rep}")
         g.replay()
         _same(_snapshot([state, out]), ref, f"conv decode replay {rep}")
+
+
+def test_two_streams_run_independent_calls():
+    # the library keeps no state between calls: a decode on one stream and a
+    # chunked prefill on another, in flight together, each equal their calls made
+    # alone (bit for bit)
+    dec = make_inputs([1] * 16, 4, 8, 128, 128, "f16", seed=505)
+    pre = make_inputs([200, 33], 2, 4, 128, 128, "f16", seed=506)
+    dd = {n: dev(dec[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    pd = {n: dev(pre[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    s_dec0 = dev(dec["initial_state"], torch)
+    s_dec = s_dec0.clone()
+    o_dec = torch.empty((16, 8, 128), dtype=torch.float16, device="cuda")
+    init = dev(pre["initial_state"], torch)
+    fin = torch.empty_like(init)
+    o_pre = torch.empty((233, 4, 128), dtype=torch.float16, device="cuda")
+    nws = gdn.gdn_forward_workspace_bytes(233, 2, 2, 4, 128, 128, gdn.GDN_F16, cu_seqlens_host=pre["cu_seqlens"])
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def decode_steps(stream):
+        for _ in range(4):
+            gdn.gdn_forward(dd["q"], dd["k"], dd["v"], dd["a"], dd["b"], dd["A_log"], dd["dt_bias"],
+                            dd["cu_seqlens"], o_dec, initial_state=s_dec, final_state=s_dec,
+                            cu_seqlens_host=dec["cu_seqlens"], plan=gdn.PLAN_RECURRENT, stream=stream)
+
+    def prefill(stream):
+        gdn.gdn_forward(pd["q"], pd["k"], pd["v"], pd["a"], pd["b"], pd["A_log"], pd["dt_bias"], pd["cu_seqlens"],
+                        o_pre, initial_state=init, final_state=fin, cu_seqlens_host=pre["cu_seqlens"],
+                        workspace=ws, plan=gdn.PLAN_CHUNK, stream=stream)
+
+    _case("two streams: each call alone")
+    decode_steps(None)
+    prefill(None)
+    ref = _snapshot([s_dec, o_dec, fin, o_pre])
+    s_dec.copy_(s_dec0)
+    fin.zero_()
+    o_pre.zero_()
+    torch.cuda.synchronize()
+    _case("two streams: together")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()      # default priority
+    with torch.cuda.stream(sa):
+        decode_steps(sa)
+    with torch.cuda.stream(sb):
+        prefill(sb)
+    torch.cuda.synchronize()
+    _same(_snapshot([s_dec, o_dec, fin, o_pre]), ref, "two streams")
