@@ -42,6 +42,18 @@ def test_chunk_ragged_vs_oracle(Hk, Hv):
     assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, f"chunk G={Hv // Hk}")
 
 
+@pytest.mark.parametrize("host_cu", [True, False])
+def test_chunk_no_tokens_at_all(host_cu):
+    # N = 0 with requests, forced CHUNK: no chunk to prepare, every scan workgroup
+    # walks zero chunks and writes back the initial state (bit for bit); without a
+    # host mirror the workspace is sized by the bound, not by the (zero) count
+    inp = make_inputs([0, 0, 0], 2, 4, 128, 128, "f16", seed=52)
+    _case(f"chunk no tokens host_cu={host_cu}")
+    res = run_forward(inp, torch, gdn, plan=gdn.PLAN_CHUNK, host_cu=host_cu)
+    assert res["output"].shape[0] == 0
+    assert np.array_equal(res["final_state"], inp["initial_state"])
+
+
 def test_chunk_matches_forced_recurrent():
     inp = make_inputs([300, 64, 129], 2, 4, 128, 128, "f16", seed=41)
     _case("chunk vs recurrent")

@@ -116,6 +116,19 @@ def test_empty_segments_copy_state():
         assert np.array_equal(res["final_state"][r], inp["initial_state"][r])
 
 
+@pytest.mark.parametrize("io,capacity", [("f32", 0), ("f16", 4)])
+def test_no_tokens_at_all(io, capacity):
+    # N = 0 with requests: every segment is empty, so the final state is the
+    # initial one (bit for bit) and, with a capsule, no capsule row is written
+    inp = make_inputs([0, 0, 0], 2, 4, 128, 64, io, seed=12, capacity=capacity)
+    _case(f"no tokens {io} capacity={capacity}")
+    res = run_forward(inp, torch, gdn, capacity=capacity, poison=-7.0)
+    assert res["output"].shape[0] == 0
+    assert np.array_equal(res["final_state"], inp["initial_state"])
+    if capacity:
+        assert np.all(res["state_update"] == -7.0)
+
+
 def test_bf16_rejected_without_writes():
     inp = make_inputs([2], 1, 1, 16, 16, "f32", seed=12)
     _case("bf16 rejected")
