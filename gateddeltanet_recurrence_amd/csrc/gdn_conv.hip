@@ -13,9 +13,12 @@
 // packed tokens with the last K - 1 inputs of each channel in registers; a block
 // may cross request boundaries, where the window restarts from the next
 // request's carried state. Blocks are independent, so long sequences spread
-// over the whole chip. The final state is written by a second kernel that runs
-// after the convolution, which keeps an in-place update (final_state ==
-// initial_state) race-free.
+// over the whole chip. The workgroup that convolves a request's last token
+// writes that request's final state from its window. An in-place update
+// (final_state == initial_state) is race-free that way only when the request's
+// tokens all fall in that one workgroup; in-place requests that span
+// workgroups, and empty requests, are written by a small final-state kernel
+// that runs after the convolution.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 

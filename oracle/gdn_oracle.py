@@ -173,8 +173,14 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
     [R, capacity, W] or None).
 
     With a capacity, request r captures its leading
-    n_r = min(len_r, capture_count[r] if given else capacity) tokens; capsule
-    rows from n_r on keep the values of state_update_init (zeros by default).
+    n_r = min(len_r, c_r) tokens, c_r being capture_count[r] clamped to
+    [0, capacity], or capacity when no counts are given; capsule rows from n_r
+    on keep the values of state_update_init (zeros by default). The clamp
+    follows the compact capture contract of the causal convolution commit
+    embedded in "[CUDA] Add compact GatedDeltaNet operator" (Description: an
+    optional per-request capture_count within a bounded capacity; Validation:
+    capture-count requirements and capacity bounds), read the same way for the
+    GatedDeltaNet capsule.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -206,8 +212,8 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
         out[t0:t1] = o
         final[r] = S
         if cap > 0:
-            n = min(t1 - t0, cap if capture_count is None else int(capture_count[r]))
-            n = max(n, 0)
+            c_r = cap if capture_count is None else min(max(int(capture_count[r]), 0), cap)
+            n = min(t1 - t0, c_r)
             unit_k = l2normalize(k[t0:t0 + n])                   # [n, Hk, Dk]
             for j in range(n):
                 capsule[r, j, s_alpha] = alpha[t0 + j]
@@ -219,19 +225,25 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
 def gdn_replay(src_state, state_update, accepted, Hk, Hv, Dk, Dv):
     """Advance the committed state by an accepted capsule prefix.
 
-    dst[r, h] = src[r, h]; then for j < accepted[r]:
+    dst[r, h] = src[r, h]; then for j < m_r:
     dst[r, h] <- alpha_j[h] * dst[r, h] + u_j[h] k^_j[g(h)]^T.
     ("Replay compact fixed state for hybrid decoding", Summary: replay only an
-    accepted prefix into an inactive state bank.)
+    accepted prefix into an inactive state bank.) m_r is accepted[r] clamped
+    to [0, capacity], capacity being the number of capsule rows: a replay never
+    reads past the rows a request owns (the capacity bound of the compact
+    capture contract in "[CUDA] Add compact GatedDeltaNet operator", embedded
+    causal convolution commit, Validation).
     """
     src = np.asarray(src_state, np.float64)
     cap_rows = np.asarray(state_update, np.float64)
     R = src.shape[0]
+    capacity = cap_rows.shape[1]
     s_alpha, s_key, s_delta = capsule_sections(Hk, Hv, Dk, Dv)
     g = key_head_index(Hk, Hv)
     dst = np.array(src, copy=True)
     for r in range(R):
-        for j in range(int(accepted[r])):
+        m = min(max(int(accepted[r]), 0), capacity)
+        for j in range(m):
             row = cap_rows[r, j]
             al = row[s_alpha]                                   # [Hv]
             kk = row[s_key].reshape(Hk, Dk)[g]                  # [Hv, Dk]

@@ -132,6 +132,40 @@ def sample_heads_inputs(inp, heads):
     return sub
 
 
+def _oracle_heads_task(sub):
+    """Worker of oracle_forward_all_heads: the float64 recurrence on one head group."""
+    from oracle import gdn_oracle as O
+    out, fin, _ = O.gdn_forward(sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], sub["A_log"],
+                                sub["dt_bias"], sub["cu_seqlens"], sub["initial_state"])
+    return out, fin
+
+
+def oracle_forward_all_heads(inp, heads_per_task=4, workers=None):
+    """The float64 recurrence over every value head of a large workload, split into
+    groups of heads (sample_heads_inputs) that run in parallel worker processes.
+    The workers are started fresh (spawn) and compute on the CPU only. Returns
+    (output [N, Hv, Dv], final_state [R, Hv, Dv, Dk]) assembled in head order."""
+    import multiprocessing as mp
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+
+    Hv = inp["Hv"]
+    groups = [list(range(h, min(h + heads_per_task, Hv))) for h in range(0, Hv, heads_per_task)]
+    if workers is None:
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), len(groups)))
+    subs = [sample_heads_inputs(inp, hs) for hs in groups]
+    N, _, Dv = inp["v"].shape
+    R = len(inp["cu_seqlens"]) - 1
+    Dk = inp["q"].shape[2]
+    out = np.zeros((N, Hv, Dv))
+    fin = np.zeros((R, Hv, Dv, Dk))
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        for hs, (o, f) in zip(groups, ex.map(_oracle_heads_task, subs)):
+            out[:, hs] = o
+            fin[:, hs] = f
+    return out, fin
+
+
 def assert_parity(io_dtype, out, ref_out, fin=None, ref_fin=None, what=""):
     if io_dtype == "f32":
         e_o = rel_max(out, ref_out)

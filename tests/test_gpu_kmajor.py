@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 import gateddeltanet_recurrence_amd as gdn          # noqa: E402
+from oracle import gdn_oracle as GO                  # noqa: E402
 from oracle import layout_oracle as LO               # noqa: E402
 
 
@@ -103,7 +104,15 @@ def test_kmajor_capsule_matches_oracle(Dk, Dv):
     lengths = np.diff(inp["cu_seqlens"])
     for r, n in enumerate(lengths):
         assert np.all(su[r, n:] == -3.0)
-    assert rel_max(su, su_ref) <= 2e-3
+    # per section, as for the V-major capsule: decay and unit key are computed
+    # from the inputs alone (1e-5); the deltas depend on the state as the outputs
+    # do (1e-3 on their scale, FP16 inputs)
+    sa, sk, sd = GO.capsule_sections(inp["Hk"], inp["Hv"], Dk, Dv)
+    rows = np.concatenate([[(r, j) for j in range(n)] for r, n in enumerate(lengths) if n]).astype(int)
+    got, ref = su[rows[:, 0], rows[:, 1]], su_ref[rows[:, 0], rows[:, 1]]
+    assert rel_max(got[:, sa], ref[:, sa]) <= 1e-5
+    assert rel_max(got[:, sk], ref[:, sk]) <= 1e-5
+    assert rel_max(got[:, sd], ref[:, sd]) <= 1e-3
 
 
 def test_kmajor_chunk_prefill():

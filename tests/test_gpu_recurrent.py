@@ -279,12 +279,20 @@ def test_dense_rank4_tensors_through_the_binding():
 
 
 def test_capture_count_clamped_to_capacity():
-    inp = make_inputs([6, 6], 1, 1, 16, 16, "f32", seed=14, capacity=3)
-    cc = np.array([99, -5], np.int32)
-    _case("capture_count clamped")
+    # counts beyond capacity capture capacity rows, negative counts none; the
+    # values are the oracle's, which clamps the same way (a pinned reading)
+    inp = make_inputs([6, 6, 2], 1, 2, 16, 16, "f32", seed=14, capacity=3)
+    cc = np.array([99, -5, 99], np.int32)
+    _case("capture_count clamped [99, -5, 99] at capacity 3")
     res = run_forward(inp, torch, gdn, capacity=3, capture_count=cc, poison=-7.0)
-    assert np.all(res["state_update"][0] != -7.0)
-    assert np.all(res["state_update"][1] == -7.0)
+    ref_o, ref_s, ref_cap = oracle_forward(inp, O, capacity=3, capture_count=cc, poison=-7.0)
+    assert_parity("f32", res["output"], ref_o, res["final_state"], ref_s, "clamped capture")
+    got = res["state_update"]
+    for r, n in enumerate([3, 0, 2]):
+        assert np.all(got[r, n:] == -7.0), r                    # bit-exact: untouched
+        assert np.all(ref_cap[r, n:] == -7.0), r
+        if n:
+            assert rel_max(got[r, :n], ref_cap[r, :n]) <= TOL_F32_REL
 
 
 # ----------------------------------------------------------------- replay
@@ -334,6 +342,23 @@ def test_replay_every_prefix_length(m):
     assert rel_max(dst, ref) <= TOL_REPLAY_REL
     if m == 0:
         assert np.array_equal(dst, inp["initial_state"])
+
+
+def test_replay_clamps_device_accepted_without_mirror():
+    # no host mirror: the kernel clamps accepted to [0, capacity] itself (a bounds
+    # check in the kernel; -3 replays nothing, cap + 5 replays the capacity rows)
+    cap, Hk, Hv, Dk, Dv = 4, 2, 4, 128, 64
+    inp = make_inputs([4, 4, 4], Hk, Hv, Dk, Dv, "f16", seed=17, capacity=cap)
+    _case("replay device accepted [-3, 9, 2], no host mirror")
+    verify = run_forward(inp, torch, gdn, capacity=cap, write_final=False)
+    acc = np.array([-3, cap + 5, 2], np.int32)
+    dst = _replay(inp["initial_state"], verify["state_update"], acc, Hk, cap, accepted_host=False)
+    ref = O.gdn_replay(inp["initial_state"], verify["state_update"], acc, Hk, Hv, Dk, Dv)
+    assert rel_max(dst, ref) <= TOL_REPLAY_REL
+    assert np.array_equal(dst[0], inp["initial_state"][0])           # clamped to 0: a copy
+    # the capacity rows replayed equal the GPU's own recurrence over those tokens
+    own = run_forward(inp, torch, gdn, plan=gdn.PLAN_RECURRENT)
+    assert rel_max(dst[1], own["final_state"][1]) <= TOL_REPLAY_REL
 
 
 def test_replay_rejects_accepted_beyond_capacity():

@@ -164,3 +164,29 @@ def test_capsule_section_order_is_caught(monkeypatch):
                 slice(Hv + Hk * Dk, Hv + Hk * Dk + Hv * Dv))
     monkeypatch.setattr(O, "capsule_sections", sections)
     assert _any_check_fails()
+
+
+def test_replay_reading_past_capacity_is_caught(monkeypatch):
+    # accepted taken as given: the replay reads rows the request does not own
+    real = O.gdn_replay
+
+    def replay(src_state, state_update, accepted, Hk, Hv, Dk, Dv):
+        su = np.asarray(state_update, float)
+        acc = np.asarray(accepted)
+        grown = np.concatenate([su, np.zeros((su.shape[0], int(max(acc.max(), 0)), su.shape[2]))], axis=1)
+        return real(src_state, grown, acc, Hk, Hv, Dk, Dv)
+    monkeypatch.setattr(O, "gdn_replay", replay)
+    assert "check_replay_accepted_clamp" in _any_check_fails()
+
+
+def test_capture_count_without_clamp_is_caught(monkeypatch):
+    # a negative count read as "capture everything"
+    real = O.gdn_forward
+
+    def forward(*args, capture_count=None, **kw):
+        if capture_count is not None:
+            cap = kw.get("state_update_capacity", 0)
+            capture_count = np.where(np.asarray(capture_count) < 0, cap, capture_count)
+        return real(*args, capture_count=capture_count, **kw)
+    monkeypatch.setattr(O, "gdn_forward", forward)
+    assert "check_capture_count_clamp" in _any_check_fails()

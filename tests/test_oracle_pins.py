@@ -309,6 +309,74 @@ def test_replay_prefix():
     check_replay_prefix()
 
 
+def check_capture_count_clamp():
+    """capture_count beyond capacity captures capacity rows; below zero, none.
+
+    The capture contract of the compact causal convolution ("[CUDA] Add compact
+    GatedDeltaNet operator", embedded commit, Validation: capture-count
+    requirements and capacity bounds), read the same way for the capsule. Rows
+    are checked against the Householder brute force, not against the oracle."""
+    Hk, Hv, Dk, Dv, cap = 1, 2, 6, 4, 3
+    lengths = [6, 6, 2, 5]
+    inp = _tiny(lengths, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, seed=29, capacity=cap)
+    R = len(lengths)
+    W = O.capsule_width(Hk, Hv, Dk, Dv)
+    poison = np.full((R, cap, W), -7.25)
+    counts = np.array([99, -5, 99, 2])
+    _, _, capsule = _forward(inp, state_update_capacity=cap, capture_count=counts,
+                             state_update_init=poison)
+    _, _, full = _forward(inp, state_update_capacity=cap, state_update_init=poison)
+    alpha, beta = bf.closed_form_gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    q, k, v = (inp[n].astype(np.float64) for n in ("q", "k", "v"))
+    cu = inp["cu_seqlens"]
+    expect_rows = [3, 0, 2, 2]                       # min(len, clamp(count, 0, cap))
+    for r in range(R):
+        t0, t1 = cu[r], cu[r + 1]
+        n = expect_rows[r]
+        assert np.all(capsule[r, n:] == -7.25)      # nothing past n_r, nothing at all for -5
+        for h in range(Hv):
+            _, _, deltas = bf.transition_form(q[t0:t1, 0], k[t0:t1, 0], v[t0:t1, h], alpha[t0:t1, h],
+                                              beta[t0:t1, h], inp["initial_state"][r, h].astype(np.float64),
+                                              1.0 / math.sqrt(Dk))
+            d0 = Hv + Hk * Dk + h * Dv
+            for j in range(n):
+                assert _rel(capsule[r, j, d0:d0 + Dv], deltas[j]) < TIGHT
+                assert abs(capsule[r, j, h] - alpha[t0 + j, h]) <= 1e-13 * alpha[t0 + j, h]
+    # a count of 99 is the same capture as no counts at all (capacity rows)
+    assert np.array_equal(capsule[0], full[0]) and np.array_equal(capsule[2], full[2])
+
+
+def test_capture_count_clamp():
+    check_capture_count_clamp()
+
+
+def check_replay_accepted_clamp():
+    """accepted beyond capacity replays the capacity rows; below zero, none (a copy).
+
+    Checked against the recurrence run on the clamped prefix of each request
+    (P-9) and, for the copy, against the committed state itself."""
+    Hk, Hv, Dk, Dv, cap = 1, 2, 6, 4, 3
+    lengths = [5, 4, 3]
+    inp = _tiny(lengths, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, seed=30, capacity=cap)
+    _, _, capsule = _forward(inp, state_update_capacity=cap)
+    cu = inp["cu_seqlens"]
+    accepted = np.array([99, -3, 3])
+    dst = O.gdn_replay(inp["initial_state"], capsule, accepted, Hk, Hv, Dk, Dv)
+    m = [3, 0, 3]
+    sub = dict(inp)
+    idx = np.concatenate([np.arange(cu[r], cu[r] + m[r]) for r in range(len(lengths))]).astype(int)
+    for name in ("q", "k", "v", "a", "b"):
+        sub[name] = inp[name][idx]
+    sub["cu_seqlens"] = cu_from_lengths(m)
+    _, fin_m, _ = _forward(sub)
+    assert _rel(dst, fin_m) < TIGHT
+    assert np.array_equal(dst[1], inp["initial_state"][1].astype(np.float64))
+
+
+def test_replay_accepted_clamp():
+    check_replay_accepted_clamp()
+
+
 # ----------------------------------------------- P-10 packing invariance
 def check_packing_invariance():
     with open(os.path.join(GOLDEN, "ragged_prompt_lengths.json")) as f:
@@ -396,7 +464,7 @@ ALL_CHECKS = [
     check_gate_closed_form, check_normalisation, check_frozen_state, check_decay_only,
     check_exact_write, check_transition_form, check_materialised_form,
     check_chunked_equals_recurrent, check_capsule_layout, check_replay_prefix,
-    check_packing_invariance, check_gqa,
+    check_packing_invariance, check_gqa, check_capture_count_clamp, check_replay_accepted_clamp,
 ]
 
 
