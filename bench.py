@@ -40,12 +40,13 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "GDN tokens/s + achieved HBM GB/s (decode/replay), MFMA % (prefill)"
 BANK_TARGET_BYTES = 512 * 2 ** 20
 
-# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs of this workload (KiB per dispatch), each scaled by what the same
-# counter reads for the 128 MiB hbm_copy workload (FETCH_SIZE reads 65547.6 KiB
-# for 131072 KiB copied: factor 1.9996; WRITE_SIZE is exact: factor 1.0000).
-# Keyed by the hash of the kernel's sources: a changed kernel reports null until
-# its counters are taken again.
+# HBM traffic per launch (per step for workloads of several kernels), from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE runs of that workload (KiB per dispatch, summed over
+# the step's kernels), each scaled by what the same counter reads for the 128 MiB
+# hbm_copy workload (FETCH_SIZE reads 65547.6 KiB for 131072 KiB copied: factor
+# 1.9996; WRITE_SIZE is exact: factor 1.0000). Keyed by the hash of the kernels'
+# sources: a changed kernel reports null until its counters are taken again.
+_KSRC = ["gateddeltanet_recurrence_amd/csrc/gdn_common.h", "gateddeltanet_recurrence_amd/csrc/gdn_kernels.h"]
 MEASURED_TRAFFIC = {
     "gdn_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
                    "sha256_16": "07d238522b060041", "fetch_kib": 66995.5, "write_kib": 131599.9,
@@ -142,7 +143,7 @@ def run_decode(args, torch, gdn):
         "roofline": {"bound": "hbm", "kernel": "gdn_decode", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "avg_kernel_us": ms_step * 1e3},
+                     "event_us_per_launch": ms_step * 1e3},
         "per_call": per_call,
         "hot_single_bank": hot,
     }
@@ -184,7 +185,8 @@ def run_decode_effective_dense(args, torch, gdn):
                        "gates": "effective (activation none)", "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv},
             "roofline": {"bound": "hbm", "kernel": "gdn_decode", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_step": nbytes}}
+                         "traffic": measured_traffic("decode_effective_dense"),
+                         "algorithmic_bytes_per_step": nbytes}}
 
 
 def run_decode_kmajor(args, torch, gdn):
@@ -300,7 +302,7 @@ def run_verify_replay(args, torch, gdn):
                        "capacity": cap, "accepted": acc_host.tolist(), "state_banks": n_banks},
             "roofline": {"bound": "hbm", "kernel": "gdn_capsule+gdn_replay", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_step": nbytes,
+                         "traffic": measured_traffic("spec_verify_replay"), "algorithmic_bytes_per_step": nbytes,
                          "verify_bytes": verify_bytes, "replay_bytes": replay_bytes}}
 
 
@@ -362,14 +364,29 @@ def run_spec_step_pooled(args, torch, gdn):
                        "capacity": cap, "accepted": acc_host.tolist(), "pool_slots": P},
             "roofline": {"bound": "hbm", "kernel": "gdn_capsule+gdn_replay+gdn_publish",
                          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("spec_step_pooled"),
                          "algorithmic_bytes_per_step": nbytes}}
 
 
 def prefill_flops(lengths, Hk, Hv, D, chunk=64):
-    """Algorithmic MFMA flops of the chunked prefill: per chunk of L tokens,
-    Hk * 4 L^2 D (Q K^T and K K^T per key head) + Hv * (6 L^2 D + 6 L D^2)
-    (the WY products and the three state contractions per value head)."""
+    """MFMA flops of the chunked prefill as the method computes it: per chunk of L
+    tokens, Hk * 4 L^2 D (Q K^T and K K^T, once per key head) + Hv * (4 L^2 D +
+    6 L D^2) per value head: U = T' (V - e^g rk X) and P U (two L x L x D
+    products) and the three state contractions K S0^T, Q S0^T and U^T K (the
+    reassociated WY form never forms W = T K). Triangular products count as full
+    L x L; the fp32 triangular inverse (about 2 % more) is not counted."""
+    total = 0
+    for n in lengths:
+        for c0 in range(0, int(n), chunk):
+            L = min(chunk, int(n) - c0)
+            total += Hk * 4 * L * L * D + Hv * (4 * L * L * D + 6 * L * D * D)
+    return total
+
+
+def prefill_flops_wy3(lengths, Hk, Hv, D, chunk=64):
+    """The same count with all three L^2 D WY products per value head (W = T K
+    formed explicitly), Hk 4 L^2 D + Hv (6 L^2 D + 6 L D^2) per chunk: reported
+    beside the executed count for comparison with that convention."""
     total = 0
     for n in lengths:
         for c0 in range(0, int(n), chunk):
@@ -404,6 +421,7 @@ def run_prefill(args, torch, gdn, name):
     ms = _time_steps(torch, step, steps, warm)
     per_call = _per_call(torch, step, 10, warm + steps)
     flops = prefill_flops(inp["lengths"], Hk, Hv, Dk)
+    flops_wy3 = prefill_flops_wy3(inp["lengths"], Hk, Hv, Dk)
     io = 2
     nbytes = (2 * N * Hk * Dk * io + 2 * N * Hv * Dv * io + 2 * N * Hv * 4 + 2 * Hv * 4
               + (R + 1) * 4 + 2 * R * Hv * Dv * Dk * 4)
@@ -413,9 +431,10 @@ def run_prefill(args, torch, gdn, name):
                        "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "chunk": 64, "workspace_bytes": nws},
             "roofline": {"bound": "mfma", "kernel": "gdn_chunk_index+gdn_chunk_prep+gdn_chunk_scan",
                          "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                         "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": measured_traffic(name),
                          "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": nbytes,
-                         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+                         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "frac_three_wy_products": flops_wy3 / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}}
 
 
 # ------------------------------------------------------- causal convolution
@@ -503,7 +522,7 @@ def run_conv(args, torch, gdn, name):
                        "timing": timing},
             "roofline": {"bound": "hbm", "kernel": "gdn_conv_forward", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_step": nbytes}}
+                         "traffic": measured_traffic(name), "algorithmic_bytes_per_step": nbytes}}
 
 
 def run_hbm_copy(args, torch):
@@ -524,29 +543,6 @@ def run_hbm_copy(args, torch):
                          "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
 
 
-def cpu_baseline_decode(inp, seconds):
-    """The float64 oracle as it stands, on this host: consecutive decode steps of
-    the same workload, each starting from the previous step's final state."""
-    from threadpoolctl import threadpool_limits
-    from oracle import gdn_oracle as O
-    state = inp["initial_state"].astype(np.float64)
-    n_steps = 0
-    N = inp["q"].shape[0]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            _, state, _ = O.gdn_forward(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
-                                        inp["dt_bias"], inp["cu_seqlens"], state)
-            n_steps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    return {"value": n_steps * N / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_steps} consecutive decode steps of the batched_decode workload "
-                      f"({N} tokens each) in {el:.1f} s, numpy float64, 1 thread; host has "
-                      f"{os.cpu_count()} logical CPUs"}
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -557,8 +553,8 @@ def main():
                              "decode_effective_dense", "conv_prefill", "conv_decode",
                              "spec_step_pooled", "decode_kmajor", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="length of the oracle CPU-baseline sample (0 skips it)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="length of each oracle CPU-baseline sample (0 skips them)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -598,8 +594,17 @@ def main():
             "decode_kmajor": run_decode_kmajor(args, torch, gdn),
         }
     if args.cpu_seconds > 0:
-        _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)
+        from gdn_workloads import workload_inputs
+        _log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s per workload")
+        from oracle.cpu_baseline import cpu_baseline
+        line["cpu_baseline"] = cpu_baseline(inp, "decode", args.cpu_seconds)
+        if args.workload == "all":
+            wl = line["workloads"]
+            wl["spec_verify_replay"]["cpu_baseline"] = cpu_baseline(
+                workload_inputs("spec_verify_replay"), "verify_replay", args.cpu_seconds)
+            for name in ("ragged_prefill", "long_prefill"):
+                wl[name]["cpu_baseline"] = cpu_baseline(workload_inputs(name), "prefill", args.cpu_seconds,
+                                                        max_tokens=8192)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

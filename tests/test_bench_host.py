@@ -6,7 +6,8 @@ more than one GPU.
 Expected values are written out from the definitions: the decode moves the FP32
 state once each way plus q, k, v, output, gates and cu_seqlens; the prefill
 counts, per chunk of L tokens, Hk 4 L^2 D for Q K^T and K K^T per key head and
-Hv (6 L^2 D + 6 L D^2) per value head.
+Hv (4 L^2 D + 6 L D^2) per value head (two L x L products and three state
+contractions), and beside it the count with a third L x L product.
 """
 from __future__ import annotations
 
@@ -40,7 +41,10 @@ def test_decode_bytes_of_the_batched_decode(bench):
 def test_prefill_flops_per_chunk(bench):
     Hk, Hv, D = 16, 48, 128
 
-    def chunk(L):
+    def chunk(L):        # executed: Q K^T, K K^T per key head; T'Z, PU and 3 state products per value head
+        return Hk * 4 * L * L * D + Hv * (4 * L * L * D + 6 * L * D * D)
+
+    def chunk_wy3(L):    # with W = T K formed as well
         return Hk * 4 * L * L * D + Hv * (6 * L * L * D + 6 * L * D * D)
 
     assert bench.prefill_flops([64], Hk, Hv, D) == chunk(64)
@@ -48,7 +52,8 @@ def test_prefill_flops_per_chunk(bench):
     assert bench.prefill_flops([65, 1], Hk, Hv, D) == chunk(64) + 2 * chunk(1)
     assert bench.prefill_flops([0], Hk, Hv, D) == 0
     # the long prefill: 512 chunks of 64
-    assert bench.prefill_flops([32768], Hk, Hv, D) == 512 * chunk(64) == 249_108_103_168
+    assert bench.prefill_flops([32768], Hk, Hv, D) == 512 * chunk(64) == 223_338_299_392
+    assert bench.prefill_flops_wy3([32768], Hk, Hv, D) == 512 * chunk_wy3(64) == 249_108_103_168
 
 
 def test_conv_bytes(bench):
@@ -75,3 +80,13 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
     assert r.stdout.strip() == "" or not r.stdout.strip().startswith("{")   # no JSON line
+
+
+def test_cpu_baseline_times_the_oracle_on_every_head():
+    # a tiny workload, two worker processes: the slowest head group sets the rate
+    from gdn_workloads import make_inputs
+    from oracle.cpu_baseline import cpu_baseline
+    inp = make_inputs([3, 5], 1, 4, 8, 8, "f32", seed=3)
+    res = cpu_baseline(inp, "prefill", 0.05)
+    assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
+    assert 1 <= res["cores"] <= 4 and "4 value heads" in res["sample"]
