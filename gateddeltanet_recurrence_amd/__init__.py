@@ -11,10 +11,10 @@ from .binding import (  # noqa: F401
     GDN_F32, GDN_F16, GDN_BF16, RULE_GATED_DELTA, GATE_RAW, GATE_NONE, ABI_VERSION,
     STATE_V_MAJOR, STATE_K_MAJOR,
     GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIAS, GDN_ERR_CAPACITY,
-    GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP, GdnParams, GdnTensors,
+    GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP, GDN_ERR_SCRATCH, GdnParams, GdnTensors,
     lib, library_path, gdn_abi_version, gdn_strerror, gdn_forward, gdn_forward_workspace_bytes,
     gdn_resolve_plan, gdn_replay, capsule_width, make_params,
     CONV_SILU, CONV_NONE, GdnConvParams, GdnConvTensors, gdn_conv_forward, gdn_conv_replay,
     GdnSlots, gdn_forward_pooled, gdn_replay_pooled, gdn_conv_forward_pooled, gdn_conv_replay_pooled,
-    gdn_publish_slots,
+    gdn_publish_slots, gdn_forward_no_alloc, NO_ALLOC_SCRATCH_BYTES,
 )

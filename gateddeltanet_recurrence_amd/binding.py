@@ -16,12 +16,14 @@ _LIB_NAME = "libgdn.so"
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIAS = 0, 1, 2, 3, 4
 GDN_ERR_CAPACITY, GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP = 5, 6, 7, 8, 9
+GDN_ERR_SCRATCH = 10
+NO_ALLOC_SCRATCH_BYTES = 128 << 20   # GDN_NO_ALLOC_SCRATCH_BYTES
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA = 0
 GATE_RAW, GATE_NONE = 0, 1
 STATE_V_MAJOR, STATE_K_MAJOR = 0, 1
-ABI_VERSION = 3          # the struct layouts below match this version of include/gdn.h
+ABI_VERSION = 4          # the struct layouts below match this version of include/gdn.h
 CONV_SILU, CONV_NONE = 0, 1
 
 
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_forward.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), vp,
                                   ctypes.c_size_t, vp]
         L.gdn_forward.restype = ctypes.c_int
+        L.gdn_forward_no_alloc.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), vp]
+        L.gdn_forward_no_alloc.restype = ctypes.c_int
         L.gdn_forward_workspace_bytes.argtypes = [ctypes.POINTER(GdnParams), vp,
                                                   ctypes.POINTER(ctypes.c_size_t)]
         L.gdn_forward_workspace_bytes.restype = ctypes.c_int
@@ -225,6 +229,15 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, **kw) -> int:
     return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, **kw)
 
 
+def gdn_forward_no_alloc(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, **kw) -> int:
+    """gdn_forward_no_alloc of include/gdn.h: gdn_forward whose workspace is the
+    library's static scratch array on the current GPU (no workspace argument).
+    Keywords as _forward, without workspace."""
+    if kw.get("workspace") is not None:
+        raise ValueError("gdn_forward_no_alloc takes no workspace")
+    return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, no_alloc=True, **kw)
+
+
 def gdn_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, num_slots: int,
                        read_slots=None, write_slots=None, read_slots_host=None,
                        write_slots_host=None, **kw) -> int:
@@ -241,7 +254,8 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
              scale: float = 0.0, chunk: int = 0, state_update_capacity: int = 0,
              plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA,
              gate_activation: int = GATE_RAW, num_reqs: Optional[int] = None, workspace=None,
-             stream=None, check: bool = True, pool=None, state_layout: int = STATE_V_MAJOR) -> int:
+             stream=None, check: bool = True, pool=None, state_layout: int = STATE_V_MAJOR,
+             no_alloc: bool = False) -> int:
     """One forward call on torch tensors; returns the status code.
 
     q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32 (for the
@@ -300,7 +314,11 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
     tens = GdnTensors(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                       _ptr(cu_seqlens), host_cu_ptr, _ptr(initial_state), _ptr(final_state),
                       _ptr(output), _ptr(state_update), _ptr(capture_count))
-    if pool is None:
+    where = "gdn_forward_pooled" if pool is not None else "gdn_forward"
+    if no_alloc:
+        where = "gdn_forward_no_alloc"
+        st = lib().gdn_forward_no_alloc(ctypes.byref(params), ctypes.byref(tens), _stream_handle(stream))
+    elif pool is None:
         st = lib().gdn_forward(ctypes.byref(params), ctypes.byref(tens), ws_ptr,
                                ctypes.c_size_t(ws_bytes), _stream_handle(stream))
     else:
@@ -310,7 +328,7 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
         del keep
     del host_cu
     if check and st != GDN_OK:
-        raise GDNError(st, "gdn_forward_pooled" if pool is not None else "gdn_forward")
+        raise GDNError(st, where)
     return st
 
 

@@ -209,6 +209,9 @@ const char* gdn_strerror(int status) {
     case GDN_ERR_PLAN: return "the forced plan cannot run these arguments";
     case GDN_ERR_RULE: return "only the gated delta update rule, with raw or effective gates, is implemented";
     case GDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case GDN_ERR_SCRATCH:
+      return "the call needs more scratch than the static array of gdn_forward_no_alloc holds "
+             "(GDN_NO_ALLOC_SCRATCH_BYTES); use gdn_forward with a workspace";
     default: return "unknown status";
   }
 }
@@ -286,7 +289,10 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
   const Span fin(t->final_state, state_bytes);
   const Span out(t->output, N * Hv * Dv * io);
   const Span cap(t->state_update, capsule ? R * (size_t)rv.cap * W * 4 : 0);
+  // the workspace size is checked before the overlap rules, which read need_ws bytes of it
   const size_t need_ws = workspace_for(rv);
+  if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
+  if (need_ws > 0 && !aligned16(workspace)) return GDN_ERR_WORKSPACE;
   const Span ws(workspace, need_ws);
   const Span outputs[] = {out, fin, cap, ws};
   for (const Span& o : outputs) {
@@ -299,9 +305,6 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
   if (out.overlaps(init) || cap.overlaps(init) || ws.overlaps(init)) return GDN_ERR_ALIAS;
   // final_state may be the very same buffer as initial_state (in-place update)
   if (fin.overlaps(init) && t->final_state != t->initial_state) return GDN_ERR_ALIAS;
-
-  if (need_ws > 0 && (workspace == nullptr || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
-  if (need_ws > 0 && !aligned16(workspace)) return GDN_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -559,3 +562,11 @@ int gdn_publish_slots(int32_t R, int32_t* committed, int32_t* inactive, void* st
 }
 
 }  // extern "C"
+
+// The forward call with a workspace the caller does not own (gdn_noalloc.hip).
+namespace gdn {
+int forward_entry(const gdn_params* p, const gdn_tensors* t, const gdn_slots* slots, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return forward_impl(p, t, slots, workspace, workspace_bytes, stream);
+}
+}  // namespace gdn

@@ -36,7 +36,8 @@
  *    returns, allocates no device memory and holds no global mutable state:
  *    calls on different streams may run concurrently as long as their buffers
  *    do not overlap. (Host-side checks of slot mirrors, gdn_pool.h, use
- *    temporary host memory.)
+ *    temporary host memory.) The one exception is gdn_forward_no_alloc, whose
+ *    workspace is a static device array per GPU (see there).
  *  - All device work is enqueued on `stream` (a hipStream_t; NULL is the null
  *    stream) and runs asynchronously; no call blocks on the device.
  *  - Every argument check runs on the host before anything is enqueued. A
@@ -57,8 +58,9 @@ extern "C" {
 /* Version of this ABI: structs, entry points and the capsule layout.
  * 2: gdn_params.gate_activation; cu_seqlens may be NULL (dense rank-4 layout).
  * 3: gdn_params.state_layout; the causal convolution (gdn_conv.h) and the state
- *    pools (gdn_pool.h). */
-#define GDN_ABI_VERSION 3
+ *    pools (gdn_pool.h).
+ * 4: gdn_forward_no_alloc and GDN_ERR_SCRATCH. */
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -70,7 +72,9 @@ typedef enum gdn_status {
   GDN_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required          */
   GDN_ERR_PLAN = 7,       /* forced plan not possible for these arguments        */
   GDN_ERR_RULE = 8,       /* update rule other than the gated delta rule         */
-  GDN_ERR_HIP = 9         /* the HIP runtime rejected a launch                   */
+  GDN_ERR_HIP = 9,        /* the HIP runtime rejected a launch                   */
+  GDN_ERR_SCRATCH = 10    /* gdn_forward_no_alloc: the call needs more scratch
+                             than its static array holds                         */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
@@ -174,6 +178,25 @@ typedef struct gdn_tensors {
  * needs none (workspace may be NULL). */
 int gdn_forward(const gdn_params* params, const gdn_tensors* tensors,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static scratch array behind gdn_forward_no_alloc: 128 MiB per GPU. */
+#define GDN_NO_ALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* gdn_forward for callers that cannot allocate device memory or provide a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, checks, kernels and results as gdn_forward;
+ * the CHUNK plan's workspace (chunk offsets, T' and P fragments, per-token
+ * factors) is a static device array of GDN_NO_ALLOC_SCRATCH_BYTES bytes instead,
+ * one per GPU, held from the library's first call on that GPU until the process
+ * ends. The call itself allocates nothing.
+ *  - A call whose workspace (gdn_forward_workspace_bytes, the exact figure with a
+ *    cu_seqlens_host mirror, else its upper bound) exceeds the array returns
+ *    GDN_ERR_SCRATCH before anything is enqueued. At Hv = 32, 128 MiB holds about
+ *    315 chunks of 64 tokens (about 20k tokens); the RECURRENT plan needs none.
+ *  - Every call on one GPU uses that GPU's one array, and nothing in it needs to
+ *    start at zero (each call writes what it reads). Calls that overlap on one
+ *    GPU (concurrent streams, or threads) race on it: serialize them. */
+int gdn_forward_no_alloc(const gdn_params* params, const gdn_tensors* tensors, void* stream);
 
 /* Workspace bytes gdn_forward needs for these params, written to *bytes.
  * cu_seqlens_host may be NULL; the result then is an upper bound that is valid

@@ -61,8 +61,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 3
+    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 4
     assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
+    assert "gdn_forward_no_alloc" in gdn.gdn_strerror(gdn.GDN_ERR_SCRATCH)
     assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
     assert gdn.gdn_strerror(12345) == "unknown status"
 
