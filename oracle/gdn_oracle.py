@@ -36,6 +36,24 @@ every value head, so that S_t = alpha_t S_{t-1} + u_t k^_t^T can be replayed
 from the committed state ("Replay compact fixed state for hybrid decoding",
 Summary).
 
+Update rules. The first page names the gated_delta rule and says the exporter
+selects among update rules and the operator validates the selection (What
+changed; Dependency), without listing the others. They are read here as the
+family that the name composes, the same family the Gated DeltaNet paper lays
+side by side when it compares linear-attention update rules: the decay gate
+alpha and the delta correction each switched on or off.
+
+  gated_delta  S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k^_t) k^_t^T
+  delta        the same with alpha_t = 1           (DeltaNet)
+  gated        S_t = alpha_t S_{t-1} + v_t k^_t^T   (gated linear attention)
+  linear       S_t = S_{t-1} + v_t k^_t^T           (linear attention)
+
+In all four, o_t = S_t q^_t and S_t = alpha_t S_{t-1} + u_t k^_t^T, with u_t the
+delta of the delta rules and u_t = v_t for the other two (alpha_t = 1 for the
+ungated ones), so the capsule and its replay hold for every rule. The ungated
+rules read no decay input (a, A_log, dt_bias), the rules without the delta
+correction no beta input (b).
+
 Everything is float64 on the exact values of the (possibly float16-rounded)
 inputs. Loops run over tokens; independent heads are batched with numpy.
 """
@@ -78,6 +96,35 @@ def gates(a, b, A_log, dt_bias, activation="raw"):
         raise ValueError(f"gate activation {activation!r}")
     alpha = np.exp(log_decay(a, A_log, dt_bias))
     beta = 1.0 / (1.0 + np.exp(-np.asarray(b, dtype=np.float64)))
+    return alpha, beta
+
+
+UPDATE_RULES = ("gated_delta", "delta", "gated", "linear")
+
+
+def rule_parts(rule):
+    """(gated, delta) of an update rule: whether it applies the decay alpha, and
+    whether it writes the delta beta (v - alpha S k^) rather than v itself."""
+    if rule not in UPDATE_RULES:
+        raise ValueError(f"update rule {rule!r}")
+    return rule in ("gated_delta", "gated"), rule in ("gated_delta", "delta")
+
+
+def rule_gates(a, b, A_log, dt_bias, activation, rule, num_tokens, Hv):
+    """(alpha, beta) [N, Hv] as the rule uses them: alpha = 1 for the ungated
+    rules and beta = None for the rules without the delta correction; inputs a
+    rule does not read may be None."""
+    gated, delta = rule_parts(rule)
+    alpha = beta = None
+    if gated or delta:
+        a_in = a if gated else np.zeros((num_tokens, Hv))
+        b_in = b if delta else np.zeros((num_tokens, Hv))
+        zeros = np.zeros(Hv)
+        alpha, beta = gates(a_in, b_in, A_log if gated else zeros, dt_bias if gated else zeros, activation)
+    if not gated:
+        alpha = np.ones((num_tokens, Hv))
+    if not delta:
+        beta = None
     return alpha, beta
 
 
@@ -160,17 +207,31 @@ def recurrence(qh, kh, v, alpha, beta, S0):
     return o, S, u_all
 
 
+def plain_write_recurrence(qh, kh, v, alpha, S0):
+    """The rules without the delta correction (gated, and linear with alpha = 1):
+    S_t = alpha_t S_{t-1} + v_t k^_t^T, o_t = S_t q^_t; shapes as recurrence.
+    Returns (o, S_T, u) with u = v, the capsule's delta for these rules."""
+    T, H, Dv = v.shape
+    S = np.array(S0, dtype=np.float64, copy=True)
+    o = np.zeros((T, H, Dv))
+    for t in range(T):
+        S = alpha[t][:, None, None] * S + v[t][:, :, None] * kh[t][:, None, :]
+        o[t] = np.einsum("hvk,hk->hv", S, qh[t])
+    return o, S, np.array(v, dtype=np.float64, copy=True)
+
+
 def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
                 scale=None, state_update_capacity=0, capture_count=None,
-                state_update_init=None, gate_activation="raw", num_reqs=None):
+                state_update_init=None, gate_activation="raw", num_reqs=None,
+                update_rule="gated_delta"):
     """Packed ragged forward by the token recurrence.
 
     Inputs as the operator takes them (q, k [N, Hk, Dk]; v [N, Hv, Dv]; a, b
     [N, Hv]; A_log, dt_bias [Hv]; cu_seqlens [R + 1], or None with num_reqs for
     the dense layout; initial_state [R, Hv, Dv, Dk] or None for zeros). a and b
     are raw gate inputs or, with gate_activation "none", alpha and beta.
-    Returns (output [N, Hv, Dv], final_state [R, Hv, Dv, Dk], state_update
-    [R, capacity, W] or None).
+    update_rule is one of UPDATE_RULES. Returns (output [N, Hv, Dv],
+    final_state [R, Hv, Dv, Dk], state_update [R, capacity, W] or None).
 
     With a capacity, request r captures its leading
     n_r = min(len_r, c_r) tokens, c_r being capture_count[r] clamped to
@@ -190,7 +251,8 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
     N, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     R = cu.shape[0] - 1
-    alpha, beta = gates(a, b, A_log, dt_bias, gate_activation)
+    _, delta = rule_parts(update_rule)
+    alpha, beta = rule_gates(a, b, A_log, dt_bias, gate_activation, update_rule, N, Hv)
     out = np.zeros((N, Hv, Dv))
     final = np.zeros((R, Hv, Dv, Dk))
     cap = int(state_update_capacity)
@@ -208,7 +270,10 @@ def gdn_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
             final[r] = S0
             continue
         qh, kh = _unit_qk(q[t0:t1], k[t0:t1], Hv, scale)
-        o, S, u = recurrence(qh, kh, v[t0:t1], alpha[t0:t1], beta[t0:t1], S0)
+        if delta:
+            o, S, u = recurrence(qh, kh, v[t0:t1], alpha[t0:t1], beta[t0:t1], S0)
+        else:
+            o, S, u = plain_write_recurrence(qh, kh, v[t0:t1], alpha[t0:t1], S0)
         out[t0:t1] = o
         final[r] = S
         if cap > 0:
@@ -288,8 +353,27 @@ def chunk_step(qh, kh, v, log_alpha, beta, S0):
     return o, S_out
 
 
+def chunk_step_plain_write(qh, kh, v, log_alpha, S0):
+    """One chunk of the rules without the delta correction: the deltas are the
+    values themselves (U = V), so
+      O   = diag(e^g) Q^ S0^T + (M o Q^ K^^T) V
+      S_L = e^{g_L} S0 + V^T diag(e^{g_L - g}) K^."""
+    L, H, Dk = kh.shape
+    Dv = v.shape[2]
+    o = np.zeros((L, H, Dv))
+    S_out = np.zeros((H, Dv, Dk))
+    g = np.cumsum(log_alpha, axis=0)
+    incl = np.tril(np.ones((L, L), dtype=bool), 0)
+    for h in range(H):
+        K, Q, V, gh = kh[:, h], qh[:, h], v[:, h], g[:, h]
+        M = np.exp(np.where(incl, gh[:, None] - gh[None, :], -np.inf))
+        o[:, h] = np.exp(gh)[:, None] * (Q @ S0[h].T) + (M * (Q @ K.T)) @ V
+        S_out[h] = np.exp(gh[-1]) * S0[h] + V.T @ (np.exp(gh[-1] - gh)[:, None] * K)
+    return o, S_out
+
+
 def chunked_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=None,
-                    scale=None, chunk=64):
+                    scale=None, chunk=64, update_rule="gated_delta"):
     """Packed ragged forward in the chunked form; chunks start at each sequence start."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -298,8 +382,9 @@ def chunked_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=Non
     N, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     R = cu.shape[0] - 1
-    la = log_decay(a, A_log, dt_bias)
-    beta = 1.0 / (1.0 + np.exp(-np.asarray(b, np.float64)))
+    gated, delta = rule_parts(update_rule)
+    la = log_decay(a, A_log, dt_bias) if gated else np.zeros((N, Hv))
+    beta = 1.0 / (1.0 + np.exp(-np.asarray(b, np.float64))) if delta else None
     out = np.zeros((N, Hv, Dv))
     final = np.zeros((R, Hv, Dv, Dk))
     for r in range(R):
@@ -309,7 +394,10 @@ def chunked_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, initial_state=Non
         for c0 in range(t0, t1, chunk):
             c1 = min(c0 + chunk, t1)
             qh, kh = _unit_qk(q[c0:c1], k[c0:c1], Hv, scale)
-            o, S = chunk_step(qh, kh, v[c0:c1], la[c0:c1], beta[c0:c1], S)
+            if delta:
+                o, S = chunk_step(qh, kh, v[c0:c1], la[c0:c1], beta[c0:c1], S)
+            else:
+                o, S = chunk_step_plain_write(qh, kh, v[c0:c1], la[c0:c1], S)
             out[c0:c1] = o
         final[r] = S
     return out, final
