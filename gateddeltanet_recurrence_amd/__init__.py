@@ -8,7 +8,7 @@ library raises an error.
 """
 from .binding import (  # noqa: F401
     GDNError, LibraryNotBuilt, PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK,
-    GDN_F32, GDN_F16, GDN_BF16, RULE_GATED_DELTA, GATE_RAW, GATE_NONE, ABI_VERSION,
+    GDN_F32, GDN_F16, GDN_BF16, RULE_GATED_DELTA, RULE_DELTA, RULE_GATED, RULE_LINEAR, GATE_RAW, GATE_NONE, ABI_VERSION,
     STATE_V_MAJOR, STATE_K_MAJOR,
     GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIAS, GDN_ERR_CAPACITY,
     GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP, GDN_ERR_SCRATCH, GdnParams, GdnTensors,

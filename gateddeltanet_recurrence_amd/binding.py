@@ -20,10 +20,10 @@ GDN_ERR_SCRATCH = 10
 NO_ALLOC_SCRATCH_BYTES = 128 << 20   # GDN_NO_ALLOC_SCRATCH_BYTES
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
-RULE_GATED_DELTA = 0
+RULE_GATED_DELTA, RULE_DELTA, RULE_GATED, RULE_LINEAR = 0, 1, 2, 3
 GATE_RAW, GATE_NONE = 0, 1
 STATE_V_MAJOR, STATE_K_MAJOR = 0, 1
-ABI_VERSION = 4          # the struct layouts below match this version of include/gdn.h
+ABI_VERSION = 5          # the struct layouts below match this version of include/gdn.h
 CONV_SILU, CONV_NONE = 0, 1
 
 

@@ -48,7 +48,9 @@ struct Resolved {
 
 int check_params(const gdn_params* p, Resolved* out) {
   if (p == nullptr) return GDN_ERR_NULL;
-  if (p->update_rule != GDN_RULE_GATED_DELTA) return GDN_ERR_RULE;
+  if (p->update_rule != GDN_RULE_GATED_DELTA && p->update_rule != GDN_RULE_DELTA &&
+      p->update_rule != GDN_RULE_GATED && p->update_rule != GDN_RULE_LINEAR)
+    return GDN_ERR_RULE;
   if (p->gate_activation != GDN_GATE_RAW && p->gate_activation != GDN_GATE_NONE) return GDN_ERR_RULE;
   if (p->state_layout != GDN_STATE_V_MAJOR && p->state_layout != GDN_STATE_K_MAJOR) return GDN_ERR_SHAPE;
   if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_F16) return GDN_ERR_DTYPE;
@@ -207,7 +209,7 @@ const char* gdn_strerror(int status) {
     case GDN_ERR_CAPACITY: return "capacity is negative or an accepted/captured count exceeds it";
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_PLAN: return "the forced plan cannot run these arguments";
-    case GDN_ERR_RULE: return "only the gated delta update rule, with raw or effective gates, is implemented";
+    case GDN_ERR_RULE: return "unknown update rule (gdn_rule) or gate activation";
     case GDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case GDN_ERR_SCRATCH:
       return "the call needs more scratch than the static array of gdn_forward_no_alloc holds "
@@ -253,9 +255,12 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
   const bool dense = t->cu_seqlens == nullptr;
   if (dense && (t->cu_seqlens_host != nullptr || rv.N % rv.R != 0)) return GDN_ERR_SHAPE;
   const bool gate_none = p->gate_activation == GDN_GATE_NONE;
-  if (!gate_none && (t->A_log == nullptr || t->dt_bias == nullptr)) return GDN_ERR_NULL;
-  if (rv.N > 0 && (t->q == nullptr || t->k == nullptr || t->v == nullptr || t->a == nullptr ||
-                   t->b == nullptr || t->output == nullptr))
+  // the decay input is read by the gated rules, beta by the rules with the delta correction
+  const bool gated = p->update_rule == GDN_RULE_GATED_DELTA || p->update_rule == GDN_RULE_GATED;
+  const bool delta = p->update_rule == GDN_RULE_GATED_DELTA || p->update_rule == GDN_RULE_DELTA;
+  if (gated && !gate_none && (t->A_log == nullptr || t->dt_bias == nullptr)) return GDN_ERR_NULL;
+  if (rv.N > 0 && (t->q == nullptr || t->k == nullptr || t->v == nullptr || (gated && t->a == nullptr) ||
+                   (delta && t->b == nullptr) || t->output == nullptr))
     return GDN_ERR_NULL;
 
   // alignment of vector-accessed buffers (the K-major kernels move v and the
@@ -320,6 +325,7 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
     a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
     a.k_major = k_major ? 1 : 0;
+    a.gated = gated ? 1 : 0; a.delta = delta ? 1 : 0;
     err = k_major ? gdn::launch_recurrent_kmajor(a, p->io_dtype, s) : gdn::launch_recurrent(a, p->io_dtype, s);
   } else {
     gdn::ChunkArgs a{};
@@ -332,6 +338,7 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     a.dense_len = dense_len; a.gate_none = gate_none ? 1 : 0;
     a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
     a.k_major = k_major ? 1 : 0;
+    a.gated = gated ? 1 : 0; a.delta = delta ? 1 : 0;
     err = gdn::launch_chunk(a, p->io_dtype, s);
   }
   return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;

@@ -883,23 +883,28 @@ __device__ __forceinline__ int frag_index(int rb, int s) { return rb == 3 ? 4 + 
 struct RawGates {
   float a, b;
 };
+// An input the update rule does not read gets an empty range (it reads as zero).
 __device__ __forceinline__ RawGates load_gates(const ChunkArgs& p, int t0, int L, int h, int t) {
   const int gate_bytes = ((L - 1) * p.Hv + 1) * 4;
+  const size_t off = (size_t)t0 * p.Hv + h;
   RawGates r;
-  r.a = buf_load_f32(make_rsrc(p.a + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
-  r.b = buf_load_f32(make_rsrc(p.b + (size_t)t0 * p.Hv + h, gate_bytes), t * p.Hv * 4);
+  r.a = buf_load_f32(make_rsrc(p.gated ? p.a + off : nullptr, p.gated ? gate_bytes : 0), t * p.Hv * 4);
+  r.b = buf_load_f32(make_rsrc(p.delta ? p.b + off : nullptr, p.delta ? gate_bytes : 0), t * p.Hv * 4);
   return r;
 }
 
 // Cumulative log decay (inclusive prefix sum over the 64 lanes = tokens) and beta
-// of head h; tokens >= L get log decay 0 and beta 0.
+// of head h; tokens >= L get log decay 0 and beta 0. Without the rule's gate the
+// log decay is 0; without its delta correction beta is 1 (T' = I; A and the
+// correction factor are zeroed where they are formed).
 __device__ __forceinline__ void gates_of(const ChunkArgs& p, int h, int L, int t, RawGates r, float* g,
                                          float* beta) {
   float la = 0.f, be = 0.f;
   if (t < L) {
     const bool gnone = p.gate_none != 0;           // A_log, dt_bias may be null then
-    la = gate_log_alpha(r.a, gnone, gnone ? 0.f : expf(p.A_log[h]), gnone ? 0.f : p.dt_bias[h]);
-    be = gate_beta(r.b, gnone);
+    if (p.gated)
+      la = gate_log_alpha(r.a, gnone, gnone ? 0.f : expf(p.A_log[h]), gnone ? 0.f : p.dt_bias[h]);
+    be = p.delta ? gate_beta(r.b, gnone) : 1.f;
   }
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -1025,7 +1030,7 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
       {
         const int t = lane;
         const float gt = gs[t], gL = gs[C - 1];
-        const float v = wave == kVecZ ? expf(gt) * sm.rk[t]
+        const float v = wave == kVecZ ? (p.delta ? expf(gt) * sm.rk[t] : 0.f)
                       : wave == kVecO ? expf(gt) * sm.rq[t]
                       : wave == kVecU ? expf(gL - gt) * sm.rk[t]
                                       : expf(gL);
@@ -1037,7 +1042,7 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_chunk_prep(ChunkArgs p, Ws w
       // per element. T' and P go out by nontemporal stores: the scan reads them
       // once, well after this workgroup (long prefill 790 -> 778 us)
       {
-        const float gr = gs[r], br = bs[r];
+        const float gr = gs[r], br = p.delta ? bs[r] : 0.f;   // A = 0 without the delta correction
         half4_t ph[4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {

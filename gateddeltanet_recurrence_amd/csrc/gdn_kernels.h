@@ -35,6 +35,8 @@ struct RecurrentArgs {
   const int32_t* final_slots;
   int32_t num_slots;            // 0: states indexed by request
   int32_t k_major;              // states stored [.., Dk, Dv] (else V-major [.., Dv, Dk])
+  int32_t gated;                // update rule applies the decay alpha (else alpha = 1, a not read)
+  int32_t delta;                // update rule writes beta (v - alpha S k^) (else v, b not read)
 };
 
 struct ReplayArgs {
@@ -75,6 +77,8 @@ struct ChunkArgs {
   const int32_t* final_slots;
   int32_t num_slots;            // 0: states indexed by request
   int32_t k_major;              // states stored [.., Dk, Dv] (else V-major [.., Dv, Dk])
+  int32_t gated;                // update rule applies the decay alpha (else alpha = 1, a not read)
+  int32_t delta;                // update rule writes beta (v - alpha S k^) (else v, b not read)
 };
 
 // Slot of request r's state. Without a pool (num_slots = 0) or without a slot

@@ -127,9 +127,10 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
     for (int i = 0; i < NR; ++i) M[i] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const bool gnone = p.gate_none != 0;
-  const float expA = gnone ? 0.f : expf(p.A_log[h]);
-  const float dtb = gnone ? 0.f : p.dt_bias[h];
+  const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
+  const bool gated = p.gated != 0, delta = p.delta != 0;
+  const float expA = (gnone || !gated) ? 0.f : expf(p.A_log[h]);
+  const float dtb = (gnone || !gated) ? 0.f : p.dt_bias[h];
   const IO* __restrict__ qp = static_cast<const IO*>(p.q);
   const IO* __restrict__ kp = static_cast<const IO*>(p.k);
   const IO* __restrict__ vp = static_cast<const IO*>(p.v);
@@ -153,8 +154,8 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
     }
     const float4_t vv = cvalid ? IoOps<IO>::load4(vp + ((size_t)t * p.Hv + h) * Dv + col)
                                : float4_t{0.f, 0.f, 0.f, 0.f};
-    const float at = p.a[(size_t)t * p.Hv + h];
-    const float bt = p.b[(size_t)t * p.Hv + h];
+    const float at = gated ? p.a[(size_t)t * p.Hv + h] : 0.f;
+    const float bt = delta ? p.b[(size_t)t * p.Hv + h] : 0.f;
 
     float ssk = 0.f, ssq = 0.f, skq = 0.f;
     float4_t pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
@@ -191,10 +192,11 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
     }
     const float rk = rsqrtf(ssk + kNormEps);
     const float rq = rsqrtf(ssq + kNormEps) * p.scale;
-    const float alpha = gate_alpha(at, gnone, expA, dtb);
-    const float beta = gate_beta(bt, gnone);
+    // the rule: alpha = 1 without the gate; u = v (beta 1, no correction) without the delta
+    const float alpha = gated ? gate_alpha(at, gnone, expA, dtb) : 1.f;
+    const float beta = delta ? gate_beta(bt, gnone) : 1.f;
     const float kq = skq * rk * rq;                // k^ . q^
-    const float ak = alpha * rk, aq = alpha * rq;
+    const float ak = (delta ? alpha : 0.f) * rk, aq = alpha * rq;
 
     float4_t u, o;
     u.x = beta * fmaf(-ak, pk.x, vv.x); u.y = beta * fmaf(-ak, pk.y, vv.y);

@@ -133,8 +133,9 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
-  const float expA = gnone ? 0.f : expf(p.A_log[h]);
-  const float dtb = gnone ? 0.f : p.dt_bias[h];
+  const bool gated = p.gated != 0, delta = p.delta != 0;
+  const float expA = (gnone || !gated) ? 0.f : expf(p.A_log[h]);
+  const float dtb = (gnone || !gated) ? 0.f : p.dt_bias[h];
   const IO* __restrict__ qp = static_cast<const IO*>(p.q);
   const IO* __restrict__ kp = static_cast<const IO*>(p.k);
   const IO* __restrict__ vp = static_cast<const IO*>(p.v);
@@ -164,8 +165,8 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
       const int row = min(row_base + i * RI + rg, Dv - 1);     // in bounds; unused past Dv
       vv[i] = IoOps<IO>::load1(vp + ((size_t)t * p.Hv + h) * Dv + row);
     }
-    const float at = p.a[(size_t)t * p.Hv + h];
-    const float bt = p.b[(size_t)t * p.Hv + h];
+    const float at = gated ? p.a[(size_t)t * p.Hv + h] : 0.f;
+    const float bt = delta ? p.b[(size_t)t * p.Hv + h] : 0.f;
 
     float ssk = 0.f, ssq = 0.f, skq = 0.f;
 #pragma unroll
@@ -179,8 +180,10 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     skq = group_sum<LPR>(skq);
     const float rk = rsqrtf(ssk + kNormEps);
     const float rq = rsqrtf(ssq + kNormEps) * p.scale;
-    const float alpha = gate_alpha(at, gnone, expA, dtb);
-    const float beta = gate_beta(bt, gnone);
+    // the rule: alpha = 1 without the gate; u = v (beta 1, no correction) without the delta
+    const float alpha = gated ? gate_alpha(at, gnone, expA, dtb) : 1.f;
+    const float beta = delta ? gate_beta(bt, gnone) : 1.f;
+    const float kd = delta ? alpha : 0.f;         // weight of the correction alpha S k^
     const float kq = skq * rk * rq;               // k^ . q^
 #pragma unroll
     for (int e = 0; e < E; ++e) kv[e] *= rk;      // k^
@@ -210,7 +213,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const float u = beta * (vv[i] - alpha * pk[i]);
+      const float u = beta * (vv[i] - kd * pk[i]);
       const float o = fmaf(alpha * rq, pq[i], u * kq);
 #pragma unroll
       for (int e = 0; e < E; ++e) S[i][e] = fmaf(alpha, S[i][e], u * kv[e]);
@@ -307,8 +310,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
-  const float expA = gnone ? 0.f : expf(p.A_log[h]);
-  const float dtb = gnone ? 0.f : p.dt_bias[h];
+  const bool gated = p.gated != 0, delta = p.delta != 0;
+  const float expA = (gnone || !gated) ? 0.f : expf(p.A_log[h]);
+  const float dtb = (gnone || !gated) ? 0.f : p.dt_bias[h];
   const IO* __restrict__ qp = static_cast<const IO*>(p.q);
   const IO* __restrict__ kp = static_cast<const IO*>(p.k);
   const IO* __restrict__ vp = static_cast<const IO*>(p.v);
@@ -359,8 +363,8 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
           sm.qh[j][part * EPT + e] = qv[e] * rq;
         }
         if (part == 0) {
-          sm.alpha[j] = gate_alpha(p.a[(size_t)t * p.Hv + h], gnone, expA, dtb);
-          sm.beta[j] = gate_beta(p.b[(size_t)t * p.Hv + h], gnone);
+          sm.alpha[j] = gated ? gate_alpha(p.a[(size_t)t * p.Hv + h], gnone, expA, dtb) : 1.f;
+          sm.beta[j] = delta ? gate_beta(p.b[(size_t)t * p.Hv + h], gnone) : 1.f;
           sm.kq[j] = skq * rk * rq;
         }
       }   // a token's 16 lanes are one aligned DPP row group: active or idle together
@@ -412,11 +416,13 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
       // the state's scale is reset (one in-place multiply) only when the
       // product would leave the range where 1/gam is safe
       const float rgn = keep_scaled ? __builtin_amdgcn_rcpf(gn) : 1.f;
+      // u = beta (v - alpha S k^) with the delta correction, v without it
+      const float gk = delta ? gn : 0.f;
       float u[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const float vv = sm.v[j][row_base + i * RI + rg - block_row0];   // zero past Dv
-        u[i] = beta * (vv - gn * pk[i]);
+        u[i] = beta * (vv - gk * pk[i]);
       }
       // the state after the segment's last token is used only as a final state
       // (the verify asks for none)

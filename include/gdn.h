@@ -1,8 +1,9 @@
 /*
  * gdn.h - C ABI of the MI355X (gfx950) GatedDeltaNet operator library, libgdn.so.
  *
- * The operator runs the gated delta rule on packed ragged inputs and keeps an
- * FP32 V-major recurrent state per request and value head:
+ * The operator runs the gated delta rule (or, on request, one of the related
+ * update rules of gdn_rule) on packed ragged inputs and keeps an FP32 V-major
+ * recurrent state per request and value head:
  *
  *   alpha_t = exp(-exp(A_log[h]) * softplus(a[t,h] + dt_bias[h]))
  *   beta_t  = sigmoid(b[t,h])
@@ -59,8 +60,9 @@ extern "C" {
  * 2: gdn_params.gate_activation; cu_seqlens may be NULL (dense rank-4 layout).
  * 3: gdn_params.state_layout; the causal convolution (gdn_conv.h) and the state
  *    pools (gdn_pool.h).
- * 4: gdn_forward_no_alloc and GDN_ERR_SCRATCH. */
-#define GDN_ABI_VERSION 4
+ * 4: gdn_forward_no_alloc and GDN_ERR_SCRATCH.
+ * 5: the update rules GDN_RULE_DELTA, GDN_RULE_GATED and GDN_RULE_LINEAR. */
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -71,7 +73,7 @@ typedef enum gdn_status {
   GDN_ERR_CAPACITY = 5,   /* capacity < 0, or capture/accepted beyond capacity   */
   GDN_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required          */
   GDN_ERR_PLAN = 7,       /* forced plan not possible for these arguments        */
-  GDN_ERR_RULE = 8,       /* update rule other than the gated delta rule         */
+  GDN_ERR_RULE = 8,       /* unknown update rule or gate activation              */
   GDN_ERR_HIP = 9,        /* the HIP runtime rejected a launch                   */
   GDN_ERR_SCRATCH = 10    /* gdn_forward_no_alloc: the call needs more scratch
                              than its static array holds                         */
@@ -87,9 +89,24 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
  * forcing CHUNK where it cannot run is GDN_ERR_PLAN. */
 typedef enum gdn_plan { GDN_PLAN_AUTO = 0, GDN_PLAN_RECURRENT = 1, GDN_PLAN_CHUNK = 2 } gdn_plan;
 
-/* Only the gated delta rule is implemented ("update-rule input validation",
- * first page, Dependency). */
-typedef enum gdn_rule { GDN_RULE_GATED_DELTA = 0 } gdn_rule;
+/* Update rule ("update-rule selection" and "update-rule input validation", first
+ * page, What changed and Dependency; the page names the gated_delta rule). The
+ * others are read as the family that name composes: the decay gate and the delta
+ * correction each on or off. With u the value written and S = alpha S + u k^^T:
+ *   GDN_RULE_GATED_DELTA  u = beta (v - alpha S k^)   alpha from a   (Gated DeltaNet)
+ *   GDN_RULE_DELTA        u = beta (v - S k^)         alpha = 1      (DeltaNet)
+ *   GDN_RULE_GATED        u = v                       alpha from a   (gated linear attention)
+ *   GDN_RULE_LINEAR       u = v                       alpha = 1      (linear attention)
+ * and out = S q^ for all four. The ungated rules read neither a nor A_log nor
+ * dt_bias (they may be NULL); the rules without the delta correction do not read
+ * b (it may be NULL). The capsule holds (alpha, k^, u) as above for every rule,
+ * so gdn_replay is the same for all. Any other value is GDN_ERR_RULE. */
+typedef enum gdn_rule {
+  GDN_RULE_GATED_DELTA = 0,
+  GDN_RULE_DELTA = 1,
+  GDN_RULE_GATED = 2,
+  GDN_RULE_LINEAR = 3
+} gdn_rule;
 
 /* What a and b hold.
  *  GDN_GATE_RAW:  the raw gate inputs; the operator forms
@@ -125,7 +142,7 @@ typedef struct gdn_params {
                                     only 64 is supported                           */
   int32_t state_update_capacity; /* capsule rows per request; 0: no capsule        */
   int32_t plan;                  /* gdn_plan                                       */
-  int32_t update_rule;           /* gdn_rule; must be GDN_RULE_GATED_DELTA         */
+  int32_t update_rule;           /* gdn_rule                                       */
   int32_t gate_activation;       /* gdn_gate_activation of a and b                 */
   int32_t state_layout;          /* gdn_state_layout of initial and final states   */
 } gdn_params;
@@ -137,11 +154,15 @@ typedef struct gdn_tensors {
   const void* k;                 /* device, io  [N, Hk, Dk]                        */
   const void* v;                 /* device, io  [N, Hv, Dv]                        */
   const float* a;                /* device, f32 [N, Hv]  decay input (see
-                                    gdn_gate_activation)                           */
-  const float* b;                /* device, f32 [N, Hv]  beta input                */
-  const float* A_log;            /* device, f32 [Hv]; may be NULL with GDN_GATE_NONE */
+                                    gdn_gate_activation); NULL allowed for the
+                                    ungated rules                                  */
+  const float* b;                /* device, f32 [N, Hv]  beta input; NULL allowed
+                                    for the rules without the delta correction     */
+  const float* A_log;            /* device, f32 [Hv]; may be NULL with GDN_GATE_NONE
+                                    or an ungated rule                             */
   const float* dt_bias;          /* device, f32 [Hv]  one scalar per value head;
-                                    may be NULL with GDN_GATE_NONE                 */
+                                    may be NULL with GDN_GATE_NONE or an ungated
+                                    rule                                           */
   const int32_t* cu_seqlens;     /* device, i32 [R + 1]: 0 = cu[0] <= ... <= cu[R] = N;
                                     request r owns tokens cu[r] .. cu[r+1]-1.
                                     NULL selects the dense rank-4 layout ("ragged

@@ -45,16 +45,30 @@ def device_inputs(inp, torch):
     return d
 
 
+RULE_NAMES = ("gated_delta", "delta", "gated", "linear")     # gdn_rule codes 0 .. 3
+
+
+def rule_reads(rule):
+    """(reads the decay input a, reads beta b) of an update rule name."""
+    return rule in ("gated_delta", "gated"), rule in ("gated_delta", "delta")
+
+
 def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0,
                 capture_count=None, poison=None, plan=None, host_cu=True, workspace=True,
-                scale=0.0, gate="raw", dense=False):
+                scale=0.0, gate="raw", dense=False, rule="gated_delta"):
     """One gdn_forward call on fresh device copies; returns numpy results.
 
     gate "none": a, b are passed as effective gates without A_log, dt_bias.
-    dense: no cu_seqlens (every request holds N / R tokens)."""
+    dense: no cu_seqlens (every request holds N / R tokens).
+    rule: update rule name; inputs the rule does not read are passed as NULL."""
     d = device_inputs(inp, torch)
     if gate == "none":
         d["A_log"] = d["dt_bias"] = None
+    reads_a, reads_b = rule_reads(rule)
+    if not reads_a:
+        d["a"] = d["A_log"] = d["dt_bias"] = None
+    if not reads_b:
+        d["b"] = None
     N, Hv, Dv = inp["v"].shape
     R = len(inp["cu_seqlens"]) - 1
     Hk, Dk = inp["Hk"], inp["Dk"]
@@ -89,7 +103,7 @@ def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0
                     state_update=su, capture_count=cc, cu_seqlens_host=cu_host,
                     state_update_capacity=capacity, plan=plan_code, workspace=ws, scale=scale,
                     gate_activation=gdn.GATE_NONE if gate == "none" else gdn.GATE_RAW,
-                    num_reqs=R if dense else None)
+                    num_reqs=R if dense else None, update_rule=RULE_NAMES.index(rule))
     torch.cuda.synchronize()
     res = {"output": out.float().cpu().numpy(),
            "final_state": None if fin is None else fin.cpu().numpy(),
@@ -98,7 +112,8 @@ def run_forward(inp, torch, gdn, *, in_place=False, write_final=True, capacity=0
     return res
 
 
-def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=None, gate="raw"):
+def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=None, gate="raw",
+                   rule="gated_delta"):
     init = None
     if capacity > 0:
         W = O.capsule_width(inp["Hk"], inp["Hv"], inp["Dk"], inp["Dv"])
@@ -108,7 +123,7 @@ def oracle_forward(inp, O, capacity=0, capture_count=None, poison=None, scale=No
                          inp["dt_bias"], inp["cu_seqlens"], inp["initial_state"],
                          scale=scale, state_update_capacity=capacity,
                          capture_count=capture_count, state_update_init=init,
-                         gate_activation=gate)
+                         gate_activation=gate, update_rule=rule)
 
 
 def sample_heads_inputs(inp, heads):

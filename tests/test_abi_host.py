@@ -61,7 +61,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 4
+    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 5
     assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
     assert "gdn_forward_no_alloc" in gdn.gdn_strerror(gdn.GDN_ERR_SCRATCH)
     assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
@@ -107,7 +107,8 @@ def test_null_structs():
 @pytest.mark.parametrize("field,value,code", [
     ("io_dtype", gdn.GDN_BF16, gdn.GDN_ERR_DTYPE),
     ("io_dtype", 7, gdn.GDN_ERR_DTYPE),
-    ("update_rule", 1, gdn.GDN_ERR_RULE),
+    ("update_rule", 4, gdn.GDN_ERR_RULE),
+    ("update_rule", -1, gdn.GDN_ERR_RULE),
     ("gate_activation", 2, gdn.GDN_ERR_RULE),
     ("num_v_heads", 3, gdn.GDN_ERR_SHAPE),          # Hk = 2 does not divide 3
     ("head_k_dim", 48, gdn.GDN_ERR_SHAPE),
@@ -152,6 +153,26 @@ def test_effective_gates_need_no_gate_parameters():
     assert _forward(_p(), t) == gdn.GDN_ERR_NULL
     t.initial_state = t.initial_state + 4
     assert _forward(_p(gate_activation=gdn.GATE_NONE), t) == gdn.GDN_ERR_SHAPE
+
+
+@pytest.mark.parametrize("rule,unread", [
+    (gdn.RULE_DELTA, ("a", "A_log", "dt_bias")),           # ungated: no decay input
+    (gdn.RULE_GATED, ("b",)),                              # no delta correction: no beta
+    (gdn.RULE_LINEAR, ("a", "b", "A_log", "dt_bias")),
+])
+def test_rules_do_not_need_the_inputs_they_do_not_read(rule, unread):
+    # with those inputs missing the call gets past the pointer checks to the next
+    # error (a misaligned state); the gated delta rule needs them all
+    t, _ = _tensors(8, 2, 2, 4, 16, 16, **{n: None for n in unread})
+    t.initial_state = t.initial_state + 4
+    assert _forward(_p(update_rule=rule), t) == gdn.GDN_ERR_SHAPE
+    assert _forward(_p(update_rule=gdn.RULE_GATED_DELTA), t) == gdn.GDN_ERR_NULL
+
+
+def test_rules_still_need_the_inputs_they_read():
+    for rule, needed in ((gdn.RULE_DELTA, "b"), (gdn.RULE_GATED, "a"), (gdn.RULE_GATED, "A_log")):
+        t, _ = _tensors(8, 2, 2, 4, 16, 16, **{needed: None})
+        assert _forward(_p(update_rule=rule), t) == gdn.GDN_ERR_NULL, (rule, needed)
 
 
 def test_tokens_without_requests_is_a_shape_error():
