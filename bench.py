@@ -306,6 +306,54 @@ def run_verify_replay(args, torch, gdn):
                          "verify_bytes": verify_bytes, "replay_bytes": replay_bytes}}
 
 
+def run_spec_step_fused(args, torch, gdn):
+    """The speculative step as one gdn_replay_forward call: the previous step's
+    accepted prefix replayed from the committed bank into the inactive bank and
+    this step's verify from that state, the committed bank read once. The banks
+    rotate as in spec_verify_replay; each step replays the capsule the previous
+    step wrote (two capsule buffers alternate)."""
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs("spec_verify_replay")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R, cap = len(inp["cu_seqlens"]) - 1, inp["capacity"]
+    W = gdn.capsule_width(Hk, Hv, Dk, Dv)
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    acc_host = inp["accepted"]
+    acc = _dev(acc_host, torch)
+    state_bytes = R * Hv * Dv * Dk * 4
+    n_banks = max(4, 2 * -(-(3 * BANK_TARGET_BYTES // 2) // (2 * state_bytes)))
+    init = _dev(inp["initial_state"], torch)
+    banks = [init.clone() for _ in range(n_banks)]
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    caps = [torch.empty((R, cap, W), dtype=torch.float32, device="cuda") for _ in range(2)]
+    host_cu = inp["cu_seqlens"]
+    # a real previous capsule for the first step: one verify from the committed bank
+    gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=banks[0], state_update=caps[1],
+                    state_update_capacity=cap, cu_seqlens_host=host_cu, plan=gdn.PLAN_RECURRENT)
+
+    def step(i):
+        gdn.gdn_replay_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=banks[(2 * i) % n_banks],
+                               state_update=caps[i % 2], state_update_capacity=cap, cu_seqlens_host=host_cu,
+                               prev_state_update=caps[(i + 1) % 2], accepted=acc, accepted_host=acc_host,
+                               replay_state=banks[(2 * i + 1) % n_banks], plan=gdn.PLAN_RECURRENT)
+
+    _log(f"fused replay+verify: R={R} T=4 Hv={Hv} banks={n_banks}")
+    ms = _time_steps(torch, step, args.steps, args.warmup)
+    per_call = _per_call(torch, step, 50, args.warmup + args.steps)
+    io = 2
+    nbytes = (2 * state_bytes + int(acc_host.sum()) * W * 4 + R * cap * W * 4 + 2 * N * Hk * Dk * io
+              + 2 * N * Hv * Dv * io + 2 * N * Hv * 4 + 2 * Hv * 4 + (R + 1) * 4 + R * 4)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "per_call": per_call,
+            "config": {"requests": R, "draft_tokens": 4, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                       "capacity": cap, "accepted": acc_host.tolist(), "state_banks": n_banks},
+            "roofline": {"bound": "hbm", "kernel": "gdn_replay_verify", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("spec_step_fused"), "algorithmic_bytes_per_step": nbytes}}
+
+
 def run_spec_step_pooled(args, torch, gdn):
     """The speculative step over a fixed-state pool: verify reads each request's
     committed slot (capsule, no final state), replay writes the accepted prefix into
@@ -551,7 +599,7 @@ def main():
     ap.add_argument("--workload", default="all",
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
                              "decode_effective_dense", "conv_prefill", "conv_decode",
-                             "spec_step_pooled", "decode_kmajor", "hbm_copy"],
+                             "spec_step_pooled", "spec_step_fused", "decode_kmajor", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="length of each oracle CPU-baseline sample (0 skips them)")
@@ -576,6 +624,7 @@ def main():
               "conv_prefill": lambda: run_conv(args, torch, gdn, "conv_prefill"),
               "conv_decode": lambda: run_conv(args, torch, gdn, "conv_decode"),
               "spec_step_pooled": lambda: run_spec_step_pooled(args, torch, gdn),
+              "spec_step_fused": lambda: run_spec_step_fused(args, torch, gdn),
               "decode_kmajor": lambda: run_decode_kmajor(args, torch, gdn),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
@@ -591,6 +640,7 @@ def main():
             "conv_prefill": run_conv(args, torch, gdn, "conv_prefill"),
             "conv_decode": run_conv(args, torch, gdn, "conv_decode"),
             "spec_step_pooled": run_spec_step_pooled(args, torch, gdn),
+            "spec_step_fused": run_spec_step_fused(args, torch, gdn),
             "decode_kmajor": run_decode_kmajor(args, torch, gdn),
         }
     if args.cpu_seconds > 0:

@@ -23,7 +23,7 @@ PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA, RULE_DELTA, RULE_GATED, RULE_LINEAR = 0, 1, 2, 3
 GATE_RAW, GATE_NONE = 0, 1
 STATE_V_MAJOR, STATE_K_MAJOR = 0, 1
-ABI_VERSION = 5          # the struct layouts below match this version of include/gdn.h
+ABI_VERSION = 6          # the struct layouts below match this version of include/gdn.h
 CONV_SILU, CONV_NONE = 0, 1
 
 
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_resolve_plan.restype = ctypes.c_int
         L.gdn_replay.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.gdn_replay.restype = ctypes.c_int
+        L.gdn_replay_forward.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), vp, vp, vp,
+                                         vp, vp]
+        L.gdn_replay_forward.restype = ctypes.c_int
         L.gdn_conv_forward.argtypes = [ctypes.POINTER(GdnConvParams),
                                        ctypes.POINTER(GdnConvTensors), vp]
         L.gdn_conv_forward.restype = ctypes.c_int
@@ -238,6 +241,19 @@ def gdn_forward_no_alloc(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, **kw
     return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, no_alloc=True, **kw)
 
 
+def gdn_replay_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, prev_state_update,
+                       accepted, replay_state, accepted_host=None, **kw) -> int:
+    """gdn_replay_forward of include/gdn.h: replay of the previous step's accepted
+    capsule prefix onto initial_state (the committed bank) into replay_state (the
+    inactive bank) and the verify of this step's tokens from that state, in one
+    pass. prev_state_update [R, capacity, W] float32, accepted [R] int32 (GPU
+    tensors), accepted_host a host int32 mirror or None, replay_state
+    [R, Hv, Dv, Dk] float32; the other keywords as _forward."""
+    return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output,
+                    replay=dict(prev=prev_state_update, accepted=accepted, state=replay_state,
+                                accepted_host=accepted_host), **kw)
+
+
 def gdn_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, num_slots: int,
                        read_slots=None, write_slots=None, read_slots_host=None,
                        write_slots_host=None, **kw) -> int:
@@ -255,7 +271,7 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
              plan: int = PLAN_AUTO, update_rule: int = RULE_GATED_DELTA,
              gate_activation: int = GATE_RAW, num_reqs: Optional[int] = None, workspace=None,
              stream=None, check: bool = True, pool=None, state_layout: int = STATE_V_MAJOR,
-             no_alloc: bool = False) -> int:
+             no_alloc: bool = False, replay=None) -> int:
     """One forward call on torch tensors; returns the status code.
 
     q, k [N, Hk, Dk], v and output [N, Hv, Dv] in float16 or float32 (for the
@@ -315,7 +331,22 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
                       _ptr(cu_seqlens), host_cu_ptr, _ptr(initial_state), _ptr(final_state),
                       _ptr(output), _ptr(state_update), _ptr(capture_count))
     where = "gdn_forward_pooled" if pool is not None else "gdn_forward"
-    if no_alloc:
+    if replay is not None:
+        if pool is not None or no_alloc or workspace is not None:
+            raise ValueError("gdn_replay_forward takes no pool and no workspace")
+        where = "gdn_replay_forward"
+        _need(replay["prev"], "prev_state_update",
+              (R, state_update_capacity, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
+        _need(replay["accepted"], "accepted", (R,), torch.int32)
+        _need(replay["state"], "replay_state", st_shape, torch.float32)
+        acc_host, acc_host_ptr = _host_i32(replay["accepted_host"])
+        if acc_host is not None and acc_host.shape != (R,):
+            raise ValueError("accepted_host must have R entries")
+        st = lib().gdn_replay_forward(ctypes.byref(params), ctypes.byref(tens), _ptr(replay["prev"]),
+                                      _ptr(replay["accepted"]), acc_host_ptr, _ptr(replay["state"]),
+                                      _stream_handle(stream))
+        del acc_host
+    elif no_alloc:
         where = "gdn_forward_no_alloc"
         st = lib().gdn_forward_no_alloc(ctypes.byref(params), ctypes.byref(tens), _stream_handle(stream))
     elif pool is None:

@@ -240,14 +240,34 @@ int gdn_forward_workspace_bytes(const gdn_params* p, const int32_t* cu_host, siz
   return GDN_OK;
 }
 
+// The previous step's capsule, accepted counts and inactive bank of gdn_replay_forward.
+struct FusedReplay {
+  const float* capsule;
+  const int32_t* accepted;
+  const int32_t* accepted_host;
+  float* state;
+};
+
 static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slots* slots,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const FusedReplay* rp = nullptr) {
   Resolved rv;
   int st = check_params(p, &rv);
   if (st != GDN_OK) return st;
   if (t == nullptr) return GDN_ERR_NULL;
   const bool capsule = t->state_update != nullptr;
   if (capsule && rv.cap == 0) return GDN_ERR_CAPACITY;   // a capsule needs rows
+  if (rp != nullptr) {
+    // the fused step: a verify (capsule) from the replayed committed V-major bank
+    if (!capsule || t->initial_state == nullptr || rp->capsule == nullptr || rp->accepted == nullptr ||
+        rp->state == nullptr)
+      return GDN_ERR_NULL;
+    if (p->state_layout != GDN_STATE_V_MAJOR) return GDN_ERR_SHAPE;
+    if (!aligned16(rp->state)) return GDN_ERR_SHAPE;
+    if (rp->accepted_host != nullptr)
+      for (int64_t r = 0; r < rv.R; ++r)
+        if (rp->accepted_host[r] < 0 || rp->accepted_host[r] > rv.cap) return GDN_ERR_CAPACITY;
+  }
   if (rv.R == 0) return rv.N == 0 ? GDN_OK : GDN_ERR_SHAPE;
 
   // required pointers; without cu_seqlens every request holds N / R tokens (dense
@@ -310,6 +330,20 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
   if (out.overlaps(init) || cap.overlaps(init) || ws.overlaps(init)) return GDN_ERR_ALIAS;
   // final_state may be the very same buffer as initial_state (in-place update)
   if (fin.overlaps(init) && t->final_state != t->initial_state) return GDN_ERR_ALIAS;
+  if (rp != nullptr) {
+    // the committed bank is read only; the previous capsule and the accepted
+    // counts are inputs; the inactive bank overlaps nothing
+    const Span prev(rp->capsule, R * (size_t)rv.cap * W * 4);
+    const Span acc(rp->accepted, R * 4);
+    const Span dst(rp->state, state_bytes);
+    if (fin.overlaps(init)) return GDN_ERR_ALIAS;
+    for (const Span& o : {out, fin, cap, dst})
+      if (o.overlaps(prev) || o.overlaps(acc)) return GDN_ERR_ALIAS;
+    for (const Span& o : {out, fin, cap, init})
+      if (o.overlaps(dst)) return GDN_ERR_ALIAS;
+    for (const Span& i : inputs)
+      if (dst.overlaps(i)) return GDN_ERR_ALIAS;
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -326,6 +360,9 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     a.initial_slots = sp.rd; a.final_slots = sp.wr; a.num_slots = (int32_t)sp.P;
     a.k_major = k_major ? 1 : 0;
     a.gated = gated ? 1 : 0; a.delta = delta ? 1 : 0;
+    if (rp != nullptr) {
+      a.replay_capsule = rp->capsule; a.accepted = rp->accepted; a.replay_state = rp->state;
+    }
     err = k_major ? gdn::launch_recurrent_kmajor(a, p->io_dtype, s) : gdn::launch_recurrent(a, p->io_dtype, s);
   } else {
     gdn::ChunkArgs a{};
@@ -517,6 +554,13 @@ int gdn_forward_pooled(const gdn_params* p, const gdn_tensors* t, const gdn_slot
                        size_t workspace_bytes, void* stream) {
   if (slots == nullptr) return GDN_ERR_NULL;
   return forward_impl(p, t, slots, workspace, workspace_bytes, stream);
+}
+
+int gdn_replay_forward(const gdn_params* p, const gdn_tensors* t, const float* prev_state_update,
+                       const int32_t* accepted, const int32_t* accepted_host, float* replay_state,
+                       void* stream) {
+  const FusedReplay rp{prev_state_update, accepted, accepted_host, replay_state};
+  return forward_impl(p, t, nullptr, nullptr, 0, stream, &rp);
 }
 
 int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,

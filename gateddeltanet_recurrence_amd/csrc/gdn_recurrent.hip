@@ -272,7 +272,7 @@ struct StageSmem {
   float alpha[kStageTokens], beta[kStageTokens], kq[kStageTokens];
 };
 
-template <typename IO, int DK, int NI, bool CAPTURE>
+template <typename IO, int DK, int NI, bool CAPTURE, bool REPLAY>
 __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, int waves_per_block,
                                                       int blocks_per_head) {
   using L = RecLayout<DK>;
@@ -308,6 +308,45 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   float S[NI][E];
   bool valid[NI];
   load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
+
+  if constexpr (REPLAY) {
+    // the previous step's accepted capsule prefix, applied in registers with the
+    // arithmetic of gdn_replay (S = alpha S + u k^, one fused multiply-add of
+    // alpha S onto the product u k^ per element), then the result to the
+    // inactive bank: replay_state equals what gdn_replay writes, bit for bit
+    const int m = min(max(p.accepted[r], 0), p.capacity);
+    const float* caprow = p.replay_capsule + (size_t)r * p.capacity * p.capsule_width;
+    for (int j = 0; j < m; ++j, caprow += p.capsule_width) {
+      const float alpha = caprow[h];
+      float kv[E];
+#pragma unroll
+      for (int jj = 0; jj < V4; ++jj)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) kv[4 * jj + x] = caprow[p.Hv + g * DK + 4 * c + 4 * LPR * jj + x];  // rows of W floats need not be 16-byte aligned
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = row_base + i * RI + rg;
+        const float u = valid[i] ? caprow[p.Hv + p.Hk * DK + h * Dv + row] : 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) S[i][e] = fmaf(alpha, S[i][e], u * kv[e]);
+      }
+    }
+  }
+  // The replayed state goes to the inactive bank once the first token group is
+  // staged: stores count with the loads in the wave's memory counter, so stores
+  // issued before the staging loads would make the staging wait for them.
+  auto store_replayed = [&]() {
+    float* dst = p.replay_state + ((size_t)r * p.Hv + h) * Dv * DK;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (!valid[i]) continue;
+      const int row = row_base + i * RI + rg;
+#pragma unroll
+      for (int j = 0; j < V4; ++j)
+        store_state4(dst + (size_t)row * DK + 4 * c + 4 * LPR * j,
+                     float4_t{S[i][4 * j + 0], S[i][4 * j + 1], S[i][4 * j + 2], S[i][4 * j + 3]});
+    }
+  };
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
   const bool gated = p.gated != 0, delta = p.delta != 0;
@@ -376,6 +415,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
       sm.v[jj][rr] = row < Dv ? IoOps<IO>::load1(vp + ((size_t)(ts + jj) * p.Hv + h) * Dv + row) : 0.f;
     }
     __syncthreads();
+    if constexpr (REPLAY) {
+      if (ts == t0) store_replayed();              // the registers still hold the replayed state
+    }
 
     for (int j = 0; j < nt; ++j) {
       const int t = ts + j;
@@ -468,6 +510,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
     }
     __syncthreads();   // the next group's staging overwrites the staged tokens
   }
+  if constexpr (REPLAY) {
+    if (t1 == t0) store_replayed();                // no tokens: the replayed state as it is
+  }
 
   if (fin != nullptr) {
 #pragma unroll
@@ -491,7 +536,13 @@ __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_decode(RecurrentArgs p
 }
 template <typename IO, int DK, int NI>
 __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_capsule(RecurrentArgs p, int wpb, int bph) {
-  recurrent_body_staged<IO, DK, NI, true>(p, wpb, bph);
+  recurrent_body_staged<IO, DK, NI, true, false>(p, wpb, bph);
+}
+// gdn_capsule preceded by the replay of the previous step's accepted prefix
+// (gdn_replay_forward): one read of the committed state for both.
+template <typename IO, int DK, int NI>
+__global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_replay_verify(RecurrentArgs p, int wpb, int bph) {
+  recurrent_body_staged<IO, DK, NI, true, true>(p, wpb, bph);
 }
 
 template <int DK, int NI>
@@ -507,8 +558,12 @@ static hipError_t launch_dk(const RecurrentArgs& p, hipStream_t stream) {
   int wpb, bph;
   if (p.state_update != nullptr) {
     launch_shape<DK, NI_CAP>(p.Dv, &wpb, &bph);
-    hipLaunchKernelGGL((gdn_capsule<IO, DK, NI_CAP>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
-                       dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+    if (p.replay_capsule != nullptr)
+      hipLaunchKernelGGL((gdn_replay_verify<IO, DK, NI_CAP>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+                         dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+    else
+      hipLaunchKernelGGL((gdn_capsule<IO, DK, NI_CAP>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+                         dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
   } else {
     launch_shape<DK, NI>(p.Dv, &wpb, &bph);
     hipLaunchKernelGGL((gdn_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),

@@ -61,8 +61,9 @@ extern "C" {
  * 3: gdn_params.state_layout; the causal convolution (gdn_conv.h) and the state
  *    pools (gdn_pool.h).
  * 4: gdn_forward_no_alloc and GDN_ERR_SCRATCH.
- * 5: the update rules GDN_RULE_DELTA, GDN_RULE_GATED and GDN_RULE_LINEAR. */
-#define GDN_ABI_VERSION 5
+ * 5: the update rules GDN_RULE_DELTA, GDN_RULE_GATED and GDN_RULE_LINEAR.
+ * 6: gdn_replay_forward (replay and verify in one pass over the committed state). */
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -248,6 +249,38 @@ int gdn_replay(int32_t num_reqs, int32_t num_k_heads, int32_t num_v_heads,
                int32_t head_k_dim, int32_t head_v_dim, int32_t state_update_capacity,
                const float* src_state, const float* state_update, const int32_t* accepted,
                const int32_t* accepted_host, float* dst_state, void* stream);
+
+/* One speculative decoding step with a single read of the committed state:
+ * replays the accepted prefix of the previous step's capsule onto the committed
+ * bank, writes the result to the inactive bank, and verifies this step's draft
+ * tokens from that state ("Replay compact fixed state for hybrid decoding",
+ * Summary: accepted-prefix replay into an inactive bank; "[CUDA] Add compact
+ * GatedDeltaNet operator", Description: the state_update capsule). It returns
+ * the same statuses and writes the same bytes as
+ *   gdn_replay(R, Hk, Hv, Dk, Dv, capacity, tensors->initial_state,
+ *              prev_state_update, accepted, accepted_host, replay_state, stream);
+ *   gdn_forward(params, tensors with initial_state = replay_state, NULL, 0, stream);
+ * but reads the committed bank once instead of twice.
+ *   params, tensors as gdn_forward, with a capsule (state_update non-NULL,
+ *                 state_update_capacity > 0, so the RECURRENT plan) and V-major
+ *                 states; tensors->initial_state is the committed bank [R, Hv,
+ *                 Dv, Dk] (required, read only); tensors->final_state is NULL or
+ *                 a further buffer that receives the state after this step's
+ *                 tokens, disjoint from the committed bank.
+ *   prev_state_update device, f32 [R, capacity, W]: the previous step's
+ *                 capsule, W as for state_update (same capacity)
+ *   accepted      device, i32 [R]; m_r = accepted[r] clamped to [0, capacity]
+ *   accepted_host host mirror of accepted or NULL; when given every value must
+ *                 lie in [0, capacity] (else GDN_ERR_CAPACITY)
+ *   replay_state  device, f32 [R, Hv, Dv, Dk], 16-byte aligned: the inactive
+ *                 bank; it overlaps no other buffer of the call.
+ * Errors as gdn_forward; GDN_ERR_NULL for a missing capsule, committed bank,
+ * previous capsule, accepted or replay_state; GDN_ERR_SHAPE for the K-major
+ * layout; GDN_ERR_ALIAS for the overlaps above. The caller guarantees
+ * m_r <= the rows the previous step captured. */
+int gdn_replay_forward(const gdn_params* params, const gdn_tensors* tensors,
+                       const float* prev_state_update, const int32_t* accepted,
+                       const int32_t* accepted_host, float* replay_state, void* stream);
 
 /* Static text for a status code. */
 const char* gdn_strerror(int status);

@@ -61,7 +61,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 5
+    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 6
     assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
     assert "gdn_forward_no_alloc" in gdn.gdn_strerror(gdn.GDN_ERR_SCRATCH)
     assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
@@ -263,3 +263,66 @@ def test_replay_validation():
     neg = np.asarray([-1, 0], np.int32)
     assert L.gdn_replay(R, Hk, Hv, D, D, 4, src, cap, acc, neg.ctypes.data, dst, None) == gdn.GDN_ERR_CAPACITY
     assert L.gdn_replay(0, Hk, Hv, D, D, 4, None, None, None, None, None, None) == gdn.GDN_OK
+
+
+# ------------------------------------------- gdn_replay_forward (fused step)
+def _fused_case(N=8, R=2, Hk=2, Hv=4, Dk=16, Dv=16, cap=4):
+    """Fake disjoint ranges for a fused call: the forward tensors with a capsule,
+    plus the previous capsule, accepted counts and the inactive bank."""
+    t, addr = _tensors(N, R, Hk, Hv, Dk, Dv)
+    W = Hv + Hk * Dk + Hv * Dv
+    t.final_state = None
+    t.state_update = addr
+    addr += (R * cap * W * 4 + 4095) // 4096 * 4096 + 4096
+    prev = addr
+    addr += (R * cap * W * 4 + 4095) // 4096 * 4096 + 4096
+    acc = addr
+    addr += 4096
+    dst = addr
+    return t, prev, acc, dst, R * Hv * Dv * Dk * 4
+
+
+def _fused(p, t, prev, acc, acc_host, dst):
+    return gdn.lib().gdn_replay_forward(ctypes.byref(p), ctypes.byref(t), prev, acc, acc_host, dst, None)
+
+
+def test_replay_forward_validation():
+    t, prev, acc, dst, state_bytes = _fused_case()
+    p = _p(capacity=4)
+    # required pointers
+    assert _fused(p, t, None, acc, None, dst) == gdn.GDN_ERR_NULL
+    assert _fused(p, t, prev, None, None, dst) == gdn.GDN_ERR_NULL
+    assert _fused(p, t, prev, acc, None, None) == gdn.GDN_ERR_NULL
+    t2, *_ = _fused_case()
+    t2.initial_state = None
+    assert _fused(p, t2, prev, acc, None, dst) == gdn.GDN_ERR_NULL
+    t3, *_ = _fused_case()
+    t3.state_update = None
+    assert _fused(p, t3, prev, acc, None, dst) == gdn.GDN_ERR_NULL
+    # the K-major layout, a forced CHUNK plan, a misaligned inactive bank
+    assert _fused(_p(capacity=4, state_layout=gdn.STATE_K_MAJOR), t, prev, acc, None, dst) \
+        == gdn.GDN_ERR_SHAPE
+    assert _fused(_p(capacity=4, plan=gdn.PLAN_CHUNK), t, prev, acc, None, dst) == gdn.GDN_ERR_PLAN
+    assert _fused(p, t, prev, acc, None, dst + 4) == gdn.GDN_ERR_SHAPE
+    # accepted_host beyond [0, capacity]
+    for bad in ([5, 0], [-1, 2]):
+        host = (ctypes.c_int32 * 2)(*bad)
+        assert _fused(p, t, prev, acc, host, dst) == gdn.GDN_ERR_CAPACITY, bad
+    # no request: nothing to do
+    assert _fused(_p(N=0, R=0, capacity=4), t, prev, acc, None, dst) == gdn.GDN_OK
+
+
+def test_replay_forward_aliasing():
+    t, prev, acc, dst, state_bytes = _fused_case()
+    p = _p(capacity=4)
+    # the inactive bank may overlap nothing: the committed bank, the capsules,
+    # the output, the counts
+    for other in (t.initial_state, t.state_update, prev, t.output, acc, t.q):
+        assert _fused(p, t, prev, acc, None, other) == gdn.GDN_ERR_ALIAS
+    # the previous capsule is an input: it may not be the new one or the output
+    assert _fused(p, t, t.state_update, acc, None, dst) == gdn.GDN_ERR_ALIAS
+    assert _fused(p, t, t.output, acc, None, dst) == gdn.GDN_ERR_ALIAS
+    # the committed bank is read only: no in-place final state
+    t2, prev2, acc2, dst2, _ = _fused_case()
+    t2.final_state = t2.initial_state
+    assert _fused(p, t2, prev2, acc2, None, dst2) == gdn.GDN_ERR_ALIAS
