@@ -12,7 +12,8 @@
 // (request, value head) is held in registers for the whole segment by DKS
 // wavefronts, each with Dk / DKS of its rows: lane l holds the 4 columns
 // 4 (l mod LK) .. +3 (one 16-byte vector, so LK adjacent lanes read a 16 LK-byte
-// run of a row) in rows dk = dk0 + l / LK + (64 / LK) i. The contraction over dk
+// run of a row) in the NR consecutive rows dk = dk0 + NR (l / LK) + i, so that
+// the lane's k and q values are one vector load each. The contraction over dk
 // is an in-lane sum over the lane's rows, a sum over the lanes of equal
 // l mod LK (DPP rotations within each row of 16 lanes, two cross-row
 // exchanges), and with DKS = 2 the partner wavefront's partial sums through
@@ -66,6 +67,31 @@ template <> struct Io4Store<_Float16> {
   }
 };
 
+// N consecutive values of a k or q row as floats: 16-byte loads where the run is
+// whole 16-byte vectors (q and k are 16-byte aligned and every run starts at a
+// multiple of its length), single loads otherwise.
+template <typename IO, int N>
+__device__ __forceinline__ void load_run(const IO* src, float (&dst)[N]) {
+  constexpr int PER16 = 16 / (int)sizeof(IO);
+  if constexpr (N % PER16 == 0) {
+#pragma unroll
+    for (int v = 0; v < N / PER16; ++v) {
+      if constexpr (PER16 == 8) {
+        const half8_t x = *reinterpret_cast<const half8_t*>(src + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[8 * v + e] = (float)x[e];
+      } else {
+        const float4_t x = *reinterpret_cast<const float4_t*>(src + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * v + e] = x[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = IoOps<IO>::load1(src + i);
+  }
+}
+
 // Dk rows of a column slice are split over DKS wavefronts (DKS = 2 at Dk = 128:
 // 32 state floats per lane instead of 64, five waves per SIMD instead of three).
 // The contractions over dk then add the DKS partial sums through LDS, one
@@ -90,7 +116,7 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int cl = lane % LK;                        // column quad within the slice
-  const int rg = lane / LK;                        // row group: rows rg + RG i of this wave's part
+  const int rg = lane / LK;                        // row group: rows NR rg .. NR rg + NR - 1 of this part
   const int part = wave % DKS;                     // which dk part of the slice
   const int sl = wave / DKS;                       // slice within the workgroup
   const int dk0 = part * (DK / DKS);
@@ -118,10 +144,11 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   const float* init = state_head(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.Hv, h, head_elems);
   float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, head_elems);
 
+  const int row0 = dk0 + NR * rg;                  // this lane's first state row
   float4_t M[NR];
   if (init != nullptr && cvalid) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) M[i] = load_state4_nt(init + (size_t)(dk0 + rg + RG * i) * Dv + col);
+    for (int i = 0; i < NR; ++i) M[i] = load_state4_nt(init + (size_t)(row0 + i) * Dv + col);
   } else {
 #pragma unroll
     for (int i = 0; i < NR; ++i) M[i] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -144,14 +171,9 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   }
 
   for (int t = t0; t < t1; ++t) {
-    const IO* krow = kp + ((size_t)t * p.Hk + g) * DK + dk0;
-    const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK + dk0;
     float kv[NR], qv[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      kv[i] = IoOps<IO>::load1(krow + rg + RG * i);
-      qv[i] = IoOps<IO>::load1(qrow + rg + RG * i);
-    }
+    load_run<IO, NR>(kp + ((size_t)t * p.Hk + g) * DK + row0, kv);
+    load_run<IO, NR>(qp + ((size_t)t * p.Hk + g) * DK + row0, qv);
     const float4_t vv = cvalid ? IoOps<IO>::load4(vp + ((size_t)t * p.Hv + h) * Dv + col)
                                : float4_t{0.f, 0.f, 0.f, 0.f};
     const float at = gated ? p.a[(size_t)t * p.Hv + h] : 0.f;
@@ -224,7 +246,7 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
           // the shared key is written once per key head, by its first value head
           if (h % p.group == 0 && cl == 0) {
 #pragma unroll
-            for (int i = 0; i < NR; ++i) caprow[p.Hv + g * DK + dk0 + rg + RG * i] = kv[i] * rk;
+            for (int i = 0; i < NR; ++i) caprow[p.Hv + g * DK + row0 + i] = kv[i] * rk;
           }
         }
       }
@@ -233,7 +255,7 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
 
   if (fin != nullptr && cvalid) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) store_state4_nt(fin + (size_t)(dk0 + rg + RG * i) * Dv + col, M[i]);
+    for (int i = 0; i < NR; ++i) store_state4_nt(fin + (size_t)(row0 + i) * Dv + col, M[i]);
   }
 }
 
