@@ -46,14 +46,37 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # hbm_copy workload (FETCH_SIZE reads 65547.6 KiB for 131072 KiB copied: factor
 # 1.9996; WRITE_SIZE is exact: factor 1.0000). Keyed by the hash of the kernels'
 # sources: a changed kernel reports null until its counters are taken again.
-_KSRC = ["gateddeltanet_recurrence_amd/csrc/gdn_common.h", "gateddeltanet_recurrence_amd/csrc/gdn_kernels.h"]
 MEASURED_TRAFFIC = {
-    "gdn_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-                   "sha256_16": "07d238522b060041", "fetch_kib": 66995.5, "write_kib": 131599.9,
-                   "bytes": 271940815},
-    "gdn_decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-                          "sha256_16": "94793b2b7224c585", "fetch_kib": 66937.6, "write_kib": 131655.0,
-                          "bytes": 271878664},
+    "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "f8ea22181ba998c4", "fetch_kib": 66997.5, "write_kib": 131620.4,
+        "bytes": 271965694},
+    "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "f8ea22181ba998c4", "fetch_kib": 66993.1, "write_kib": 131607.8,
+        "bytes": 271943879},
+    "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "19be5ad2968d9cc6", "fetch_kib": 66938.1, "write_kib": 131687.3,
+        "bytes": 271912622},
+    "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "49b88f346ce267d6", "fetch_kib": 51114.8, "write_kib": 52118.8,
+        "bytes": 158034097},
+    "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "f8ea22181ba998c4", "fetch_kib": 26510.5, "write_kib": 52095.7,
+        "bytes": 107629796},
+    "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "49b88f346ce267d6", "fetch_kib": 51117.2, "write_kib": 52114.6,
+        "bytes": 158034790},
+    "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "b288356a98f7d4c2", "fetch_kib": 366618.3, "write_kib": 240719.2,
+        "bytes": 997196802},
+    "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "b288356a98f7d4c2", "fetch_kib": 669603.6, "write_kib": 724475.0,
+        "bytes": 2112965885},
+    "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "94de7a18eed7959c", "fetch_kib": 131140.9, "write_kib": 246423.9,
+        "bytes": 520866775},
+    "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "94de7a18eed7959c", "fetch_kib": 3716.6, "write_kib": 7168.0,
+        "bytes": 14950330},
 }
 
 
@@ -126,7 +149,7 @@ def run_decode(args, torch, gdn):
     ms_step = total_ms / args.steps
     nbytes = decode_bytes(inp)
     achieved = nbytes / (ms_step * 1e-3) / 1e9
-    traffic = measured_traffic("gdn_decode")
+    traffic = measured_traffic("batched_decode")
     # context only: single-call times, and one bank reused every step (its 128 MiB
     # can then stay in the 256 MB Infinity Cache between steps)
     per_call = _per_call(torch, step, 50, args.warmup + args.steps)
@@ -220,7 +243,7 @@ def run_decode_kmajor(args, torch, gdn):
                        "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "state_banks": n_banks},
             "roofline": {"bound": "hbm", "kernel": "gdn_decode_kmajor", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("gdn_decode_kmajor"),
+                         "traffic": measured_traffic("decode_kmajor"),
                          "algorithmic_bytes_per_step": nbytes}}
 
 
