@@ -66,12 +66,17 @@ def test_conv_bytes(bench):
 
 
 def test_traffic_figure_kept_only_for_unchanged_sources(bench, monkeypatch):
-    rec = dict(bench.MEASURED_TRAFFIC["gdn_decode"])
-    assert bench.measured_traffic("gdn_decode") in (rec["bytes"], None)
+    # every timed workload carries a counter figure, valid while its kernels' sources are
+    for wl in ("batched_decode", "decode_effective_dense", "decode_kmajor", "spec_verify_replay",
+               "spec_step_fused", "spec_step_pooled", "ragged_prefill", "long_prefill", "conv_prefill",
+               "conv_decode"):
+        rec = bench.MEASURED_TRAFFIC[wl]
+        assert bench.measured_traffic(wl) in (rec["bytes"], None), wl
+    rec = dict(bench.MEASURED_TRAFFIC["batched_decode"])
     stale = dict(rec, sha256_16="0" * 16)
-    monkeypatch.setitem(bench.MEASURED_TRAFFIC, "gdn_decode", stale)
-    assert bench.measured_traffic("gdn_decode") is None
-    assert bench.measured_traffic("no_such_kernel") is None
+    monkeypatch.setitem(bench.MEASURED_TRAFFIC, "batched_decode", stale)
+    assert bench.measured_traffic("batched_decode") is None
+    assert bench.measured_traffic("no_such_workload") is None
 
 
 def test_more_than_one_gpu_is_refused():
