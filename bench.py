@@ -439,6 +439,67 @@ def run_spec_step_pooled(args, torch, gdn):
                          "algorithmic_bytes_per_step": nbytes}}
 
 
+def run_spec_step_pooled_fused(args, torch, gdn):
+    """spec_step_pooled with the fused step: one gdn_replay_forward_pooled call (the
+    previous step's accepted prefix replayed from each committed slot into its
+    inactive slot, this step's verify from that state) and the publication, per
+    step. Pool and slot sets as spec_step_pooled; two capsule buffers alternate."""
+    from gdn_workloads import workload_inputs
+    inp = workload_inputs("spec_verify_replay")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R, cap = len(inp["cu_seqlens"]) - 1, inp["capacity"]
+    W = gdn.capsule_width(Hk, Hv, Dk, Dv)
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    acc_host = inp["accepted"]
+    acc = _dev(acc_host, torch)
+    state_bytes = R * Hv * Dv * Dk * 4
+    sets = max(2, -(-(3 * BANK_TARGET_BYTES // 2) // (2 * state_bytes)))
+    P = 2 * R * sets
+    pool = torch.empty((P, Hv, Dv, Dk), dtype=torch.float32, device="cuda")
+    init = _dev(inp["initial_state"], torch)
+    pairs = []
+    for j in range(sets):
+        base = 2 * R * j
+        committed = torch.arange(base, base + R, dtype=torch.int32, device="cuda")
+        inactive = torch.arange(base + R, base + 2 * R, dtype=torch.int32, device="cuda")
+        pool[base:base + R] = init
+        pool[base + R:base + 2 * R] = init
+        pairs.append((committed, inactive))
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    caps = [torch.empty((R, cap, W), dtype=torch.float32, device="cuda") for _ in range(2)]
+    host_cu = inp["cu_seqlens"]
+    # a real previous capsule for the first step
+    gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=init, state_update=caps[1],
+                    state_update_capacity=cap, cu_seqlens_host=host_cu, plan=gdn.PLAN_RECURRENT)
+
+    def step(i):
+        committed, inactive = pairs[i % sets]
+        gdn.gdn_replay_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu, out, num_slots=P, read_slots=committed,
+                                      write_slots=inactive, initial_state=pool, replay_pool=pool,
+                                      prev_state_update=caps[(i + 1) % 2], state_update=caps[i % 2],
+                                      state_update_capacity=cap, accepted=acc, accepted_host=acc_host,
+                                      cu_seqlens_host=host_cu, plan=gdn.PLAN_RECURRENT)
+        gdn.gdn_publish_slots(committed, inactive)
+
+    _log(f"pooled fused replay+verify+publish: R={R} T=4 Hv={Hv} slots={P}")
+    ms = _time_steps(torch, step, args.steps, args.warmup)
+    per_call = _per_call(torch, step, 50, args.warmup + args.steps)
+    io = 2
+    nbytes = (2 * state_bytes + int(acc_host.sum()) * W * 4 + R * cap * W * 4 + 2 * N * Hk * Dk * io
+              + 2 * N * Hv * Dv * io + 2 * N * Hv * 4 + 2 * Hv * 4 + (R + 1) * 4 + R * 4 + 2 * R * 4
+              + 4 * R * 4)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "per_call": per_call,
+            "config": {"requests": R, "draft_tokens": 4, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                       "capacity": cap, "accepted": acc_host.tolist(), "pool_slots": P},
+            "roofline": {"bound": "hbm", "kernel": "gdn_replay_verify+gdn_publish",
+                         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("spec_step_pooled_fused"),
+                         "algorithmic_bytes_per_step": nbytes}}
+
+
 def prefill_flops(lengths, Hk, Hv, D, chunk=64):
     """MFMA flops of the chunked prefill as the method computes it: per chunk of L
     tokens, Hk * 4 L^2 D (Q K^T and K K^T, once per key head) + Hv * (4 L^2 D +
@@ -622,7 +683,8 @@ def main():
     ap.add_argument("--workload", default="all",
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
                              "decode_effective_dense", "conv_prefill", "conv_decode",
-                             "spec_step_pooled", "spec_step_fused", "decode_kmajor", "hbm_copy"],
+                             "spec_step_pooled", "spec_step_fused", "spec_step_pooled_fused", "decode_kmajor",
+                             "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="length of each oracle CPU-baseline sample (0 skips them)")
@@ -648,6 +710,7 @@ def main():
               "conv_decode": lambda: run_conv(args, torch, gdn, "conv_decode"),
               "spec_step_pooled": lambda: run_spec_step_pooled(args, torch, gdn),
               "spec_step_fused": lambda: run_spec_step_fused(args, torch, gdn),
+              "spec_step_pooled_fused": lambda: run_spec_step_pooled_fused(args, torch, gdn),
               "decode_kmajor": lambda: run_decode_kmajor(args, torch, gdn),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
@@ -664,6 +727,7 @@ def main():
             "conv_decode": run_conv(args, torch, gdn, "conv_decode"),
             "spec_step_pooled": run_spec_step_pooled(args, torch, gdn),
             "spec_step_fused": run_spec_step_fused(args, torch, gdn),
+            "spec_step_pooled_fused": run_spec_step_pooled_fused(args, torch, gdn),
             "decode_kmajor": run_decode_kmajor(args, torch, gdn),
         }
     if args.cpu_seconds > 0:

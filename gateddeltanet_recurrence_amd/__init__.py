@@ -13,7 +13,7 @@ from .binding import (  # noqa: F401
     GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIAS, GDN_ERR_CAPACITY,
     GDN_ERR_WORKSPACE, GDN_ERR_PLAN, GDN_ERR_RULE, GDN_ERR_HIP, GDN_ERR_SCRATCH, GdnParams, GdnTensors,
     lib, library_path, gdn_abi_version, gdn_strerror, gdn_forward, gdn_forward_workspace_bytes,
-    gdn_resolve_plan, gdn_replay, gdn_replay_forward, capsule_width, make_params,
+    gdn_resolve_plan, gdn_replay, gdn_replay_forward, gdn_replay_forward_pooled, capsule_width, make_params,
     CONV_SILU, CONV_NONE, GdnConvParams, GdnConvTensors, gdn_conv_forward, gdn_conv_replay,
     GdnSlots, gdn_forward_pooled, gdn_replay_pooled, gdn_conv_forward_pooled, gdn_conv_replay_pooled,
     gdn_publish_slots, gdn_forward_no_alloc, NO_ALLOC_SCRATCH_BYTES,

@@ -117,6 +117,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_forward_pooled.restype = ctypes.c_int
         L.gdn_replay_pooled.argtypes = [ctypes.POINTER(GdnParams), vp, vp, vp, vp, vp, sp, vp]
         L.gdn_replay_pooled.restype = ctypes.c_int
+        L.gdn_replay_forward_pooled.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors), sp, vp,
+                                                vp, vp, vp, vp]
+        L.gdn_replay_forward_pooled.restype = ctypes.c_int
         L.gdn_conv_forward_pooled.argtypes = [ctypes.POINTER(GdnConvParams),
                                               ctypes.POINTER(GdnConvTensors), sp, vp]
         L.gdn_conv_forward_pooled.restype = ctypes.c_int
@@ -254,6 +257,19 @@ def gdn_replay_forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, pre
                                 accepted_host=accepted_host), **kw)
 
 
+def gdn_replay_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, num_slots: int,
+                              prev_state_update, accepted, replay_pool, read_slots=None, write_slots=None,
+                              read_slots_host=None, write_slots_host=None, accepted_host=None, **kw) -> int:
+    """gdn_replay_forward_pooled of include/gdn_pool.h: initial_state and replay_pool
+    are pools [P, Hv, Dv, Dk] (may be one tensor); request r replays from slot
+    read_slots[r] into slot write_slots[r] and verifies from it."""
+    pool = dict(num_slots=num_slots, read_slots=read_slots, write_slots=write_slots,
+                read_slots_host=read_slots_host, write_slots_host=write_slots_host)
+    return _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, pool=pool,
+                    replay=dict(prev=prev_state_update, accepted=accepted, state=replay_pool,
+                                accepted_host=accepted_host), **kw)
+
+
 def gdn_forward_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, num_slots: int,
                        read_slots=None, write_slots=None, read_slots_host=None,
                        write_slots_host=None, **kw) -> int:
@@ -332,9 +348,9 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
                       _ptr(output), _ptr(state_update), _ptr(capture_count))
     where = "gdn_forward_pooled" if pool is not None else "gdn_forward"
     if replay is not None:
-        if pool is not None or no_alloc or workspace is not None:
-            raise ValueError("gdn_replay_forward takes no pool and no workspace")
-        where = "gdn_replay_forward"
+        if no_alloc or workspace is not None:
+            raise ValueError("gdn_replay_forward takes no workspace")
+        where = "gdn_replay_forward" if pool is None else "gdn_replay_forward_pooled"
         _need(replay["prev"], "prev_state_update",
               (R, state_update_capacity, capsule_width(Hk, Hv, Dk, Dv)), torch.float32)
         _need(replay["accepted"], "accepted", (R,), torch.int32)
@@ -342,9 +358,16 @@ def _forward(q, k, v, a, b, A_log, dt_bias, cu_seqlens, output, *, initial_state
         acc_host, acc_host_ptr = _host_i32(replay["accepted_host"])
         if acc_host is not None and acc_host.shape != (R,):
             raise ValueError("accepted_host must have R entries")
-        st = lib().gdn_replay_forward(ctypes.byref(params), ctypes.byref(tens), _ptr(replay["prev"]),
-                                      _ptr(replay["accepted"]), acc_host_ptr, _ptr(replay["state"]),
-                                      _stream_handle(stream))
+        if pool is None:
+            st = lib().gdn_replay_forward(ctypes.byref(params), ctypes.byref(tens), _ptr(replay["prev"]),
+                                          _ptr(replay["accepted"]), acc_host_ptr, _ptr(replay["state"]),
+                                          _stream_handle(stream))
+        else:
+            sl, keep = _slots(R, **pool)
+            st = lib().gdn_replay_forward_pooled(ctypes.byref(params), ctypes.byref(tens), ctypes.byref(sl),
+                                                 _ptr(replay["prev"]), _ptr(replay["accepted"]), acc_host_ptr,
+                                                 _ptr(replay["state"]), _stream_handle(stream))
+            del keep
         del acc_host
     elif no_alloc:
         where = "gdn_forward_no_alloc"

@@ -264,6 +264,8 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
       return GDN_ERR_NULL;
     if (p->state_layout != GDN_STATE_V_MAJOR) return GDN_ERR_SHAPE;
     if (!aligned16(rp->state)) return GDN_ERR_SHAPE;
+    // with pools the write slots address the replayed state; no final state then
+    if (slots != nullptr && t->final_state != nullptr) return GDN_ERR_SHAPE;
     if (rp->accepted_host != nullptr)
       for (int64_t r = 0; r < rv.R; ++r)
         if (rp->accepted_host[r] < 0 || rp->accepted_host[r] > rv.cap) return GDN_ERR_CAPACITY;
@@ -301,7 +303,10 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
   const size_t Dk = (size_t)rv.Dk, Dv = (size_t)rv.Dv;
   const size_t W = Hv + Hk * Dk + Hv * Dv;
   SlotPlan sp;
-  st = plan_slots(slots, rv.R, t->initial_state != nullptr && t->initial_state == t->final_state, &sp);
+  // the pool written (the final state, or the replayed state of a fused step) may be
+  // the pool read
+  const float* write_pool = rp != nullptr ? rp->state : t->final_state;
+  st = plan_slots(slots, rv.R, t->initial_state != nullptr && t->initial_state == write_pool, &sp);
   if (st != GDN_OK) return st;
   const size_t state_bytes = (sp.P > 0 ? (size_t)sp.P : R) * Hv * Dv * Dk * 4;
   const Span inputs[] = {
@@ -339,8 +344,10 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     if (fin.overlaps(init)) return GDN_ERR_ALIAS;
     for (const Span& o : {out, fin, cap, dst})
       if (o.overlaps(prev) || o.overlaps(acc)) return GDN_ERR_ALIAS;
-    for (const Span& o : {out, fin, cap, init})
+    for (const Span& o : {out, fin, cap})
       if (o.overlaps(dst)) return GDN_ERR_ALIAS;
+    // one pool for the committed and the inactive slots (distinct slots), or disjoint banks
+    if (init.overlaps(dst) && !(sp.P > 0 && rp->state == t->initial_state)) return GDN_ERR_ALIAS;
     for (const Span& i : inputs)
       if (dst.overlaps(i)) return GDN_ERR_ALIAS;
   }
@@ -561,6 +568,14 @@ int gdn_replay_forward(const gdn_params* p, const gdn_tensors* t, const float* p
                        void* stream) {
   const FusedReplay rp{prev_state_update, accepted, accepted_host, replay_state};
   return forward_impl(p, t, nullptr, nullptr, 0, stream, &rp);
+}
+
+int gdn_replay_forward_pooled(const gdn_params* p, const gdn_tensors* t, const gdn_slots* slots,
+                              const float* prev_state_update, const int32_t* accepted,
+                              const int32_t* accepted_host, float* replay_pool, void* stream) {
+  if (slots == nullptr) return GDN_ERR_NULL;
+  const FusedReplay rp{prev_state_update, accepted, accepted_host, replay_pool};
+  return forward_impl(p, t, slots, nullptr, 0, stream, &rp);
 }
 
 int gdn_replay(int32_t R, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t capacity,

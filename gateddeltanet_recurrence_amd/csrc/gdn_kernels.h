@@ -37,9 +37,10 @@ struct RecurrentArgs {
   int32_t k_major;              // states stored [.., Dk, Dv] (else V-major [.., Dv, Dk])
   int32_t gated;                // update rule applies the decay alpha (else alpha = 1, a not read)
   int32_t delta;                // update rule writes beta (v - alpha S k^) (else v, b not read)
-  // Fused replay (capsule capture only, V-major, states by request): before the
-  // tokens, the leading accepted[r] rows of replay_capsule are applied to the
-  // initial state and the result is written to replay_state.
+  // Fused replay (capsule capture only, V-major): before the tokens, the leading
+  // accepted[r] rows of replay_capsule are applied to the initial state and the
+  // result is written to replay_state, at the slot final_slots names with pools
+  // (the final state is not written then).
   const float* replay_capsule;  // null: no replay
   const int32_t* accepted;
   float* replay_state;

@@ -336,7 +336,10 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   // staged: stores count with the loads in the wave's memory counter, so stores
   // issued before the staging loads would make the staging wait for them.
   auto store_replayed = [&]() {
-    float* dst = p.replay_state + ((size_t)r * p.Hv + h) * Dv * DK;
+    // the replayed state's slot: the write slot with pools (none: not written)
+    float* dst = state_head(p.replay_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h,
+                            (size_t)Dv * DK);
+    if (dst == nullptr) return;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (!valid[i]) continue;

@@ -62,7 +62,8 @@ extern "C" {
  *    pools (gdn_pool.h).
  * 4: gdn_forward_no_alloc and GDN_ERR_SCRATCH.
  * 5: the update rules GDN_RULE_DELTA, GDN_RULE_GATED and GDN_RULE_LINEAR.
- * 6: gdn_replay_forward (replay and verify in one pass over the committed state). */
+ * 6: gdn_replay_forward (replay and verify in one pass over the committed state)
+ *    and its pooled form gdn_replay_forward_pooled (gdn_pool.h). */
 #define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {

@@ -67,6 +67,18 @@ int gdn_replay_pooled(const gdn_params* params, const float* src_pool, const flo
                       const int32_t* accepted, const int32_t* accepted_host, float* dst_pool,
                       const gdn_slots* slots, void* stream);
 
+/* gdn_replay_forward over a pool: request r's committed state is
+ * tensors->initial_state[read_slots[r]], its replayed state goes to
+ * replay_pool[write_slots[r]] (a write slot outside [0, P) writes nothing), and
+ * the verify runs from that state. tensors->final_state must be NULL (else
+ * GDN_ERR_SHAPE). replay_pool may be the same pool as initial_state (distinct
+ * read and write slots, as for gdn_replay_pooled) or a disjoint one. Otherwise
+ * as gdn_replay_forward: the same bytes as gdn_replay_pooled followed by
+ * gdn_forward_pooled from the write slots, with one read of the committed slots. */
+int gdn_replay_forward_pooled(const gdn_params* params, const gdn_tensors* tensors, const gdn_slots* slots,
+                              const float* prev_state_update, const int32_t* accepted,
+                              const int32_t* accepted_host, float* replay_pool, void* stream);
+
 /* gdn_conv_forward with initial_state and final_state read as pools [P, C, K - 1]. */
 int gdn_conv_forward_pooled(const gdn_conv_params* params, const gdn_conv_tensors* tensors,
                             const gdn_slots* slots, void* stream);

@@ -326,3 +326,26 @@ def test_replay_forward_aliasing():
     t2, prev2, acc2, dst2, _ = _fused_case()
     t2.final_state = t2.initial_state
     assert _fused(p, t2, prev2, acc2, None, dst2) == gdn.GDN_ERR_ALIAS
+
+
+def test_replay_forward_pooled_validation():
+    t, prev, acc, dst, state_bytes = _fused_case()
+    p = _p(capacity=4)
+    L = gdn.lib()
+    sl = gdn.GdnSlots()
+    sl.num_slots = 4
+    assert L.gdn_replay_forward_pooled(ctypes.byref(p), ctypes.byref(t), None, prev, acc, None, dst,
+                                       None) == gdn.GDN_ERR_NULL
+    # a final state is not taken with pools
+    t2, prev2, acc2, dst2, _ = _fused_case()
+    t2.final_state = dst2 + 8 * 4096 * 64
+    assert L.gdn_replay_forward_pooled(ctypes.byref(p), ctypes.byref(t2), ctypes.byref(sl), prev2, acc2, None,
+                                       dst2, None) == gdn.GDN_ERR_SHAPE
+    # one pool: request 1 writes the slot request 0 reads (checked through the mirrors)
+    rd = (ctypes.c_int32 * 2)(0, 1)
+    wr = (ctypes.c_int32 * 2)(2, 0)
+    sl.read_slots, sl.write_slots = FAKE - 8192, FAKE - 4096
+    sl.read_slots_host = ctypes.cast(rd, ctypes.c_void_p)
+    sl.write_slots_host = ctypes.cast(wr, ctypes.c_void_p)
+    assert L.gdn_replay_forward_pooled(ctypes.byref(p), ctypes.byref(t), ctypes.byref(sl), prev, acc, None,
+                                       t.initial_state, None) == gdn.GDN_ERR_ALIAS

@@ -178,3 +178,69 @@ def test_fused_step_spec_workload_chain():
         torch.cuda.synchronize()
         assert torch.equal(dst_a, dst_b) and torch.equal(cap_a, cap_b), step
         bank_a, bank_b, prev_a, prev_b = dst_a, dst_b, cap_a, cap_b
+
+
+def _i32(x):
+    return torch.tensor(np.asarray(x, np.int32), device="cuda")
+
+
+@pytest.mark.parametrize("one_pool", [True, False])
+def test_fused_step_pooled_equals_separate_calls(one_pool):
+    # committed and inactive slots of one pool (or two pools); request 5's write
+    # slot is -1: its replayed state is not written, its verify still runs
+    R, cap, Hk, Hv, D = 6, 4, 2, 4, 128
+    lengths = [4, 4, 3, 4, 0, 2]
+    inp, prev, accepted = _step_inputs(lengths, Hk, Hv, D, D, "f16", cap, seed=1010)
+    P = 2 * R
+    rng = np.random.default_rng(1011)
+    committed_np = rng.permutation(P)[:R].astype(np.int32)
+    inactive_np = np.array([s for s in range(P) if s not in set(committed_np.tolist())], np.int32)
+    rng.shuffle(inactive_np)
+    inactive_np[5] = -1
+    pool_np = rng.standard_normal((P, Hv, D, D)).astype(np.float32) * np.float32(0.05)
+    pool_np[committed_np] = inp["initial_state"]
+    d = device_inputs(inp, torch)
+    W = gdn.capsule_width(Hk, Hv, D, D)
+    acc = dev(accepted, torch)
+    _case(f"fused pooled step one_pool={one_pool} accepted={accepted.tolist()}")
+
+    def run(fused):
+        pool = dev(pool_np, torch)
+        dst_pool = pool if one_pool else dev(pool_np, torch)
+        capsule = torch.full((R, cap, W), -7.0, dtype=torch.float32, device="cuda")
+        out = torch.full((inp["v"].shape[0], Hv, D), float("nan"), dtype=torch.float16, device="cuda")
+        common = dict(state_update=capsule, state_update_capacity=cap, cu_seqlens_host=inp["cu_seqlens"])
+        if fused:
+            gdn.gdn_replay_forward_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                          d["cu_seqlens"], out, num_slots=P, read_slots=_i32(committed_np),
+                                          write_slots=_i32(inactive_np), read_slots_host=committed_np,
+                                          write_slots_host=inactive_np, initial_state=pool,
+                                          prev_state_update=prev, accepted=acc, accepted_host=accepted,
+                                          replay_pool=dst_pool, **common)
+        else:
+            gdn.gdn_replay_pooled(pool, prev, acc, dst_pool, num_k_heads=Hk, state_update_capacity=cap,
+                                  read_slots=_i32(committed_np), write_slots=_i32(inactive_np),
+                                  read_slots_host=committed_np, write_slots_host=inactive_np,
+                                  accepted_host=accepted)
+            # the verify of request 5 (no written slot) reads the replay the fused call
+            # keeps in registers: give the separate call that state through a scratch pool
+            scratch = torch.zeros((R, Hv, D, D), dtype=torch.float32, device="cuda")
+            gdn.gdn_replay(d["initial_state"], prev, acc, scratch, num_k_heads=Hk, state_update_capacity=cap)
+            gdn.gdn_forward(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], d["cu_seqlens"],
+                            out, initial_state=scratch, **common)
+        torch.cuda.synchronize()
+        return pool, dst_pool, out, capsule
+
+    pa, da, oa, ca = run(False)
+    pb, db, ob, cb = run(True)
+    assert torch.equal(oa, ob) and torch.equal(ca, cb)
+    assert torch.equal(da, db)
+    got = db.cpu().numpy()
+    # committed slots untouched; the slot of the request without a write slot too
+    assert np.array_equal(pb.cpu().numpy()[committed_np], inp["initial_state"])
+    untouched = [s for s in range(P) if s not in set(inactive_np.tolist())]
+    assert np.array_equal(got[untouched], pool_np[untouched])
+    ref = O.gdn_replay(inp["initial_state"], prev.cpu().numpy(), accepted, Hk, Hv, D, D)
+    for r in range(R):
+        if inactive_np[r] >= 0:
+            assert rel_l2(got[inactive_np[r]], ref[r]) <= 1e-5, r
