@@ -48,35 +48,38 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "f8ea22181ba998c4", "fetch_kib": 66997.5, "write_kib": 131620.4,
-        "bytes": 271965694},
+        "sha256_16": "6216aa733eaad176", "fetch_kib": 66994.5, "write_kib": 131621.5,
+        "bytes": 271960675},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "f8ea22181ba998c4", "fetch_kib": 66993.1, "write_kib": 131607.8,
-        "bytes": 271943879},
+        "sha256_16": "6216aa733eaad176", "fetch_kib": 66990.1, "write_kib": 131614.3,
+        "bytes": 271944386},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "19be5ad2968d9cc6", "fetch_kib": 66938.1, "write_kib": 131687.3,
-        "bytes": 271912622},
+        "sha256_16": "866621969ee55f07", "fetch_kib": 66938.1, "write_kib": 131671.5,
+        "bytes": 271896430},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "49b88f346ce267d6", "fetch_kib": 51114.8, "write_kib": 52118.8,
-        "bytes": 158034097},
+        "sha256_16": "fa23c94b4a0b1d3c", "fetch_kib": 51118.3, "write_kib": 52110.9,
+        "bytes": 158033189},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "f8ea22181ba998c4", "fetch_kib": 26510.5, "write_kib": 52095.7,
-        "bytes": 107629796},
+        "sha256_16": "6216aa733eaad176", "fetch_kib": 26521.4, "write_kib": 52095.1,
+        "bytes": 107651601},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "49b88f346ce267d6", "fetch_kib": 51117.2, "write_kib": 52114.6,
-        "bytes": 158034790},
+        "sha256_16": "fa23c94b4a0b1d3c", "fetch_kib": 51120.7, "write_kib": 52107.2,
+        "bytes": 158034397},
+    "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "fa23c94b4a0b1d3c", "fetch_kib": 26523.9, "write_kib": 52088.0,
+        "bytes": 107649318},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "b288356a98f7d4c2", "fetch_kib": 366618.3, "write_kib": 240719.2,
-        "bytes": 997196802},
+        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 367975.8, "write_kib": 240719.3,
+        "bytes": 999976559},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "b288356a98f7d4c2", "fetch_kib": 669603.6, "write_kib": 724475.0,
-        "bytes": 2112965885},
+        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 669602.3, "write_kib": 724664.7,
+        "bytes": 2113157641},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "94de7a18eed7959c", "fetch_kib": 131140.9, "write_kib": 246423.9,
-        "bytes": 520866775},
+        "sha256_16": "5d26c730968d1b84", "fetch_kib": 131216.5, "write_kib": 246410.1,
+        "bytes": 521007494},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "94de7a18eed7959c", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950330},
+        "sha256_16": "5d26c730968d1b84", "fetch_kib": 3716.6, "write_kib": 7168.0,
+        "bytes": 14950329},
 }
 
 
