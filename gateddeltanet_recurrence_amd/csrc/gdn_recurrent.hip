@@ -20,6 +20,8 @@
 //   u  = beta (v - alpha pk)
 //   o  = alpha pq + u (k^ . q^)      ( = S_new q^ )
 //   S  = alpha S + u k^^T
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -272,6 +274,27 @@ struct StageSmem {
   float alpha[kStageTokens], beta[kStageTokens], kq[kStageTokens];
 };
 
+// For the verify with fp16 I/O at Dk = 128 a token group's raw inputs come into
+// LDS by direct loads that one wave issues before its state loads: k, q (a
+// 256-byte row each), the block's value rows (a 256-byte window) and the raw
+// gates. They complete ahead of the state, so the normalisation runs while the
+// state is in flight and no register holds a staged value across the state loads
+// (verify 18.1 -> 17.1 us).
+template <int DK>
+struct StageSmemDma : StageSmem<DK> {
+  _Float16 rawk[kStageTokens][128];
+  _Float16 rawq[kStageTokens][128];
+  _Float16 rawv[kStageTokens][128];
+  float rawa[64], rawb[64];
+};
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void lds_dma16(rsrc_t r, void* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, void* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voffset, 0, 0, 0);
+}
+
 template <typename IO, int DK, int NI, bool CAPTURE, bool REPLAY>
 __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, int waves_per_block,
                                                       int blocks_per_head) {
@@ -279,9 +302,15 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   constexpr int LPR = L::LPR, E = L::E, V4 = L::V4, RI = L::RI, RW = RI * NI;
   constexpr int TPT = 16;                 // threads per staged token
   constexpr int EPT = DK / TPT;           // elements per staging thread
-  __shared__ StageSmem<DK> sm;
+  // (the fused replay keeps the plain staging: with both its registers exceed
+  // three waves per SIMD, and capped there it was no faster)
+  constexpr bool kDma = std::is_same<IO, _Float16>::value && DK == 128 && !REPLAY;
+  __shared__ std::conditional_t<kDma, StageSmemDma<DK>, StageSmem<DK>> sm;
 
   const int tid = threadIdx.x;
+  // the workgroup size from the argument: blockDim.x is a load from the dispatch
+  // packet, and its wait would also wait for the state loads in flight
+  const int nthreads = 64 * waves_per_block;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int rg = lane / LPR;
@@ -304,19 +333,54 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
                                 (size_t)Dv * DK);
   float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
 
-  // ---- state rows into registers (issued before any staging)
+  const bool gated = p.gated != 0, delta = p.delta != 0;
+  // raw inputs of the group of tokens ts .. ts + nt - 1 into LDS (wave 0; tokens
+  // past nt read zero, past the ranges)
+  auto issue_dma = [&](int ts, int nt) {
+    if constexpr (kDma) {
+      if (wave != 0 || nt <= 0) return;
+      const int kbytes = ((nt - 1) * p.Hk * DK + DK) * 2;
+      const rsrc_t rk = make_rsrc(static_cast<const _Float16*>(p.k) + ((size_t)ts * p.Hk + g) * DK, kbytes);
+      const rsrc_t rq = make_rsrc(static_cast<const _Float16*>(p.q) + ((size_t)ts * p.Hk + g) * DK, kbytes);
+      const rsrc_t rv = make_rsrc(static_cast<const _Float16*>(p.v) + ((size_t)ts * p.Hv + h) * Dv + block_row0,
+                                  ((nt - 1) * p.Hv * Dv + (Dv - block_row0)) * 2);
+      // four tokens per load: lane l takes 16 bytes of token 4 i + l / 16
+      for (int i = 0; i < (nt + 3) / 4; ++i) {
+        const int j = 4 * i + (lane >> 4);
+        lds_dma16(rk, &sm.rawk[4 * i][0], j * p.Hk * DK * 2 + 16 * (lane & 15));
+        lds_dma16(rq, &sm.rawq[4 * i][0], j * p.Hk * DK * 2 + 16 * (lane & 15));
+        lds_dma16(rv, &sm.rawv[4 * i][0], j * p.Hv * Dv * 2 + 16 * (lane & 15));
+      }
+      if (gated) lds_dma4(make_rsrc(p.a + (size_t)ts * p.Hv + h, ((nt - 1) * p.Hv + 1) * 4), sm.rawa, lane * p.Hv * 4);
+      if (delta) lds_dma4(make_rsrc(p.b + (size_t)ts * p.Hv + h, ((nt - 1) * p.Hv + 1) * 4), sm.rawb, lane * p.Hv * 4);
+    }
+  };
+  issue_dma(t0, min(kStageTokens, t1 - t0));
+  int m_rep = 0;
+  if constexpr (REPLAY) m_rep = min(max(p.accepted[r], 0), p.capacity);
+  // the state loads stay behind the direct loads (the waits below count on it)
+  if constexpr (kDma) __builtin_amdgcn_sched_barrier(0);
+
+  // ---- state rows into registers (issued before any other staging)
   float S[NI][E];
   bool valid[NI];
   load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
+  if constexpr (kDma) __builtin_amdgcn_sched_barrier(0);
 
+  // the previous step's accepted capsule prefix, applied in registers with the
+  // arithmetic of gdn_replay (S = alpha S + u k^, one fused multiply-add of
+  // alpha S onto the product u k^ per element), then the result to the inactive
+  // bank: replay_state equals what gdn_replay writes, bit for bit. With the
+  // direct-load staging it runs after the normalisation, which it would
+  // otherwise hold behind the state loads.
+  // the previous step's accepted capsule prefix, applied in registers with the
+  // arithmetic of gdn_replay (S = alpha S + u k^, one fused multiply-add of
+  // alpha S onto the product u k^ per element): replay_state equals what
+  // gdn_replay writes, bit for bit. Its loads follow the state loads, and it
+  // runs as soon as they land (the staged tokens are then in LDS already).
   if constexpr (REPLAY) {
-    // the previous step's accepted capsule prefix, applied in registers with the
-    // arithmetic of gdn_replay (S = alpha S + u k^, one fused multiply-add of
-    // alpha S onto the product u k^ per element), then the result to the
-    // inactive bank: replay_state equals what gdn_replay writes, bit for bit
-    const int m = min(max(p.accepted[r], 0), p.capacity);
     const float* caprow = p.replay_capsule + (size_t)r * p.capacity * p.capsule_width;
-    for (int j = 0; j < m; ++j, caprow += p.capsule_width) {
+    for (int j = 0; j < m_rep; ++j, caprow += p.capsule_width) {
       const float alpha = caprow[h];
       float kv[E];
 #pragma unroll
@@ -352,7 +416,6 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   };
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
-  const bool gated = p.gated != 0, delta = p.delta != 0;
   const float expA = (gnone || !gated) ? 0.f : expf(p.A_log[h]);
   const float dtb = (gnone || !gated) ? 0.f : p.dt_bias[h];
   const IO* __restrict__ qp = static_cast<const IO*>(p.q);
@@ -371,21 +434,51 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   // The registers hold S / gam: a token's decay then folds into gam and the
   // update is one fused multiply-add per element, S/gam += (u/gam) k^.
   float gam = 1.f;
-  for (int ts = t0; ts < t1; ts += kStageTokens) {
+  // One token group; the first is called outside the loop, so that the compiler's
+  // flush of the memory counter at the entry of a loop that reads the state comes
+  // only after that group's staging.
+  auto group = [&](int ts) {
     const int nt = min(kStageTokens, t1 - ts);
+    if constexpr (kDma) {
+      // the group's raw inputs are in LDS once wave 0's direct loads land: for the
+      // first group they precede exactly NI V4 state loads, so waiting until no
+      // more than those are pending leaves the state in flight
+      if (ts != t0) issue_dma(ts, nt);
+      if (ts == t0) {
+        constexpr int kState = NI * V4;
+        static_assert(kState < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_s_waitcnt((kState & 15) | (7 << 4) | (15 << 8) | ((kState >> 4) << 14));
+      } else {
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));      // vmcnt(0)
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
     // ---- stage: 16 threads per token normalise k and q and form the gates (a
     // workgroup of fewer than four waves takes several passes)
-    for (int j = tid / TPT; j < nt; j += (int)blockDim.x / TPT) {
+    for (int j = tid / TPT; j < nt; j += nthreads / TPT) {
       const int part = tid % TPT;
       {
         const int t = ts + j;
-        const IO* krow = kp + ((size_t)t * p.Hk + g) * DK + part * EPT;
-        const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK + part * EPT;
         float kv[EPT], qv[EPT];
+        if constexpr (kDma) {
+          static_assert(EPT == 8, "one 16-byte LDS read per thread");
+          const half8_t k8 = *reinterpret_cast<const half8_t*>(&sm.rawk[j][part * EPT]);
+          const half8_t q8 = *reinterpret_cast<const half8_t*>(&sm.rawq[j][part * EPT]);
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          kv[e] = IoOps<IO>::load1(krow + e);
-          qv[e] = IoOps<IO>::load1(qrow + e);
+          for (int e = 0; e < EPT; ++e) {
+            kv[e] = (float)k8[e];
+            qv[e] = (float)q8[e];
+          }
+        } else {
+          const IO* krow = kp + ((size_t)t * p.Hk + g) * DK + part * EPT;
+          const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK + part * EPT;
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) {
+            kv[e] = IoOps<IO>::load1(krow + e);
+            qv[e] = IoOps<IO>::load1(qrow + e);
+          }
         }
         float ssk = 0.f, ssq = 0.f, skq = 0.f;
 #pragma unroll
@@ -405,21 +498,32 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
           sm.qh[j][part * EPT + e] = qv[e] * rq;
         }
         if (part == 0) {
-          sm.alpha[j] = gated ? gate_alpha(p.a[(size_t)t * p.Hv + h], gnone, expA, dtb) : 1.f;
-          sm.beta[j] = delta ? gate_beta(p.b[(size_t)t * p.Hv + h], gnone) : 1.f;
+          float ra = 0.f, rb = 0.f;
+          if constexpr (kDma) {
+            ra = sm.rawa[j];
+            rb = sm.rawb[j];
+          } else {
+            if (gated) ra = p.a[(size_t)t * p.Hv + h];
+            if (delta) rb = p.b[(size_t)t * p.Hv + h];
+          }
+          sm.alpha[j] = gated ? gate_alpha(ra, gnone, expA, dtb) : 1.f;
+          sm.beta[j] = delta ? gate_beta(rb, gnone) : 1.f;
           sm.kq[j] = skq * rk * rq;
         }
       }   // a token's 16 lanes are one aligned DPP row group: active or idle together
     }
     // this block's value rows of every staged token
-    for (int idx = tid; idx < nt * block_rows; idx += blockDim.x) {
+    for (int idx = tid; idx < nt * block_rows; idx += nthreads) {
       const int jj = idx / block_rows, rr = idx % block_rows;
       const int row = block_row0 + rr;
-      sm.v[jj][rr] = row < Dv ? IoOps<IO>::load1(vp + ((size_t)(ts + jj) * p.Hv + h) * Dv + row) : 0.f;
+      if constexpr (kDma)
+        sm.v[jj][rr] = row < Dv ? (float)sm.rawv[jj][rr] : 0.f;
+      else
+        sm.v[jj][rr] = row < Dv ? IoOps<IO>::load1(vp + ((size_t)(ts + jj) * p.Hv + h) * Dv + row) : 0.f;
     }
     __syncthreads();
     if constexpr (REPLAY) {
-      if (ts == t0) store_replayed();              // the registers still hold the replayed state
+      if (ts == t0) store_replayed();              // the registers hold the replayed state
     }
 
     for (int j = 0; j < nt; ++j) {
@@ -512,7 +616,9 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
       gam = keep_scaled ? gn : 1.f;
     }
     __syncthreads();   // the next group's staging overwrites the staged tokens
-  }
+  };
+  if (t1 > t0) group(t0);
+  for (int ts = t0 + kStageTokens; ts < t1; ts += kStageTokens) group(ts);
   if constexpr (REPLAY) {
     if (t1 == t0) store_replayed();                // no tokens: the replayed state as it is
   }
