@@ -1,7 +1,8 @@
 """GPU: the hot path captured in HIP graphs (torch.cuda.CUDAGraph) and replayed.
 
 A serving loop captures a decode step, or the speculative step (verify, replay
-of the accepted prefix, publication of the slot arrays), once and replays it.
+of the accepted prefix, publication of the slot arrays; or the fused step and
+the publication), once and replays it.
 Each graph here is replayed several times, with the program's own eager work
 and synchronisations between the replays, and every replay is compared bit for
 bit with the same calls made eagerly from the same starting state (the kernels
@@ -139,6 +140,69 @@ def test_speculative_step_graph_publishes_on_the_device():
             _case(f"speculative step: trial {trial} replay {k}")
             g.replay()
             _same(_snapshot(watched), refs[k], f"trial {trial} replay {k}")
+
+
+def test_fused_speculative_step_graph():
+    # the fused step over the pool (replay of the previous capsule's accepted
+    # prefix from the committed slots into the inactive ones, verify from that
+    # state) and the publication; two steps per graph, since the capsule buffers
+    # alternate: replay k of the graph must equal 2 (k + 1) eager steps
+    T, R, cap, Hk, Hv, D = 4, 6, 4, 2, 4, 128
+    inp = make_inputs([T] * R, Hk, Hv, D, D, "f16", seed=503, capacity=cap)
+    P = 2 * R
+    rng = np.random.default_rng(8)
+    perm = rng.permutation(P)
+    committed_np, inactive_np = perm[:R], perm[R:]
+    pool_np = rng.standard_normal((P, Hv, D, D)).astype(np.float32) * 0.05
+    pool_np[committed_np] = inp["initial_state"]
+    accepted = _i32([0, 1, 2, 3, 4, 2])
+    accepted_host = np.array([0, 1, 2, 3, 4, 2], np.int32)
+    pool0 = dev(pool_np, torch)
+    pool = pool0.clone()
+    committed, inactive = _i32(committed_np), _i32(inactive_np)
+    d = {n: dev(inp[n], torch) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    out = torch.empty((T * R, Hv, D), dtype=torch.float16, device="cuda")
+    W = gdn.capsule_width(Hk, Hv, D, D)
+    caps0 = [torch.randn((R, cap, W), device="cuda") * 0.01 for _ in range(2)]
+    caps = [c.clone() for c in caps0]
+
+    def one(k):
+        gdn.gdn_replay_forward_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                      d["cu_seqlens"], out, num_slots=P, read_slots=committed,
+                                      write_slots=inactive, initial_state=pool, replay_pool=pool,
+                                      prev_state_update=caps[(k + 1) % 2], state_update=caps[k % 2],
+                                      state_update_capacity=cap, accepted=accepted, accepted_host=accepted_host,
+                                      cu_seqlens_host=inp["cu_seqlens"], plan=gdn.PLAN_RECURRENT)
+        gdn.gdn_publish_slots(committed, inactive)
+
+    def two():
+        one(0)
+        one(1)
+
+    def reset():
+        pool.copy_(pool0)
+        committed.copy_(_i32(committed_np))
+        inactive.copy_(_i32(inactive_np))
+        for c, c0 in zip(caps, caps0):
+            c.copy_(c0)
+        out.zero_()
+        torch.cuda.synchronize()
+
+    watched = [pool, committed, inactive, out, caps[0], caps[1]]
+    _case("fused speculative step: eager reference, 3 x 2 steps")
+    refs = []
+    for _ in range(3):
+        two()
+        refs.append(_snapshot(watched))
+    reset()
+    _case("fused speculative step: capture")
+    g = _capture(two)
+    for trial in range(2):
+        reset()
+        for k in range(3):
+            _case(f"fused speculative step: trial {trial} replay {k}")
+            g.replay()
+            _same(_snapshot(watched), refs[k], f"fused trial {trial} replay {k}")
 
 
 def test_chunked_prefill_graph():
