@@ -48,38 +48,38 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6216aa733eaad176", "fetch_kib": 66994.5, "write_kib": 131621.5,
-        "bytes": 271960675},
+        "sha256_16": "6acf8da7f7265014", "fetch_kib": 66997.5, "write_kib": 131624.3,
+        "bytes": 271969837},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6216aa733eaad176", "fetch_kib": 66990.1, "write_kib": 131614.3,
-        "bytes": 271944386},
+        "sha256_16": "6acf8da7f7265014", "fetch_kib": 66993.1, "write_kib": 131615.8,
+        "bytes": 271952119},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "866621969ee55f07", "fetch_kib": 66938.1, "write_kib": 131671.5,
-        "bytes": 271896430},
+        "sha256_16": "866621969ee55f07", "fetch_kib": 66938.1, "write_kib": 131672.4,
+        "bytes": 271897410},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fa23c94b4a0b1d3c", "fetch_kib": 51118.3, "write_kib": 52110.9,
-        "bytes": 158033189},
+        "sha256_16": "d5b4105ea84f605f", "fetch_kib": 51131.3, "write_kib": 52117.3,
+        "bytes": 158066495},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6216aa733eaad176", "fetch_kib": 26521.4, "write_kib": 52095.1,
-        "bytes": 107651601},
+        "sha256_16": "6acf8da7f7265014", "fetch_kib": 26532.9, "write_kib": 52095.6,
+        "bytes": 107675686},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fa23c94b4a0b1d3c", "fetch_kib": 51120.7, "write_kib": 52107.2,
-        "bytes": 158034397},
+        "sha256_16": "d5b4105ea84f605f", "fetch_kib": 51133.8, "write_kib": 52114.9,
+        "bytes": 158069071},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fa23c94b4a0b1d3c", "fetch_kib": 26523.9, "write_kib": 52088.0,
-        "bytes": 107649318},
+        "sha256_16": "d5b4105ea84f605f", "fetch_kib": 26534.8, "write_kib": 52094.7,
+        "bytes": 107678572},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 367975.8, "write_kib": 240719.3,
-        "bytes": 999976559},
+        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 367812.4, "write_kib": 240719.0,
+        "bytes": 999642185},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 669602.3, "write_kib": 724664.7,
-        "bytes": 2113157641},
+        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 669763.2, "write_kib": 725681.3,
+        "bytes": 2114528870},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "5d26c730968d1b84", "fetch_kib": 131216.5, "write_kib": 246410.1,
-        "bytes": 521007494},
+        "sha256_16": "5d26c730968d1b84", "fetch_kib": 130542.3, "write_kib": 246424.8,
+        "bytes": 519642147},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "5d26c730968d1b84", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950329},
+        "sha256_16": "5d26c730968d1b84", "fetch_kib": 3716.6, "write_kib": 7168.4,
+        "bytes": 14950783},
 }
 
 
