@@ -20,7 +20,8 @@
 // LDS; the update M = alpha M + k^ u^T is lane-local. LK = 8 (full 128-byte
 // lines per row segment) took the batched decode from 69 us (LK = 4, 64-byte
 // segments) to 51 us; DKS = 2 at Dk = 128 (104 VGPRs, four waves per SIMD,
-// against 150 and three) to 49.5 us.
+// against 150 and three) to 49.5 us; range-checked loads with no branch around
+// them (every load issued before the first wait) to 48.1 us.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -39,23 +40,51 @@ namespace {
 constexpr int kDppRowRor4 = 0x124;    // row_ror:4 within a row of 16 lanes
 constexpr int kDppRowRor8 = 0x128;    // row_ror:8
 
+// x[l] + x[l ^ 16] and x[l] + x[l ^ 32] on the VALU: v_permlane16_swap exchanges
+// the odd 16-lane rows of one register with the even rows of another, and
+// v_permlane32_swap the upper half of one with the lower half of the other. With
+// x in both, every lane holds the two values of its pair, one in each result;
+// their sum is the pair's sum in every lane (a + b = b + a exactly).
+__device__ __forceinline__ float swap16_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the lanes of each class l mod LK (LK = 4 or 8 lanes per row
-// segment); every lane gets its class total. All 64 lanes must be active.
+// segment); every lane gets its class total. All 64 lanes must be active. Only
+// DPP and lane swaps: no LDS permutes.
 template <int LK>
 __device__ __forceinline__ float column_sum(float x) {
   if constexpr (LK == 4) x += dpp<kDppRowRor4>(x);
   x += dpp<kDppRowRor8>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  x = swap16_sum(x);
+  return swap32_sum(x);
 }
 
-__device__ __forceinline__ float4_t load_state4_nt(const float* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(p));
-}
 __device__ __forceinline__ void store_state4_nt(float* p, float4_t x) {
   __builtin_nontemporal_store(x, reinterpret_cast<float4_t*>(p));
 }
+
+// Four consecutive values of a row as floats through a range-checked buffer
+// load: past the range they read as zero, so lanes past Dv need no branch.
+template <typename IO> struct Io4Buf;
+template <> struct Io4Buf<float> {
+  static __device__ __forceinline__ float4_t load(rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+  }
+};
+template <> struct Io4Buf<_Float16> {
+  static __device__ __forceinline__ float4_t load(rsrc_t r, int byte_off) {
+    const half4_t h = buf_load_h4(r, byte_off);
+    return float4_t{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+  }
+};
 
 template <typename IO> struct Io4Store;
 template <> struct Io4Store<float> {
@@ -145,13 +174,22 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
   float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, head_elems);
 
   const int row0 = dk0 + NR * rg;                  // this lane's first state row
+  // The state rows come in through range-checked buffer loads over the head's
+  // Dk x Dv floats (an empty range without an initial state); a lane past Dv
+  // reads from the end of the range, i.e. zeros. With no branch around them the
+  // k, q, v and gate loads that follow are issued before any of them is waited
+  // for; a branch on the lane's validity had compiled to a wait for every load
+  // (the state included) before the gates were even requested.
+  const int head_bytes = (int)(head_elems * 4);
   float4_t M[NR];
-  if (init != nullptr && cvalid) {
+  {
+    const rsrc_t rs = make_rsrc(init != nullptr ? static_cast<const void*>(init) : p.q,
+                                init != nullptr ? head_bytes : 0);
+    const int lane_off = cvalid ? (row0 * Dv + col) * 4 : head_bytes;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) M[i] = load_state4_nt(init + (size_t)(row0 + i) * Dv + col);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) M[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NR; ++i)
+      M[i] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + i * Dv * 4, 0,
+                                                                                kBufferNontemporal));
   }
 
   const bool gnone = p.gate_none != 0;             // A_log, dt_bias may be null then
@@ -174,10 +212,13 @@ __device__ __forceinline__ void kmajor_body(const RecurrentArgs& p, int waves_pe
     float kv[NR], qv[NR];
     load_run<IO, NR>(kp + ((size_t)t * p.Hk + g) * DK + row0, kv);
     load_run<IO, NR>(qp + ((size_t)t * p.Hk + g) * DK + row0, qv);
-    const float4_t vv = cvalid ? IoOps<IO>::load4(vp + ((size_t)t * p.Hv + h) * Dv + col)
-                               : float4_t{0.f, 0.f, 0.f, 0.f};
-    const float at = gated ? p.a[(size_t)t * p.Hv + h] : 0.f;
-    const float bt = delta ? p.b[(size_t)t * p.Hv + h] : 0.f;
+    const int io = (int)sizeof(IO);
+    const float4_t vv = Io4Buf<IO>::load(make_rsrc(vp + ((size_t)t * p.Hv + h) * Dv, Dv * io),
+                                         cvalid ? col * io : Dv * io);
+    // the gates of an absent rule term read as zero from an empty range
+    const size_t gi = (size_t)t * p.Hv + h;
+    const float at = buf_load_f32(make_rsrc(gated ? static_cast<const void*>(p.a + gi) : p.q, gated ? 4 : 0), 0);
+    const float bt = buf_load_f32(make_rsrc(delta ? static_cast<const void*>(p.b + gi) : p.q, delta ? 4 : 0), 0);
 
     float ssk = 0.f, ssq = 0.f, skq = 0.f;
     float4_t pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
