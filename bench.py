@@ -660,6 +660,64 @@ def run_conv(args, torch, gdn, name):
                          "traffic": measured_traffic(name), "algorithmic_bytes_per_step": nbytes}}
 
 
+def run_conv_decode_fused(args, torch, gdn):
+    """The batched decode step with its causal convolution fused in
+    (gdn_conv_decode_forward): 64 requests x 1 token, Hk=16, Hv=32, D=128, fp16, the
+    convolution over the 8192 concatenated q, k, v channels (K = 4, SiLU). The GDN
+    state is updated in place over rotating banks; the convolution's carried inputs
+    go from one bank to the next (they cannot be updated in place). Beside it, the
+    same step as the two separate calls it replaces (gdn_conv_forward, then
+    gdn_forward on contiguous q, k, v), timed the same way."""
+    from gdn_workloads import workload_inputs
+    from gdn_workloads.conv import conv_channels, make_conv_inputs
+    inp = workload_inputs("batched_decode")
+    N, Hk, Dk = inp["q"].shape
+    Hv, Dv = inp["v"].shape[1:]
+    R = len(inp["cu_seqlens"]) - 1
+    C, K = conv_channels(Hk, Hv, Dk, Dv), 4
+    cinp = make_conv_inputs([1] * R, C, K, "f16", seed=1)
+    q, k, v, a, b = (_dev(inp[n], torch) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias, cu = _dev(inp["A_log"], torch), _dev(inp["dt_bias"], torch), _dev(inp["cu_seqlens"], torch)
+    x, w, bias = (_dev(cinp[n], torch) for n in ("x", "weight", "bias"))
+    state_bytes = R * Hv * Dv * Dk * 4
+    n_banks = max(2, -(-BANK_TARGET_BYTES // state_bytes))
+    banks = [_dev(inp["initial_state"], torch) for _ in range(n_banks)]
+    cbanks = [_dev(cinp["initial_state"], torch) for _ in range(n_banks + 1)]
+    out = torch.empty((N, Hv, Dv), dtype=q.dtype, device="cuda")
+    y = torch.empty_like(x)
+    host_cu = inp["cu_seqlens"]
+
+    def fused(i):
+        s = banks[i % n_banks]
+        gdn.gdn_conv_decode_forward(x, w, bias, a, b, A_log, dt_bias, cu, out, num_k_heads=Hk, head_k_dim=Dk,
+                                    conv_initial_state=cbanks[i % (n_banks + 1)],
+                                    conv_final_state=cbanks[(i + 1) % (n_banks + 1)],
+                                    initial_state=s, final_state=s, cu_seqlens_host=host_cu)
+
+    def separate(i):
+        s = banks[i % n_banks]
+        cs = cbanks[i % (n_banks + 1)]
+        gdn.gdn_conv_forward(x, w, bias, cu, y, initial_state=cs, final_state=cs, cu_seqlens_host=host_cu)
+        gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=s, final_state=s,
+                        cu_seqlens_host=host_cu, plan=gdn.PLAN_RECURRENT)
+
+    _log(f"decode with the convolution fused: R={R} Hv={Hv} C={C} banks={n_banks}")
+    ms = _time_steps(torch, fused, args.steps, args.warmup)
+    ms_sep = _time_steps(torch, separate, args.steps, args.warmup)
+    nbytes = (decode_bytes(inp) - 2 * N * Hk * Dk * 2 - N * Hv * Dv * 2      # q, k, v not read
+              + N * C * 2 + 2 * R * C * (K - 1) * 4 + C * K * 4 + C * 4)     # x, carried inputs, filter
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"value": N / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"tokens": N, "requests": R, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv, "io_dtype": "f16",
+                       "channels": C, "kernel_size": K, "activation": "silu", "state_banks": n_banks,
+                       "separate_calls_ms_per_step": ms_sep,
+                       "separate_calls": "gdn_conv_forward (8192 channels, in place) + gdn_forward (decode)"},
+            "roofline": {"bound": "hbm", "kernel": "gdn_conv_decode", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("conv_decode_fused"),
+                         "algorithmic_bytes_per_step": nbytes}}
+
+
 def run_hbm_copy(args, torch):
     """Reference stream: device-to-device copies of 128 MiB fp32 buffers rotated over
     banks (read 128 MiB + write 128 MiB per step). Its known byte count calibrates
@@ -687,7 +745,7 @@ def main():
                     choices=["all", "batched_decode", "spec_verify_replay", "ragged_prefill", "long_prefill",
                              "decode_effective_dense", "conv_prefill", "conv_decode",
                              "spec_step_pooled", "spec_step_fused", "spec_step_pooled_fused", "decode_kmajor",
-                             "hbm_copy"],
+                             "conv_decode_fused", "hbm_copy"],
                     help="all: the decode line plus the other workloads under 'workloads'")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="length of each oracle CPU-baseline sample (0 skips them)")
@@ -715,6 +773,7 @@ def main():
               "spec_step_fused": lambda: run_spec_step_fused(args, torch, gdn),
               "spec_step_pooled_fused": lambda: run_spec_step_pooled_fused(args, torch, gdn),
               "decode_kmajor": lambda: run_decode_kmajor(args, torch, gdn),
+              "conv_decode_fused": lambda: run_conv_decode_fused(args, torch, gdn),
               "hbm_copy": lambda: run_hbm_copy(args, torch)}[args.workload]
         res = fn()
         print(json.dumps({"metric": METRIC, "workload": args.workload, **res}), flush=True)
@@ -732,6 +791,7 @@ def main():
             "spec_step_fused": run_spec_step_fused(args, torch, gdn),
             "spec_step_pooled_fused": run_spec_step_pooled_fused(args, torch, gdn),
             "decode_kmajor": run_decode_kmajor(args, torch, gdn),
+            "conv_decode_fused": run_conv_decode_fused(args, torch, gdn),
         }
     if args.cpu_seconds > 0:
         from gdn_workloads import workload_inputs

@@ -16,5 +16,5 @@ from .binding import (  # noqa: F401
     gdn_resolve_plan, gdn_replay, gdn_replay_forward, gdn_replay_forward_pooled, capsule_width, make_params,
     CONV_SILU, CONV_NONE, GdnConvParams, GdnConvTensors, gdn_conv_forward, gdn_conv_replay,
     GdnSlots, gdn_forward_pooled, gdn_replay_pooled, gdn_conv_forward_pooled, gdn_conv_replay_pooled,
-    gdn_publish_slots, gdn_forward_no_alloc, NO_ALLOC_SCRATCH_BYTES,
+    gdn_publish_slots, gdn_forward_no_alloc, NO_ALLOC_SCRATCH_BYTES, GdnConvFused, gdn_conv_decode_forward,
 )

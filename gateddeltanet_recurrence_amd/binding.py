@@ -23,7 +23,7 @@ PLAN_AUTO, PLAN_RECURRENT, PLAN_CHUNK = 0, 1, 2
 RULE_GATED_DELTA, RULE_DELTA, RULE_GATED, RULE_LINEAR = 0, 1, 2, 3
 GATE_RAW, GATE_NONE = 0, 1
 STATE_V_MAJOR, STATE_K_MAJOR = 0, 1
-ABI_VERSION = 6          # the struct layouts below match this version of include/gdn.h
+ABI_VERSION = 7          # the struct layouts below match this version of include/gdn.h
 CONV_SILU, CONV_NONE = 0, 1
 
 
@@ -65,6 +65,11 @@ class GdnConvTensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "weight", "bias", "cu_seqlens", "cu_seqlens_host", "initial_state", "final_state",
         "output", "state_update", "capture_count")]
+
+
+class GdnConvFused(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("mixed", "weight", "bias", "initial_state", "final_state")] + \
+               [("kernel_size", ctypes.c_int32), ("activation", ctypes.c_int32)]
 
 
 class GdnSlots(ctypes.Structure):
@@ -125,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv_forward_pooled.restype = ctypes.c_int
         L.gdn_conv_replay_pooled.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sp, vp]
         L.gdn_conv_replay_pooled.restype = ctypes.c_int
+        L.gdn_conv_decode_forward.argtypes = [ctypes.POINTER(GdnParams), ctypes.POINTER(GdnTensors),
+                                              ctypes.POINTER(GdnConvFused), vp]
+        L.gdn_conv_decode_forward.restype = ctypes.c_int
         L.gdn_publish_slots.argtypes = [i32, vp, vp, vp]
         L.gdn_publish_slots.restype = ctypes.c_int
         L.gdn_strerror.argtypes = [ctypes.c_int]
@@ -543,6 +551,69 @@ def _conv_forward(x, weight, bias, cu_seqlens, output, *, initial_state=None,
     del host_cu
     if check and st != GDN_OK:
         raise GDNError(st, "gdn_conv_forward_pooled" if pool is not None else "gdn_conv_forward")
+    return st
+
+
+def gdn_conv_decode_forward(mixed, conv_weight, conv_bias, a, b, A_log, dt_bias, cu_seqlens, output, *,
+                            num_k_heads: int, head_k_dim: int, conv_initial_state=None, conv_final_state=None,
+                            conv_activation: int = CONV_SILU, initial_state=None, final_state=None,
+                            cu_seqlens_host=None, scale: float = 0.0, plan: int = PLAN_AUTO,
+                            update_rule: int = RULE_GATED_DELTA, gate_activation: int = GATE_RAW,
+                            num_reqs: Optional[int] = None, stream=None, check: bool = True) -> int:
+    """gdn_conv_decode_forward of include/gdn_conv.h on torch tensors; returns the status.
+
+    mixed [N, Cm] (dense layout, cu_seqlens None: [R, S, Cm]) float16 or float32,
+    Cm = 2 Hk Dk + Hv Dv with the channels [q | k | v]; conv_weight [Cm, K] and
+    conv_bias [Cm] float32; conv states [R, Cm, K - 1] float32; output [N, Hv, Dv]
+    (or [R, S, Hv, Dv]) gives Hv and Dv; the rest as gdn_forward (V-major states).
+    """
+    torch = _torch()
+    if cu_seqlens is None and mixed.dim() == 3:
+        if num_reqs is None:
+            num_reqs = mixed.shape[0]
+        mixed = mixed.reshape(-1, mixed.shape[2])
+        output = output.reshape(-1, output.shape[2], output.shape[3])
+        a, b = (x.reshape(-1, x.shape[-1]) if x is not None else None for x in (a, b))
+    N, Cm = mixed.shape
+    Hv, Dv = output.shape[1], output.shape[2]
+    Hk, Dk = int(num_k_heads), int(head_k_dim)
+    if Cm != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError(f"mixed has {Cm} channels, expected 2 Hk Dk + Hv Dv = {2 * Hk * Dk + Hv * Dv}")
+    K = conv_weight.shape[1]
+    if cu_seqlens is None:
+        if num_reqs is None:
+            raise ValueError("the dense layout (cu_seqlens None) needs num_reqs or [R, S, Cm] inputs")
+        R = int(num_reqs)
+    else:
+        R = cu_seqlens.shape[0] - 1
+    io = mixed.dtype
+    _need(mixed, "mixed", (N, Cm))
+    _need(output, "output", (N, Hv, Dv), io)
+    _need(conv_weight, "conv_weight", (Cm, K), torch.float32)
+    _need(conv_bias, "conv_bias", (Cm,), torch.float32)
+    _need(conv_initial_state, "conv_initial_state", (R, Cm, K - 1), torch.float32)
+    _need(conv_final_state, "conv_final_state", (R, Cm, K - 1), torch.float32)
+    _need(a, "a", (N, Hv), torch.float32)
+    _need(b, "b", (N, Hv), torch.float32)
+    _need(A_log, "A_log", (Hv,), torch.float32)
+    _need(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _need(cu_seqlens, "cu_seqlens", (R + 1,), torch.int32)
+    _need(initial_state, "initial_state", (R, Hv, Dv, Dk), torch.float32)
+    _need(final_state, "final_state", (R, Hv, Dv, Dk), torch.float32)
+    host_cu, host_cu_ptr = _host_i32(cu_seqlens_host)
+    if host_cu is not None and host_cu.shape != (R + 1,):
+        raise ValueError("cu_seqlens_host must have R + 1 entries")
+    params = make_params(N, R, Hk, Hv, Dk, Dv, _io_code(io), scale=scale, plan=plan, update_rule=update_rule,
+                         gate_activation=gate_activation)
+    tens = GdnTensors(None, None, None, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens),
+                      host_cu_ptr, _ptr(initial_state), _ptr(final_state), _ptr(output), None, None)
+    conv = GdnConvFused(_ptr(mixed), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_initial_state),
+                        _ptr(conv_final_state), int(K), int(conv_activation))
+    st = lib().gdn_conv_decode_forward(ctypes.byref(params), ctypes.byref(tens), ctypes.byref(conv),
+                                       _stream_handle(stream))
+    del host_cu
+    if check and st != GDN_OK:
+        raise GDNError(st, "gdn_conv_decode_forward")
     return st
 
 

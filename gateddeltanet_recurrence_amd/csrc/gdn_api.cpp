@@ -250,13 +250,21 @@ struct FusedReplay {
 
 static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slots* slots,
                         void* workspace, size_t workspace_bytes, void* stream,
-                        const FusedReplay* rp = nullptr) {
+                        const FusedReplay* rp = nullptr, const gdn_conv_fused* cv = nullptr) {
   Resolved rv;
   int st = check_params(p, &rv);
   if (st != GDN_OK) return st;
   if (t == nullptr) return GDN_ERR_NULL;
   const bool capsule = t->state_update != nullptr;
   if (capsule && rv.cap == 0) return GDN_ERR_CAPACITY;   // a capsule needs rows
+  if (cv != nullptr) {
+    // the fused convolution: q, k, v come from it; V-major decode, no capsule
+    if (cv->activation != GDN_CONV_SILU && cv->activation != GDN_CONV_NONE) return GDN_ERR_RULE;
+    if (cv->kernel_size != gdn::kConvFusedK) return GDN_ERR_SHAPE;
+    if (t->q != nullptr || t->k != nullptr || t->v != nullptr) return GDN_ERR_SHAPE;
+    if (capsule || p->state_layout != GDN_STATE_V_MAJOR) return GDN_ERR_SHAPE;
+    if (p->plan == GDN_PLAN_CHUNK) return GDN_ERR_PLAN;
+  }
   if (rp != nullptr) {
     // the fused step: a verify (capsule) from the replayed committed V-major bank
     if (!capsule || t->initial_state == nullptr || rp->capsule == nullptr || rp->accepted == nullptr ||
@@ -281,9 +289,11 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
   const bool gated = p->update_rule == GDN_RULE_GATED_DELTA || p->update_rule == GDN_RULE_GATED;
   const bool delta = p->update_rule == GDN_RULE_GATED_DELTA || p->update_rule == GDN_RULE_DELTA;
   if (gated && !gate_none && (t->A_log == nullptr || t->dt_bias == nullptr)) return GDN_ERR_NULL;
-  if (rv.N > 0 && (t->q == nullptr || t->k == nullptr || t->v == nullptr || (gated && t->a == nullptr) ||
-                   (delta && t->b == nullptr) || t->output == nullptr))
+  const bool qkv_given = cv == nullptr;
+  if (rv.N > 0 && ((qkv_given && (t->q == nullptr || t->k == nullptr || t->v == nullptr)) ||
+                   (gated && t->a == nullptr) || (delta && t->b == nullptr) || t->output == nullptr))
     return GDN_ERR_NULL;
+  if (cv != nullptr && rv.N > 0 && (cv->mixed == nullptr || cv->weight == nullptr)) return GDN_ERR_NULL;
 
   // alignment of vector-accessed buffers (the K-major kernels move v and the
   // output in 4-column vectors)
@@ -292,8 +302,14 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
                             k_major ? t->output : nullptr};
   for (const void* ptr : vec_ptrs)
     if (ptr != nullptr && !aligned16(ptr)) return GDN_ERR_SHAPE;
+  if (cv != nullptr) {
+    const void* conv_vec[] = {cv->mixed, cv->weight, cv->initial_state, cv->final_state};
+    for (const void* ptr : conv_vec)
+      if (ptr != nullptr && !aligned16(ptr)) return GDN_ERR_SHAPE;
+  }
 
-  st = resolve_plan(p, t->cu_seqlens_host, capsule, &rv, dense);
+  // the fused convolution runs with the token-recurrent kernel only
+  st = resolve_plan(p, t->cu_seqlens_host, capsule || cv != nullptr, &rv, dense);
   if (st != GDN_OK) return st;
   const int32_t dense_len = dense ? (int32_t)(rv.N / rv.R) : 0;
 
@@ -351,6 +367,22 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     for (const Span& i : inputs)
       if (dst.overlaps(i)) return GDN_ERR_ALIAS;
   }
+  const size_t Cm = 2 * Hk * Dk + Hv * Dv;         // channels of the fused convolution
+  if (cv != nullptr) {
+    // its carried inputs are read by every workgroup of a key head and written by
+    // one, so the new ones go to another buffer; nothing else overlaps them
+    const size_t K = (size_t)cv->kernel_size;
+    const Span c_in[] = {Span(cv->mixed, N * Cm * io), Span(cv->weight, Cm * K * 4), Span(cv->bias, Cm * 4),
+                         Span(cv->initial_state, R * Cm * (K - 1) * 4)};
+    const Span c_fin(cv->final_state, R * Cm * (K - 1) * 4);
+    for (const Span& o : {out, fin, cap, ws, c_fin})
+      for (const Span& i : c_in)
+        if (o.overlaps(i)) return GDN_ERR_ALIAS;
+    for (const Span& o : {out, fin, cap, ws, init})
+      if (c_fin.overlaps(o)) return GDN_ERR_ALIAS;
+    for (const Span& i : inputs)
+      if (c_fin.overlaps(i)) return GDN_ERR_ALIAS;
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -369,6 +401,11 @@ static int forward_impl(const gdn_params* p, const gdn_tensors* t, const gdn_slo
     a.gated = gated ? 1 : 0; a.delta = delta ? 1 : 0;
     if (rp != nullptr) {
       a.replay_capsule = rp->capsule; a.accepted = rp->accepted; a.replay_state = rp->state;
+    }
+    if (cv != nullptr) {
+      a.mixed = cv->mixed; a.conv_weight = cv->weight; a.conv_bias = cv->bias;
+      a.conv_init = cv->initial_state; a.conv_final = cv->final_state;
+      a.conv_channels = (int32_t)Cm; a.conv_silu = cv->activation == GDN_CONV_SILU ? 1 : 0;
     }
     err = k_major ? gdn::launch_recurrent_kmajor(a, p->io_dtype, s) : gdn::launch_recurrent(a, p->io_dtype, s);
   } else {
@@ -592,6 +629,11 @@ int gdn_replay_pooled(const gdn_params* p, const float* src_pool, const float* c
   return replay_impl(p->num_reqs, p->num_k_heads, p->num_v_heads, p->head_k_dim, p->head_v_dim,
                      p->state_update_capacity, src_pool, capsule, accepted, accepted_host, dst_pool, slots,
                      p->state_layout == GDN_STATE_K_MAJOR, stream);
+}
+
+int gdn_conv_decode_forward(const gdn_params* p, const gdn_tensors* t, const gdn_conv_fused* conv, void* stream) {
+  if (conv == nullptr) return GDN_ERR_NULL;
+  return forward_impl(p, t, nullptr, nullptr, 0, stream, nullptr, conv);
 }
 
 int gdn_conv_forward(const gdn_conv_params* p, const gdn_conv_tensors* t, void* stream) {

@@ -68,6 +68,18 @@ __device__ __forceinline__ float decay_from_raw(float a, float expA, float dt_bi
 
 __device__ __forceinline__ float sigmoid_f(float b) { return 1.0f / (1.0f + expf(-b)); }
 
+// SiLU(z) = z * sigmoid(z) after the causal convolution, with the hardware
+// base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each) in
+// place of a library exp and an IEEE division: the convolution does little else
+// per element, so those would make it bound by vector ALU issue rather than by
+// HBM. Limits: z -> -inf gives 2^(+inf) = inf, 1/inf = 0, result -0; z -> +inf
+// gives 1/1, result z. The convolution kernels and the decode with the fused
+// convolution share it, so both round alike.
+__device__ __forceinline__ float silu(float z) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
 // Precomputed effective decay (gate activation none), clamped to [0, 1], the
 // range of the raw form.
 __device__ __forceinline__ float effective_decay(float a) { return fminf(fmaxf(a, 0.f), 1.f); }

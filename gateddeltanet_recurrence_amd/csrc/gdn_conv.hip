@@ -51,16 +51,6 @@ template <> struct Io4<_Float16> {
   }
 };
 
-// SiLU(z) = z * sigmoid(z), with the hardware base-2 exponential and reciprocal
-// (v_exp_f32, v_rcp_f32, about 1 ulp each) in place of a library exp and an IEEE
-// division: the convolution does little else per element, so those would make it
-// bound by vector ALU issue rather than by HBM. Limits: z -> -inf gives
-// 2^(+inf) = inf, 1/inf = 0, result -0; z -> +inf gives 1/1, result z.
-__device__ __forceinline__ float silu(float z) {
-  constexpr float kLog2e = 1.4426950408889634f;
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
-}
-
 // Request that holds packed token t (t < N, the same t in every thread of the
 // workgroup): the last r with seq_start(r) <= t, which skips empty requests.
 // The workgroup searches cooperatively: each round, its threads test evenly

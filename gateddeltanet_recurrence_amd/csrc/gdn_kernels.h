@@ -44,7 +44,22 @@ struct RecurrentArgs {
   const float* replay_capsule;  // null: no replay
   const int32_t* accepted;
   float* replay_state;
+  // Fused causal convolution (decode, V-major, no capture): q, k, v are the
+  // convolution of `mixed` [N, conv_channels] (channels [q | k | v], conv_channels
+  // = 2 Hk Dk + Hv Dv) with kernel size kConvFusedK, conv_weight [C, K],
+  // conv_bias [C] or null, carried inputs conv_init [R, C, K - 1] (null: zeros),
+  // the last K - 1 inputs written to conv_final (null: not written).
+  const void* mixed;            // may be null when there are no tokens
+  const float* conv_weight;
+  const float* conv_bias;
+  const float* conv_init;
+  float* conv_final;
+  int32_t conv_channels;        // 0: no fused convolution (q, k, v read as given)
+  int32_t conv_silu;            // SiLU after the convolution (else the identity)
 };
+
+// Kernel size of the fused convolution.
+constexpr int kConvFusedK = 4;
 
 struct ReplayArgs {
   const float* src;

@@ -101,7 +101,197 @@ __device__ __forceinline__ void load_state_rows(const float* init, const void* a
   }
 }
 
-template <typename IO, int DK, int NI, bool CAPTURE>
+// ---- The causal convolution fused into the decode (RecurrentArgs::mixed).
+// A workgroup of (request r, value head h, state rows rb0 .. rb0 + nrow - 1)
+// convolves, per token, the channels it reads: the q and k channels of key
+// head g (DK each) and the v channels of its rows, in groups of 4 adjacent
+// channels; group i lands at floats 4 i .. 4 i + 3 of the token's LDS slot,
+// which is [q (DK) | k (DK) | v rows].
+template <int DK>
+__device__ __forceinline__ int conv_channel(const RecurrentArgs& p, int g, int h, int rb0, int gi) {
+  if (gi < DK / 4) return g * DK + 4 * gi;
+  if (gi < DK / 2) return p.Hk * DK + g * DK + 4 * (gi - DK / 4);
+  return 2 * p.Hk * DK + h * p.Dv + rb0 + 4 * (gi - DK / 2);
+}
+
+// Entry idx of e = [carried inputs (K - 1), x of the request's tokens] for the
+// 4 channels c .. c + 3: from the carried state below K - 1 (an empty range
+// without one reads zeros), else from packed token t0 + idx - (K - 1).
+template <typename IO>
+__device__ __forceinline__ float4_t conv_entry(const RecurrentArgs& p, rsrc_t rs, int c, int t0, int idx) {
+  constexpr int K = kConvFusedK;
+  if (idx < K - 1) {
+    float4_t v;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) v[ch] = buf_load_f32(rs, ((c + ch) * (K - 1) + idx) * 4);
+    return v;
+  }
+  return IoOps<IO>::load4(static_cast<const IO*>(p.mixed) + (size_t)(t0 + idx - (K - 1)) * p.conv_channels + c);
+}
+
+__device__ __forceinline__ rsrc_t conv_state_rsrc(const RecurrentArgs& p, int r) {
+  constexpr int K = kConvFusedK;
+  const int bytes = p.conv_channels * (K - 1) * 4;
+  return p.conv_init != nullptr ? make_rsrc(p.conv_init + (size_t)r * p.conv_channels * (K - 1), bytes)
+                                : make_rsrc(p.mixed, 0);
+}
+
+// Token j of the request: y = act(bias + sum_{m<K} w[m] e[j + m]), the
+// multiply-adds in the convolution kernel's order (oldest entry first), rounded
+// to the I/O type as the convolution's stored output is, into dst.
+template <typename IO, int DK>
+__device__ __forceinline__ void conv_token(const RecurrentArgs& p, int r, int g, int h, int rb0, int nrow,
+                                           int t0, int j, int nthreads, float* dst, int gi0) {
+  constexpr int K = kConvFusedK;
+  const int ngroups = DK / 2 + nrow / 4;
+  const rsrc_t rs = conv_state_rsrc(p, r);
+  const rsrc_t rb = make_rsrc(p.conv_bias != nullptr ? static_cast<const void*>(p.conv_bias) : p.mixed,
+                              p.conv_bias != nullptr ? p.conv_channels * 4 : 0);
+  for (int gi = gi0; gi < ngroups; gi += nthreads) {
+    const int c = conv_channel<DK>(p, g, h, rb0, gi);
+    // weights [C, K]: 4 K consecutive floats, channel-major
+    float wf[4 * K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const float4_t x = *reinterpret_cast<const float4_t*>(p.conv_weight + (size_t)c * K + 4 * i);
+      wf[4 * i + 0] = x.x; wf[4 * i + 1] = x.y; wf[4 * i + 2] = x.z; wf[4 * i + 3] = x.w;
+    }
+    float4_t e[K];
+#pragma unroll
+    for (int m = 0; m < K; ++m) e[m] = conv_entry<IO>(p, rs, c, t0, j + m);
+    float y[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      float z = buf_load_f32(rb, (c + ch) * 4);
+#pragma unroll
+      for (int m = 0; m < K; ++m) z = fmaf(wf[ch * K + m], e[m][ch], z);
+      y[ch] = (float)(IO)(p.conv_silu ? silu(z) : z);
+    }
+    *reinterpret_cast<float4_t*>(dst + 4 * gi) = float4_t{y[0], y[1], y[2], y[3]};
+  }
+}
+
+// The inputs of the first token for the thread's first channel group (group
+// threadIdx.x), loaded before the state rows so that they arrive first (loads
+// complete in issue order) and the convolution runs while the state is in
+// flight; the carried inputs also serve the final write. Range-checked buffer
+// loads with no branch: a thread without a group reads past the ranges, i.e.
+// zeros (unused), and without a token the input row's range is empty.
+struct ConvFirst {
+  float4_t w[kConvFusedK];        // the 4 K weights of channels c .. c + 3, [C, K] order
+  float4_t st[kConvFusedK - 1];   // their 4 (K - 1) carried inputs, [C, K - 1] order
+  float4_t x;                     // their inputs at the first token
+  float4_t bias;
+};
+
+template <typename IO, int DK>
+__device__ __forceinline__ ConvFirst conv_first_load(const RecurrentArgs& p, int r, int g, int h, int rb0,
+                                                     int nrow, int t0, bool has_token) {
+  constexpr int K = kConvFusedK;
+  const int C = p.conv_channels;
+  const int gi = threadIdx.x;
+  const bool on = gi < DK / 2 + nrow / 4;
+  const int c = on ? conv_channel<DK>(p, g, h, rb0, gi) : 0;
+  ConvFirst f;
+  const rsrc_t rw = make_rsrc(p.conv_weight != nullptr ? static_cast<const void*>(p.conv_weight) : p.mixed,
+                              p.conv_weight != nullptr ? C * K * 4 : 0);
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    f.w[i] = __builtin_bit_cast(float4_t,
+                                __builtin_amdgcn_raw_buffer_load_b128(rw, on ? c * K * 4 + 16 * i : C * K * 4, 0, 0));
+  const rsrc_t rs = conv_state_rsrc(p, r);
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i)
+    f.st[i] = __builtin_bit_cast(
+        float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, on ? c * (K - 1) * 4 + 16 * i : C * (K - 1) * 4, 0, 0));
+  const int io = (int)sizeof(IO);
+  const rsrc_t rx = make_rsrc(p.mixed != nullptr ? static_cast<const IO*>(p.mixed) + (size_t)t0 * C : nullptr,
+                              (p.mixed != nullptr && has_token) ? C * io : 0);
+  if constexpr (sizeof(IO) == 2) {
+    const half4_t hx = buf_load_h4(rx, on ? c * io : C * io);
+    f.x = float4_t{(float)hx.x, (float)hx.y, (float)hx.z, (float)hx.w};
+  } else {
+    f.x = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, on ? c * io : C * io, 0, 0));
+  }
+  const rsrc_t rb = make_rsrc(p.conv_bias != nullptr ? static_cast<const void*>(p.conv_bias) : p.mixed,
+                              p.conv_bias != nullptr ? C * 4 : 0);
+  f.bias = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, on ? c * 4 : C * 4, 0, 0));
+  return f;
+}
+
+// The first token's output of the thread's first group from f: the window is
+// the carried inputs then the token's input, the arithmetic that of conv_token.
+template <typename IO, int DK>
+__device__ __forceinline__ void conv_first_compute(const RecurrentArgs& p, const ConvFirst& f, int nrow,
+                                                   float* dst) {
+  constexpr int K = kConvFusedK;
+  const int gi = threadIdx.x;
+  if (gi >= DK / 2 + nrow / 4) return;
+  float wf[4 * K], sf[4 * (K - 1)];
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wf[4 * i + jj] = f.w[i][jj];
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) sf[4 * i + jj] = f.st[i][jj];
+  float y[4];
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    float z = f.bias[ch];
+#pragma unroll
+    for (int m = 0; m < K - 1; ++m) z = fmaf(wf[ch * K + m], sf[ch * (K - 1) + m], z);
+    z = fmaf(wf[ch * K + K - 1], f.x[ch], z);
+    y[ch] = (float)(IO)(p.conv_silu ? silu(z) : z);
+  }
+  *reinterpret_cast<float4_t*>(dst + 4 * gi) = float4_t{y[0], y[1], y[2], y[3]};
+}
+
+// The request's new carried inputs, e[L .. L + K - 2] (L tokens), for the
+// channels this workgroup owns: its v rows, and the q and k channels of g when
+// own_qk (one workgroup per key head and request). With at most one token the
+// thread's first group takes them from the inputs fetched for that token.
+template <typename IO, int DK>
+__device__ __forceinline__ void conv_final_write(const RecurrentArgs& p, int r, int g, int h, int rb0, int nrow,
+                                                 int t0, int L, bool own_qk, int nthreads, const ConvFirst& cf) {
+  constexpr int K = kConvFusedK;
+  const int ngroups = DK / 2 + nrow / 4;
+  const rsrc_t rs = conv_state_rsrc(p, r);
+  float* fin = p.conv_final + (size_t)r * p.conv_channels * (K - 1);
+  for (int gi = threadIdx.x; gi < ngroups; gi += nthreads) {
+    if (gi < DK / 2 && !own_qk) continue;
+    const int c = conv_channel<DK>(p, g, h, rb0, gi);
+    float f[4 * (K - 1)];                          // channel-major: f[ch (K - 1) + m]
+    if (gi == (int)threadIdx.x && L <= 1) {
+      // cf.st holds the carried inputs in this order already; one token shifts them
+      float sf[4 * (K - 1)];
+#pragma unroll
+      for (int i = 0; i < K - 1; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sf[4 * i + jj] = cf.st[i][jj];
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m)
+          f[ch * (K - 1) + m] = L == 0 ? sf[ch * (K - 1) + m]
+                                       : (m + 1 < K - 1 ? sf[ch * (K - 1) + m + 1] : cf.x[ch]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < K - 1; ++m) {
+        const float4_t v = conv_entry<IO>(p, rs, c, t0, L + m);
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) f[ch * (K - 1) + m] = v[ch];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < K - 1; ++i)
+      *reinterpret_cast<float4_t*>(fin + (size_t)c * (K - 1) + 4 * i) =
+          float4_t{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
+  }
+}
+
+template <typename IO, int DK, int NI, bool CAPTURE, bool CONV = false>
 __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves_per_block,
                                                int blocks_per_head) {
   using L = RecLayout<DK>;
@@ -129,6 +319,12 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
                                 (size_t)Dv * DK);
   float* fin = state_head(p.final_state, state_slot(p.final_slots, r, p.num_slots), p.Hv, h, (size_t)Dv * DK);
 
+  // fused convolution: the first token's inputs are requested before the state
+  const int rb0 = blk * waves_per_block * RW;
+  const int nrow = min(waves_per_block * RW, Dv - rb0);
+  ConvFirst cfirst;
+  if constexpr (CONV) cfirst = conv_first_load<IO, DK>(p, r, g, h, rb0, nrow, t0, t1 > t0);
+
   // ---- state rows into registers
   float S[NI][E];
   bool valid[NI];
@@ -150,22 +346,51 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     ncap = min(t1 - t0, cmax);
   }
 
-  for (int t = t0; t < t1; ++t) {
-    const IO* krow = kp + ((size_t)t * p.Hk + g) * DK;
-    const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK;
+  // fused convolution: a slot per token parity (one barrier per token: a slot is
+  // rewritten two tokens later, after every wave has passed the barrier of the
+  // token in between)
+  constexpr int kConvSlot = CONV ? 2 * DK + GDN_REC_WAVES * RW : 1;
+  __shared__ __attribute__((aligned(16))) float conv_slot[CONV ? 2 : 1][kConvSlot];
+
+  // one token; `first` (a constant at each call) marks the first token of the
+  // segment, whose convolution inputs were fetched ahead of the state
+  auto step = [&](const int t, const bool first) __attribute__((always_inline)) {
     float kv[E], qv[E];
-#pragma unroll
-    for (int j = 0; j < V4; ++j) {
-      const float4_t kx = IoOps<IO>::load4(krow + 4 * c + 4 * LPR * j);
-      const float4_t qx = IoOps<IO>::load4(qrow + 4 * c + 4 * LPR * j);
-      kv[4 * j + 0] = kx.x; kv[4 * j + 1] = kx.y; kv[4 * j + 2] = kx.z; kv[4 * j + 3] = kx.w;
-      qv[4 * j + 0] = qx.x; qv[4 * j + 1] = qx.y; qv[4 * j + 2] = qx.z; qv[4 * j + 3] = qx.w;
-    }
     float vv[NI];
+    if constexpr (CONV) {
+      float* cs = conv_slot[(t - t0) & 1];
+      const int nthreads = 64 * waves_per_block;
+      if (first) {
+        conv_first_compute<IO, DK>(p, cfirst, nrow, cs);
+        conv_token<IO, DK>(p, r, g, h, rb0, nrow, t0, 0, nthreads, cs, threadIdx.x + nthreads);
+      } else {
+        conv_token<IO, DK>(p, r, g, h, rb0, nrow, t0, t - t0, nthreads, cs, threadIdx.x);
+      }
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = min(row_base + i * RI + rg, Dv - 1);     // in bounds; unused past Dv
-      vv[i] = IoOps<IO>::load1(vp + ((size_t)t * p.Hv + h) * Dv + row);
+      for (int j = 0; j < V4; ++j) {
+        const float4_t qx = *reinterpret_cast<const float4_t*>(cs + 4 * c + 4 * LPR * j);
+        const float4_t kx = *reinterpret_cast<const float4_t*>(cs + DK + 4 * c + 4 * LPR * j);
+        kv[4 * j + 0] = kx.x; kv[4 * j + 1] = kx.y; kv[4 * j + 2] = kx.z; kv[4 * j + 3] = kx.w;
+        qv[4 * j + 0] = qx.x; qv[4 * j + 1] = qx.y; qv[4 * j + 2] = qx.z; qv[4 * j + 3] = qx.w;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vv[i] = cs[2 * DK + wave * RW + i * RI + rg];   // unused past Dv
+    } else {
+      const IO* krow = kp + ((size_t)t * p.Hk + g) * DK;
+      const IO* qrow = qp + ((size_t)t * p.Hk + g) * DK;
+#pragma unroll
+      for (int j = 0; j < V4; ++j) {
+        const float4_t kx = IoOps<IO>::load4(krow + 4 * c + 4 * LPR * j);
+        const float4_t qx = IoOps<IO>::load4(qrow + 4 * c + 4 * LPR * j);
+        kv[4 * j + 0] = kx.x; kv[4 * j + 1] = kx.y; kv[4 * j + 2] = kx.z; kv[4 * j + 3] = kx.w;
+        qv[4 * j + 0] = qx.x; qv[4 * j + 1] = qx.y; qv[4 * j + 2] = qx.z; qv[4 * j + 3] = qx.w;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = min(row_base + i * RI + rg, Dv - 1);     // in bounds; unused past Dv
+        vv[i] = IoOps<IO>::load1(vp + ((size_t)t * p.Hv + h) * Dv + row);
+      }
     }
     const float at = gated ? p.a[(size_t)t * p.Hv + h] : 0.f;
     const float bt = delta ? p.b[(size_t)t * p.Hv + h] : 0.f;
@@ -240,6 +465,12 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
         }
       }
     }
+  };
+  if constexpr (CONV) {
+    if (t0 < t1) step(t0, true);
+    for (int t = t0 + 1; t < t1; ++t) step(t, false);
+  } else {
+    for (int t = t0; t < t1; ++t) step(t, false);
   }
 
   if (fin != nullptr) {
@@ -253,6 +484,11 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
         store_state4(fin + (size_t)row * DK + 4 * c + 4 * LPR * j, x);
       }
     }
+  }
+  if constexpr (CONV) {
+    if (p.conv_final != nullptr)
+      conv_final_write<IO, DK>(p, r, g, h, rb0, nrow, t0, t1 - t0, h % p.group == 0 && blk == 0,
+                               64 * waves_per_block, cfirst);
   }
 }
 
@@ -638,10 +874,15 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   }
 }
 
-// Distinct kernel names for the profiler: gdn_decode (no capture) and gdn_capsule.
+// Distinct kernel names for the profiler: gdn_decode (no capture), gdn_conv_decode
+// (the causal convolution fused in), gdn_capsule.
 template <typename IO, int DK, int NI>
 __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_decode(RecurrentArgs p, int wpb, int bph) {
   recurrent_body<IO, DK, NI, false>(p, wpb, bph);
+}
+template <typename IO, int DK, int NI>
+__global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_conv_decode(RecurrentArgs p, int wpb, int bph) {
+  recurrent_body<IO, DK, NI, false, true>(p, wpb, bph);
 }
 template <typename IO, int DK, int NI>
 __global__ void __launch_bounds__(64 * GDN_REC_WAVES) gdn_capsule(RecurrentArgs p, int wpb, int bph) {
@@ -675,8 +916,12 @@ static hipError_t launch_dk(const RecurrentArgs& p, hipStream_t stream) {
                          dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
   } else {
     launch_shape<DK, NI>(p.Dv, &wpb, &bph);
-    hipLaunchKernelGGL((gdn_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
-                       dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+    if (p.conv_channels > 0)
+      hipLaunchKernelGGL((gdn_conv_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+                         dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+    else
+      hipLaunchKernelGGL((gdn_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+                         dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
   }
   return hipGetLastError();
 }

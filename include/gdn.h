@@ -64,7 +64,7 @@ extern "C" {
  * 5: the update rules GDN_RULE_DELTA, GDN_RULE_GATED and GDN_RULE_LINEAR.
  * 6: gdn_replay_forward (replay and verify in one pass over the committed state)
  *    and its pooled form gdn_replay_forward_pooled (gdn_pool.h). */
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum gdn_status {
   GDN_OK = 0,

@@ -37,6 +37,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -95,6 +97,53 @@ int gdn_conv_replay(int32_t num_reqs, int32_t channels, int32_t kernel_size,
                     int32_t state_update_capacity, const float* src_state,
                     const float* state_update, const int32_t* accepted,
                     const int32_t* accepted_host, float* dst_state, void* stream);
+
+/* ---- The convolution fused into the GatedDeltaNet decode.
+ *
+ * In a hybrid layer the convolution's output is exactly the q, k and v the
+ * GatedDeltaNet operator reads ("Add GatedDeltaNet evaluation export for Qwen
+ * hybrid models", Summary: the layer keeps its Q/K/V layout and causal
+ * convolution ahead of the recurrent operator). gdn_conv_decode_forward runs
+ * both in one kernel: every workgroup convolves the channels it needs for each
+ * token in registers and LDS, so q, k and v never go through HBM.
+ *
+ * The convolution runs over the concatenated channels
+ *   mixed[t] = [q (Hk Dk) | k (Hk Dk) | v (Hv Dv)],  Cm = 2 Hk Dk + Hv Dv,
+ * with the semantics of gdn_conv_forward above (kernel size K, weight [Cm, K],
+ * optional bias, SiLU or the identity, K - 1 carried inputs per channel), and
+ * its output, rounded to io_dtype exactly as gdn_conv_forward stores it, is
+ * split into q, k, v for the token recurrence of gdn_forward. The results equal
+ * gdn_conv_forward followed by gdn_forward on the split output, bit for bit. */
+typedef struct gdn_conv_fused {
+  const void* mixed;             /* device, io  [N, Cm] in the token order of the GDN
+                                    call (its cu_seqlens or dense layout); 16-byte
+                                    aligned; may be NULL when N = 0                  */
+  const float* weight;           /* device, f32 [Cm, K]; 16-byte aligned             */
+  const float* bias;             /* device, f32 [Cm], or NULL for zero               */
+  const float* initial_state;    /* device, f32 [R, Cm, K - 1], or NULL for zeros;
+                                    16-byte aligned                                  */
+  float* final_state;            /* device, f32 [R, Cm, K - 1], or NULL (not written);
+                                    16-byte aligned. It must not overlap
+                                    initial_state: several workgroups read a
+                                    channel's carried inputs while one writes them. */
+  int32_t kernel_size;           /* K; only 4 is supported                           */
+  int32_t activation;            /* gdn_conv_activation                              */
+} gdn_conv_fused;
+
+/* One decode (or short-segment) call of the fused pair. params and tensors are
+ * as for gdn_forward, with these differences:
+ *   tensors->q, k, v must be NULL (the convolution supplies them);
+ *   the token-recurrent kernel runs whatever the segment lengths: plan AUTO or
+ *   RECURRENT (CHUNK is GDN_ERR_PLAN);
+ *   no capsule (state_update NULL) and the V-major state layout only
+ *   (GDN_ERR_SHAPE otherwise).
+ * Errors as for gdn_forward, plus: GDN_ERR_NULL (conv NULL, or mixed or weight
+ * missing with N > 0), GDN_ERR_SHAPE (kernel_size other than 4, a misaligned
+ * convolution buffer), GDN_ERR_RULE (unknown activation), GDN_ERR_ALIAS (the
+ * convolution's final_state overlapping its initial_state or any other
+ * argument, or an output overlapping a convolution input). */
+int gdn_conv_decode_forward(const gdn_params* params, const gdn_tensors* tensors, const gdn_conv_fused* conv,
+                            void* stream);
 
 #ifdef __cplusplus
 }

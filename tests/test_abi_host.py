@@ -61,7 +61,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 6
+    assert gdn.gdn_abi_version() == gdn.ABI_VERSION == 7
     assert gdn.gdn_strerror(gdn.GDN_OK) == "ok"
     assert "gdn_forward_no_alloc" in gdn.gdn_strerror(gdn.GDN_ERR_SCRATCH)
     assert "BF16" in gdn.gdn_strerror(gdn.GDN_ERR_DTYPE)
@@ -349,3 +349,81 @@ def test_replay_forward_pooled_validation():
     sl.write_slots_host = ctypes.cast(wr, ctypes.c_void_p)
     assert L.gdn_replay_forward_pooled(ctypes.byref(p), ctypes.byref(t), ctypes.byref(sl), prev, acc, None,
                                        t.initial_state, None) == gdn.GDN_ERR_ALIAS
+
+
+def _conv_case(N=8, R=2, Hk=2, Hv=4, Dk=16, Dv=16, K=4, io=2):
+    """Fake disjoint ranges for a fused convolution + decode call: the forward
+    tensors without q, k, v, and the convolution's input, weights, bias and two
+    state banks."""
+    t, addr = _tensors(N, R, Hk, Hv, Dk, Dv)
+    t.q = t.k = t.v = None
+    Cm = 2 * Hk * Dk + Hv * Dv
+    c = gdn.GdnConvFused()
+    for name, size in (("mixed", N * Cm * io), ("weight", Cm * K * 4), ("bias", Cm * 4),
+                       ("initial_state", R * Cm * (K - 1) * 4), ("final_state", R * Cm * (K - 1) * 4)):
+        setattr(c, name, addr)
+        addr += (size + 4095) // 4096 * 4096 + 4096
+    c.kernel_size, c.activation = K, gdn.CONV_SILU
+    return t, c
+
+
+def _conv_decode(p, t, c):
+    return gdn.lib().gdn_conv_decode_forward(ctypes.byref(p), ctypes.byref(t),
+                                             ctypes.byref(c) if c is not None else None, None)
+
+
+def test_conv_decode_validation():
+    p = _p()
+    t, c = _conv_case()
+    assert _conv_decode(p, t, None) == gdn.GDN_ERR_NULL
+    # q, k, v come from the convolution
+    t2, c2 = _conv_case()
+    t2.k = t.a
+    assert _conv_decode(p, t2, c2) == gdn.GDN_ERR_SHAPE
+    # kernel size 4 only; a known activation
+    t2, c2 = _conv_case()
+    c2.kernel_size = 3
+    assert _conv_decode(p, t2, c2) == gdn.GDN_ERR_SHAPE
+    c2.kernel_size, c2.activation = 4, 7
+    assert _conv_decode(p, t2, c2) == gdn.GDN_ERR_RULE
+    # no capsule, V-major only, never the CHUNK plan
+    t2, c2 = _conv_case()
+    t2.state_update = t2.output + (1 << 24)
+    assert _conv_decode(_p(capacity=2), t2, c2) == gdn.GDN_ERR_SHAPE
+    assert _conv_decode(_p(state_layout=gdn.STATE_K_MAJOR), t, c) == gdn.GDN_ERR_SHAPE
+    assert _conv_decode(_p(Dk=128, Dv=128, plan=gdn.PLAN_CHUNK), *_conv_case(Dk=128, Dv=128)) \
+        == gdn.GDN_ERR_PLAN
+    # required convolution inputs when there are tokens
+    for name in ("mixed", "weight"):
+        t2, c2 = _conv_case()
+        setattr(c2, name, None)
+        assert _conv_decode(p, t2, c2) == gdn.GDN_ERR_NULL, name
+    # 16-byte alignment of the vector-accessed convolution buffers
+    for name in ("mixed", "weight", "initial_state", "final_state"):
+        t2, c2 = _conv_case()
+        setattr(c2, name, getattr(c2, name) + 4)
+        assert _conv_decode(p, t2, c2) == gdn.GDN_ERR_SHAPE, name
+    # no request: nothing to do
+    assert _conv_decode(_p(N=0, R=0), t, c) == gdn.GDN_OK
+
+
+def test_conv_decode_aliasing():
+    p = _p()
+    # the new carried inputs go to a bank of their own
+    t, c = _conv_case()
+    c.final_state = c.initial_state
+    assert _conv_decode(p, t, c) == gdn.GDN_ERR_ALIAS
+    for other in ("mixed", "weight", "bias"):
+        t, c = _conv_case()
+        c.final_state = getattr(c, other)
+        assert _conv_decode(p, t, c) == gdn.GDN_ERR_ALIAS, other
+    for other in ("output", "final_state", "initial_state", "a", "cu_seqlens"):
+        t, c = _conv_case()
+        c.final_state = getattr(t, other)
+        assert _conv_decode(p, t, c) == gdn.GDN_ERR_ALIAS, other
+    # outputs of the recurrence overlapping a convolution input
+    for out in ("output", "final_state"):
+        for inp in ("mixed", "weight", "initial_state"):
+            t, c = _conv_case()
+            setattr(t, out, getattr(c, inp))
+            assert _conv_decode(p, t, c) == gdn.GDN_ERR_ALIAS, (out, inp)
