@@ -43,43 +43,46 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # HBM traffic per launch (per step for workloads of several kernels), from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of that workload (KiB per dispatch, summed over
 # the step's kernels), each scaled by what the same counter reads for the 128 MiB
-# hbm_copy workload (FETCH_SIZE reads 65547.6 KiB for 131072 KiB copied: factor
+# hbm_copy workload (FETCH_SIZE reads 65547.7 KiB for 131072 KiB copied: factor
 # 1.9996; WRITE_SIZE is exact: factor 1.0000). Keyed by the hash of the kernels'
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6acf8da7f7265014", "fetch_kib": 66997.5, "write_kib": 131624.3,
-        "bytes": 271969837},
+        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 66996.5, "write_kib": 131626.0,
+        "bytes": 271969274},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6acf8da7f7265014", "fetch_kib": 66993.1, "write_kib": 131615.8,
-        "bytes": 271952119},
+        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 66992.1, "write_kib": 131612.2,
+        "bytes": 271946222},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "866621969ee55f07", "fetch_kib": 66938.1, "write_kib": 131672.4,
-        "bytes": 271897410},
+        "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.7,
+        "bytes": 271812618},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "d5b4105ea84f605f", "fetch_kib": 51131.3, "write_kib": 52117.3,
-        "bytes": 158066495},
+        "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 51131.4, "write_kib": 52116.9,
+        "bytes": 158065958},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6acf8da7f7265014", "fetch_kib": 26532.9, "write_kib": 52095.6,
-        "bytes": 107675686},
+        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 26525.5, "write_kib": 52095.3,
+        "bytes": 107660028},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "d5b4105ea84f605f", "fetch_kib": 51133.8, "write_kib": 52114.9,
-        "bytes": 158069071},
+        "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 51133.8, "write_kib": 52113.3,
+        "bytes": 158067291},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "d5b4105ea84f605f", "fetch_kib": 26534.8, "write_kib": 52094.7,
-        "bytes": 107678572},
+        "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 26527.5, "write_kib": 52090.9,
+        "bytes": 107659636},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 367812.4, "write_kib": 240719.0,
-        "bytes": 999642185},
+        "sha256_16": "e65b529c13d7051c", "fetch_kib": 367429.8, "write_kib": 240715.4,
+        "bytes": 998854039},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "bb7d6f9b04aac4e0", "fetch_kib": 669763.2, "write_kib": 725681.3,
-        "bytes": 2114528870},
+        "sha256_16": "e65b529c13d7051c", "fetch_kib": 669600.4, "write_kib": 724766.8,
+        "bytes": 2113257344},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "5d26c730968d1b84", "fetch_kib": 130542.3, "write_kib": 246424.8,
-        "bytes": 519642147},
+        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 130800.4, "write_kib": 246426.6,
+        "bytes": 520172183},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "5d26c730968d1b84", "fetch_kib": 3716.6, "write_kib": 7168.4,
-        "bytes": 14950783},
+        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
+        "bytes": 14950329},
+    "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
+        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 74903.1, "write_kib": 137757.6,
+        "bytes": 294437887},
 }
 
 
