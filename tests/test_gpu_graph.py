@@ -1,8 +1,8 @@
 """GPU: the hot path captured in HIP graphs (torch.cuda.CUDAGraph) and replayed.
 
-A serving loop captures a decode step, or the speculative step (verify, replay
-of the accepted prefix, publication of the slot arrays; or the fused step and
-the publication), once and replays it.
+A serving loop captures a decode step (also with the causal convolution fused
+in), or the speculative step (verify, replay of the accepted prefix, publication
+of the slot arrays; or the fused step and the publication), once and replays it.
 Each graph here is replayed several times, with the program's own eager work
 and synchronisations between the replays, and every replay is compared bit for
 bit with the same calls made eagerly from the same starting state (the kernels
@@ -263,6 +263,46 @@ def test_conv_decode_graph():
         _case(f"conv decode: replay {rep}")
         g.replay()
         _same(_snapshot([state, out]), ref, f"conv decode replay {rep}")
+
+
+def test_conv_fused_decode_graph():
+    # three decode steps with the convolution fused: the GDN state in place, the
+    # carried inputs passed from bank to bank (A -> B -> A -> B)
+    R, Hk, Hv, D, K = 8, 2, 4, 128, 4
+    C = 2 * Hk * D + Hv * D
+    g_in = make_inputs([1] * R, Hk, Hv, D, D, "f16", seed=505)
+    c_in = make_conv_inputs([1] * R, C, K, "f16", seed=506)
+    d = {n: dev(g_in[n], torch) for n in ("a", "b", "A_log", "dt_bias", "cu_seqlens")}
+    x, w, b = dev(c_in["x"], torch), dev(c_in["weight"], torch), dev(c_in["bias"], torch)
+    s0, c0 = dev(g_in["initial_state"], torch), dev(c_in["initial_state"], torch)
+    state, ca, cb = s0.clone(), c0.clone(), torch.zeros_like(c0)
+    out = torch.empty((R, Hv, D), dtype=torch.float16, device="cuda")
+
+    def run():
+        for src, dst in ((ca, cb), (cb, ca), (ca, cb)):
+            gdn.gdn_conv_decode_forward(x, w, b, d["a"], d["b"], d["A_log"], d["dt_bias"], d["cu_seqlens"], out,
+                                        num_k_heads=Hk, head_k_dim=D, conv_initial_state=src,
+                                        conv_final_state=dst, initial_state=state, final_state=state,
+                                        cu_seqlens_host=g_in["cu_seqlens"])
+
+    def reset():
+        state.copy_(s0)
+        ca.copy_(c0)
+        cb.zero_()
+        out.zero_()
+        torch.cuda.synchronize()
+
+    _case("fused conv decode: eager reference")
+    run()
+    ref = _snapshot([state, ca, cb, out])
+    reset()
+    _case("fused conv decode: capture")
+    g = _capture(run)
+    for rep in range(3):
+        reset()
+        _case(f"fused conv decode: replay {rep}")
+        g.replay()
+        _same(_snapshot([state, ca, cb, out]), ref, f"fused conv decode replay {rep}")
 
 
 def test_two_streams_run_independent_calls():
