@@ -320,7 +320,12 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, void* lds, int byte_off, in
 }
 
 constexpr int kTouchLoads = 3;     // L2 prefetch loads per loader wave and chunk
-constexpr int kTouchAhead = 3;     // prefetched this many chunks ahead of the direct loads
+// Prefetched this many chunks ahead of the direct loads. Further ahead, the lines in
+// flight per XCD approach its 4 MB L2 when every CU runs a workgroup, and some are
+// evicted before their direct loads: one chunk ahead took the ragged prefill from
+// 223-229 to 214-218 us (three ahead), the long one unchanged; without the prefetch
+// the long prefill took 904 us.
+constexpr int kTouchAhead = 1;
 
 // Copies chunk (slot, t0, L) into LDS buffer B; rows >= L read as zero (L = 0: no
 // memory is read, the buffer fills with zeros). Loader wave w copies rows
