@@ -49,40 +49,40 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 66996.5, "write_kib": 131626.0,
-        "bytes": 271969274},
+        "bytes": 271969365},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 66992.1, "write_kib": 131612.2,
-        "bytes": 271946222},
+        "bytes": 271946313},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.7,
-        "bytes": 271812618},
+        "bytes": 271812709},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 51131.4, "write_kib": 52116.9,
-        "bytes": 158065958},
+        "bytes": 158066028},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 26525.5, "write_kib": 52095.3,
-        "bytes": 107660028},
+        "bytes": 107660065},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 51133.8, "write_kib": 52113.3,
-        "bytes": 158067291},
+        "bytes": 158067361},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 26527.5, "write_kib": 52090.9,
-        "bytes": 107659636},
+        "bytes": 107659673},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e65b529c13d7051c", "fetch_kib": 367429.8, "write_kib": 240715.4,
-        "bytes": 998854039},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258850.4, "write_kib": 240802.8,
+        "bytes": 776613120},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e65b529c13d7051c", "fetch_kib": 669600.4, "write_kib": 724766.8,
-        "bytes": 2113257344},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669510.9, "write_kib": 715780.8,
+        "bytes": 2103873287},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 130800.4, "write_kib": 246426.6,
-        "bytes": 520172183},
+        "bytes": 520172361},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950329},
+        "bytes": 14950334},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 74903.1, "write_kib": 137757.6,
-        "bytes": 294437887},
+        "bytes": 294437989},
 }
 
 
