@@ -302,11 +302,26 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
   const int rg = lane / LPR;
   const int c = lane % LPR;
 
-  int item = blockIdx.x;
-  const int blk = item % blocks_per_head;
-  item /= blocks_per_head;
-  const int h = item % p.Hv;
-  const int r = item / p.Hv;
+  int r, h, blk;
+  if constexpr (CONV) {
+    // The workgroups of one (request, key head) convolve the same q and k
+    // channels: they are dealt to one XCD (workgroups go to the 8 XCDs round-robin
+    // by index), so the convolution's inputs are fetched into one L2 rather than
+    // into each of four (the grid is padded to whole rounds of 8 units).
+    const int per_unit = p.group * blocks_per_head;
+    const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+    const int unit = xcd + 8 * (j / per_unit), m = j % per_unit;
+    if (unit >= p.R * p.Hk) return;                  // padding: uniform, before any barrier
+    r = unit / p.Hk;
+    h = (unit % p.Hk) * p.group + m / blocks_per_head;
+    blk = m % blocks_per_head;
+  } else {
+    int item = blockIdx.x;
+    blk = item % blocks_per_head;
+    item /= blocks_per_head;
+    h = item % p.Hv;
+    r = item / p.Hv;
+  }
   const int g = h / p.group;
   const int Dv = p.Dv;
   const int row_base = (blk * waves_per_block + wave) * RW;
@@ -916,9 +931,12 @@ static hipError_t launch_dk(const RecurrentArgs& p, hipStream_t stream) {
                          dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
   } else {
     launch_shape<DK, NI>(p.Dv, &wpb, &bph);
-    if (p.conv_channels > 0)
-      hipLaunchKernelGGL((gdn_conv_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
+    if (p.conv_channels > 0) {
+      // whole rounds of 8 (request, key head) units, see recurrent_body
+      const size_t units = 8 * (((size_t)p.R * p.Hk + 7) / 8);
+      hipLaunchKernelGGL((gdn_conv_decode<IO, DK, NI>), dim3((unsigned)(units * p.group * bph)),
                          dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
+    }
     else
       hipLaunchKernelGGL((gdn_decode<IO, DK, NI>), dim3((unsigned)((size_t)p.R * p.Hv * bph)),
                          dim3((unsigned)(64 * wpb)), 0, stream, p, wpb, bph);
