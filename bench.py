@@ -48,41 +48,41 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 66996.5, "write_kib": 131626.0,
-        "bytes": 271969365},
+        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 66997.5, "write_kib": 131624.0,
+        "bytes": 271969338},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 66992.1, "write_kib": 131612.2,
-        "bytes": 271946313},
+        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 66993.1, "write_kib": 131616.3,
+        "bytes": 271952459},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.7,
-        "bytes": 271812709},
+        "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131595.6,
+        "bytes": 271814623},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 51131.4, "write_kib": 52116.9,
-        "bytes": 158066028},
+        "sha256_16": "fb186d8b26c2268a", "fetch_kib": 51131.3, "write_kib": 52115.9,
+        "bytes": 158064969},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 26525.5, "write_kib": 52095.3,
-        "bytes": 107660065},
+        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 26531.9, "write_kib": 52097.8,
+        "bytes": 107675781},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 51133.8, "write_kib": 52113.3,
-        "bytes": 158067361},
+        "sha256_16": "fb186d8b26c2268a", "fetch_kib": 51133.7, "write_kib": 52115.8,
+        "bytes": 158069819},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "d4b03de43ffe04e4", "fetch_kib": 26527.5, "write_kib": 52090.9,
-        "bytes": 107659673},
+        "sha256_16": "fb186d8b26c2268a", "fetch_kib": 26533.9, "write_kib": 52094.9,
+        "bytes": 107676831},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258850.4, "write_kib": 240802.8,
-        "bytes": 776613120},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258842.9, "write_kib": 240792.8,
+        "bytes": 776587590},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669510.9, "write_kib": 715780.8,
-        "bytes": 2103873287},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669510.8, "write_kib": 715780.7,
+        "bytes": 2103872861},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 130800.4, "write_kib": 246426.6,
-        "bytes": 520172361},
+        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 131124.1, "write_kib": 246423.3,
+        "bytes": 520831610},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950334},
+        "bytes": 14950329},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "dbe0ecf78b02e6dc", "fetch_kib": 74903.1, "write_kib": 137757.6,
-        "bytes": 294437989},
+        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 69403.6, "write_kib": 137757.5,
+        "bytes": 283176958},
 }
 
 
