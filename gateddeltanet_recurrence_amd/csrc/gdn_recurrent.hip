@@ -518,7 +518,9 @@ constexpr int kStageTokens = 16;
 constexpr float kMinStateScale = 0x1p-40f;
 
 template <int DK>
-struct StageSmem {
+struct __attribute__((aligned(16))) StageSmem {
+  // 16-byte aligned so that a lane's four consecutive floats of kh / qh are one
+  // ds_read_b128 (the compiler split them into pairs of 4-byte reads without it)
   float kh[kStageTokens][DK];      // unit keys
   float qh[kStageTokens][DK];      // unit queries times the scale
   float v[kStageTokens][256];      // this block's value rows (at most 4 waves x 64 rows)
