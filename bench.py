@@ -48,41 +48,41 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 66997.5, "write_kib": 131624.0,
-        "bytes": 271969338},
+        "sha256_16": "fc604236efda3687", "fetch_kib": 66994.5, "write_kib": 131625.7,
+        "bytes": 271965009},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 66993.1, "write_kib": 131616.3,
-        "bytes": 271952459},
+        "sha256_16": "fc604236efda3687", "fetch_kib": 66990.1, "write_kib": 131616.0,
+        "bytes": 271946032},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131595.6,
-        "bytes": 271814623},
+        "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.5,
+        "bytes": 271812451},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fb186d8b26c2268a", "fetch_kib": 51131.3, "write_kib": 52115.9,
-        "bytes": 158064969},
+        "sha256_16": "60257157ef6901de", "fetch_kib": 51126.9, "write_kib": 52118.1,
+        "bytes": 158058025},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 26531.9, "write_kib": 52097.8,
-        "bytes": 107675781},
+        "sha256_16": "fc604236efda3687", "fetch_kib": 26524.9, "write_kib": 52092.1,
+        "bytes": 107655742},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fb186d8b26c2268a", "fetch_kib": 51133.7, "write_kib": 52115.8,
-        "bytes": 158069819},
+        "sha256_16": "60257157ef6901de", "fetch_kib": 51129.3, "write_kib": 52114.5,
+        "bytes": 158059389},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fb186d8b26c2268a", "fetch_kib": 26533.9, "write_kib": 52094.9,
-        "bytes": 107676831},
+        "sha256_16": "60257157ef6901de", "fetch_kib": 26526.9, "write_kib": 52090.9,
+        "bytes": 107658595},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258842.9, "write_kib": 240792.8,
-        "bytes": 776587590},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258823.4, "write_kib": 240767.0,
+        "bytes": 776521141},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669510.8, "write_kib": 715780.7,
-        "bytes": 2103872861},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669509.4, "write_kib": 715784.4,
+        "bytes": 2103873805},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 131124.1, "write_kib": 246423.3,
-        "bytes": 520831610},
+        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 131133.8, "write_kib": 246428.3,
+        "bytes": 520856655},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950329},
+        "bytes": 14950332},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "c3d2fdca44bf99ee", "fetch_kib": 69403.6, "write_kib": 137757.5,
-        "bytes": 283176958},
+        "sha256_16": "fc604236efda3687", "fetch_kib": 69411.1, "write_kib": 137759.6,
+        "bytes": 283194472},
 }
 
 
