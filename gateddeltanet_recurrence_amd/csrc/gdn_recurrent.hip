@@ -1,4 +1,6 @@
-// Token-recurrent GatedDeltaNet kernels: gdn_decode and gdn_capsule.
+// Token-recurrent GatedDeltaNet kernels: gdn_decode, gdn_capsule, the fused
+// speculative step gdn_replay_verify and the decode with the causal convolution
+// fused in, gdn_conv_decode.
 //
 // The recurrent decode path of the operator ("[CUDA] Add compact GatedDeltaNet
 // operator", Description) and, with a capsule, the compact state-update capture
@@ -13,7 +15,9 @@
 // contiguous) is spread over LPR adjacent lanes holding E = Dk/LPR floats each,
 // loaded as 16-byte vectors: one wave instruction covers RI full rows, i.e. RI
 // fully used 128-byte lines for Dk = 128. Row dot products (S k^ and S q^) are
-// in-lane FMAs followed by a DPP reduction over the LPR lanes; no LDS is used.
+// in-lane FMAs followed by a DPP reduction over the LPR lanes; the decode uses no
+// LDS (the capsule kernels stage their tokens in LDS, and gdn_conv_decode its
+// convolution's output).
 //
 // Per token, with the old state S:
 //   pk = S k^, pq = S q^  (one pass over the registers, reduced together)
