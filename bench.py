@@ -48,41 +48,41 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fc604236efda3687", "fetch_kib": 66994.5, "write_kib": 131625.7,
-        "bytes": 271965009},
+        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 66994.5, "write_kib": 131622.2,
+        "bytes": 271961426},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fc604236efda3687", "fetch_kib": 66990.1, "write_kib": 131616.0,
-        "bytes": 271946032},
+        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 66990.1, "write_kib": 131615.8,
+        "bytes": 271945894},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.5,
-        "bytes": 271812451},
+        "bytes": 271812403},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "60257157ef6901de", "fetch_kib": 51126.9, "write_kib": 52118.1,
-        "bytes": 158058025},
+        "sha256_16": "ab0d9f99053ce36c", "fetch_kib": 51126.8, "write_kib": 52116.3,
+        "bytes": 158056205},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fc604236efda3687", "fetch_kib": 26524.9, "write_kib": 52092.1,
-        "bytes": 107655742},
+        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 26525.0, "write_kib": 52088.0,
+        "bytes": 107651576},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "60257157ef6901de", "fetch_kib": 51129.3, "write_kib": 52114.5,
-        "bytes": 158059389},
+        "sha256_16": "ab0d9f99053ce36c", "fetch_kib": 51129.3, "write_kib": 52115.9,
+        "bytes": 158060768},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "60257157ef6901de", "fetch_kib": 26526.9, "write_kib": 52090.9,
-        "bytes": 107658595},
+        "sha256_16": "ab0d9f99053ce36c", "fetch_kib": 26527.0, "write_kib": 52085.3,
+        "bytes": 107652908},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258823.4, "write_kib": 240767.0,
-        "bytes": 776521141},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258792.7, "write_kib": 240761.7,
+        "bytes": 776452826},
     "long_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669509.4, "write_kib": 715784.4,
-        "bytes": 2103873805},
+        "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669508.5, "write_kib": 715781.8,
+        "bytes": 2103869140},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 131133.8, "write_kib": 246428.3,
-        "bytes": 520856655},
+        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 130733.7, "write_kib": 246423.5,
+        "bytes": 520032609},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950332},
+        "bytes": 14950330},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "fc604236efda3687", "fetch_kib": 69411.1, "write_kib": 137759.6,
-        "bytes": 283194472},
+        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 69411.1, "write_kib": 137760.9,
+        "bytes": 283195776},
 }
 
 
