@@ -557,6 +557,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
                                                       int blocks_per_head) {
   using L = RecLayout<DK>;
   constexpr int LPR = L::LPR, E = L::E, V4 = L::V4, RI = L::RI, RW = RI * NI;
+  static_assert(NI <= LPR, "a lane group writes its NI rows with one lane each");
   constexpr int TPT = 16;                 // threads per staged token
   constexpr int EPT = DK / TPT;           // elements per staging thread
   // (the fused replay keeps the plain staging: with both its registers exceed
@@ -846,15 +847,29 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
           for (int e = 0; e < E; ++e) S[i][e] = fmaf(w, kv[e], S[i][e]);
         }
       }
+      // One store per token for the NI rows of a lane group: every lane of the group
+      // holds every row's total, and lane c < NI writes row c. The stores are range
+      // checked against the head's Dv rows, so lanes c >= NI (sent past the range)
+      // and rows past Dv write nothing, without a branch per row.
+      {
+        float o_c = 0.f, u_c = 0.f;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int row = row_base + i * RI + rg;
-        const float o = fmaf(gn, pq[i], u[i] * kq);
-        if (valid[i] && c == 0) {
-          IoOps<IO>::store1(op + ((size_t)t * p.Hv + h) * Dv + row, o);
-          if constexpr (CAPTURE) {
-            if (caprow != nullptr) caprow[p.Hv + p.Hk * DK + h * Dv + row] = u[i];
-          }
+        for (int i = 0; i < NI; ++i) {
+          const float o = fmaf(gn, pq[i], u[i] * kq);
+          o_c = c == i ? o : o_c;
+          u_c = c == i ? u[i] : u_c;
+        }
+        const int row_c = c < NI ? row_base + c * RI + rg : Dv;
+        const rsrc_t ro = make_rsrc(op + ((size_t)t * p.Hv + h) * Dv, Dv * (int)sizeof(IO));
+        if constexpr (sizeof(IO) == 2)
+          buf_store_h1((_Float16)o_c, ro, row_c * 2);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, o_c), ro, row_c * 4, 0, 0);
+        if constexpr (CAPTURE) {
+          if (caprow != nullptr)                   // uniform over the workgroup
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(unsigned, u_c), make_rsrc(caprow + p.Hv + p.Hk * DK + h * Dv, Dv * 4),
+                row_c * 4, 0, 0);
         }
       }
       if constexpr (CAPTURE) {
