@@ -300,6 +300,7 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
                                                int blocks_per_head) {
   using L = RecLayout<DK>;
   constexpr int LPR = L::LPR, E = L::E, V4 = L::V4, RI = L::RI, RW = RI * NI;
+  static_assert(NI <= LPR, "a lane group writes its NI rows with one lane each");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -457,18 +458,30 @@ __device__ __forceinline__ void recurrent_body(const RecurrentArgs& p, int waves
     if constexpr (CAPTURE) {
       if (jcap < ncap) caprow = p.state_update + ((size_t)r * p.capacity + jcap) * p.capsule_width;
     }
+    // one range-checked store per token for the lane group's NI rows: lane c < NI
+    // writes row c (as in recurrent_body_staged)
+    float o_c = 0.f, u_c = 0.f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const float u = beta * (vv[i] - kd * pk[i]);
       const float o = fmaf(alpha * rq, pq[i], u * kq);
 #pragma unroll
       for (int e = 0; e < E; ++e) S[i][e] = fmaf(alpha, S[i][e], u * kv[e]);
-      const int row = row_base + i * RI + rg;
-      if (valid[i] && c == 0) {
-        IoOps<IO>::store1(op + ((size_t)t * p.Hv + h) * Dv + row, o);
-        if constexpr (CAPTURE) {
-          if (caprow != nullptr) caprow[p.Hv + p.Hk * DK + h * Dv + row] = u;
-        }
+      o_c = c == i ? o : o_c;
+      u_c = c == i ? u : u_c;
+    }
+    {
+      const int row_c = c < NI ? row_base + c * RI + rg : Dv;
+      const rsrc_t ro = make_rsrc(op + ((size_t)t * p.Hv + h) * Dv, Dv * (int)sizeof(IO));
+      if constexpr (sizeof(IO) == 2)
+        buf_store_h1((_Float16)o_c, ro, row_c * 2);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, o_c), ro, row_c * 4, 0, 0);
+      if constexpr (CAPTURE) {
+        if (caprow != nullptr)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(unsigned, u_c), make_rsrc(caprow + p.Hv + p.Hk * DK + h * Dv, Dv * 4),
+              row_c * 4, 0, 0);
       }
     }
     if constexpr (CAPTURE) {
