@@ -48,26 +48,26 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 66994.5, "write_kib": 131622.2,
-        "bytes": 271961426},
+        "sha256_16": "e01ac215981079b8", "fetch_kib": 66930.5, "write_kib": 131601.8,
+        "bytes": 271809452},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 66990.1, "write_kib": 131615.8,
-        "bytes": 271945894},
+        "sha256_16": "e01ac215981079b8", "fetch_kib": 66926.1, "write_kib": 131595.1,
+        "bytes": 271793571},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.5,
         "bytes": 271812403},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "ab0d9f99053ce36c", "fetch_kib": 51126.8, "write_kib": 52116.3,
-        "bytes": 158056205},
+        "sha256_16": "4b6383eea84265db", "fetch_kib": 51122.8, "write_kib": 52117.5,
+        "bytes": 158049191},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 26525.0, "write_kib": 52088.0,
-        "bytes": 107651576},
+        "sha256_16": "e01ac215981079b8", "fetch_kib": 26530.9, "write_kib": 52098.0,
+        "bytes": 107673887},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "ab0d9f99053ce36c", "fetch_kib": 51129.3, "write_kib": 52115.9,
-        "bytes": 158060768},
+        "sha256_16": "4b6383eea84265db", "fetch_kib": 51125.3, "write_kib": 52114.6,
+        "bytes": 158051278},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "ab0d9f99053ce36c", "fetch_kib": 26527.0, "write_kib": 52085.3,
-        "bytes": 107652908},
+        "sha256_16": "4b6383eea84265db", "fetch_kib": 26532.9, "write_kib": 52093.2,
+        "bytes": 107673069},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258792.7, "write_kib": 240761.7,
         "bytes": 776452826},
@@ -81,8 +81,8 @@ MEASURED_TRAFFIC = {
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
         "bytes": 14950330},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e5c21e4f3c02ca48", "fetch_kib": 69411.1, "write_kib": 137760.9,
-        "bytes": 283195776},
+        "sha256_16": "e01ac215981079b8", "fetch_kib": 69409.1, "write_kib": 137757.2,
+        "bytes": 283187923},
 }
 
 
