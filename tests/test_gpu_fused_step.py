@@ -85,6 +85,7 @@ def _fused(d, inp, prev, acc, acc_host, cap, fin):
     ("f16", 128, 128, [4, 0, 3, 1, 4], True),
     ("f32", 64, 32, [2, 4, 0, 3], True),
     ("f32", 16, 16, [1, 4, 4], False),
+    ("f16", 128, 16, [4, 2, 0, 3], True),          # rows past Dv in the one wave of a head
 ])
 def test_fused_step_equals_separate_calls(io, Dk, Dv, lengths, final):
     cap = 4

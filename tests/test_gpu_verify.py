@@ -2,8 +2,9 @@
 Dk = Dv = 128, V-major) against the float64 oracle, called through the C ABI,
 on what the speculative verify workload does not reach: segments longer than
 one staged group of tokens, final states (in place too), no initial state with
-every update rule, capture counts past either end of [0, capacity], and state
-rows over a wide range of magnitudes.
+every update rule, capture counts past either end of [0, capacity], state rows
+over a wide range of magnitudes, and heads with fewer value rows (Dv = 16, 32)
+than one wave holds.
 
 Tolerances (as for every fp16 path): output max-abs <= 2e-2, final state
 relative L2 <= 1e-3; capsule alpha and k^ rel-max <= 1e-5, u <= 1e-3; untouched
@@ -110,3 +111,19 @@ def test_verify_state_rows_over_wide_range():
         nz = scale > 0
         assert np.all(err[nz] <= 1e-4 * scale[nz]), float((err[nz] / scale[nz]).max())
         assert rel_max(got[r, :L, sa], ref_cap[r, :L, sa]) <= 1e-5
+
+
+@pytest.mark.parametrize("io", ["f16", "f32"])
+@pytest.mark.parametrize("Dv", [16, 32])
+def test_verify_rows_past_dv(io, Dv):
+    # Dk = 128 with Dv below one wave's 32 state rows: the lanes whose rows lie
+    # past Dv must write neither output nor delta (their range-checked stores are
+    # dropped); the rows that exist match the oracle
+    lengths = [4, 3, 0, 4, 1]
+    cap = 4
+    inp = make_inputs(lengths, 2, 4, 128, Dv, io, seed=910 + Dv, capacity=cap)
+    _case(f"verify rows past Dv io={io} Dk=128 Dv={Dv} lengths={lengths}")
+    res = run_forward(inp, torch, gdn, capacity=cap, poison=-7.0, plan=gdn.PLAN_RECURRENT)
+    ref_o, ref_s, ref_cap = oracle_forward(inp, O, capacity=cap, poison=-7.0)
+    assert_parity(io, res["output"], ref_o, res["final_state"], ref_s, f"verify Dv={Dv}")
+    _check_capsule(res["state_update"], ref_cap, inp, lengths)
