@@ -80,7 +80,7 @@ struct RecLayout {
 // loads had compiled to waits for the first loads before the later ones were
 // issued, and to waits that also covered the state where only later loads
 // were needed.
-template <int DK, int NI>
+template <int DK, int NI, int I0 = 0, int NL = NI>
 __device__ __forceinline__ void load_state_rows(const float* init, const void* any_base, int row_base, int rg,
                                                 int c, int Dv, float (&S)[NI][RecLayout<DK>::E],
                                                 bool (&valid)[NI]) {
@@ -89,7 +89,7 @@ __device__ __forceinline__ void load_state_rows(const float* init, const void* a
   const rsrc_t rs = make_rsrc(init != nullptr ? static_cast<const void*>(init) : any_base,
                               init != nullptr ? Dv * DK * 4 : 0);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int i = I0; i < I0 + NL; ++i) {
     const int row = row_base + i * RI + rg;
     valid[i] = row < Dv;
 #pragma unroll
@@ -635,7 +635,15 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   // ---- state rows into registers (issued before any other staging)
   float S[NI][E];
   bool valid[NI];
-  load_state_rows<DK, NI>(init, p.q, row_base, rg, c, Dv, S, valid);
+  // The verify walks a lane group's rows in NP passes of NH rows. Only the
+  // first pass's state is loaded here; the second pass's loads go out once the
+  // first token group is staged and land while the first pass computes (the
+  // whole grid is resident at once, so without this every wave would wait for
+  // all of its state before its first token). The replaying kernel keeps one
+  // pass: its replay and the replayed-state stores need every row first.
+  constexpr int NP = (!REPLAY && NI % 2 == 0 && NI >= 4) ? 2 : 1;
+  constexpr int NH = NI / NP;
+  load_state_rows<DK, NI, 0, NH>(init, p.q, row_base, rg, c, Dv, S, valid);
   if constexpr (kDma) __builtin_amdgcn_sched_barrier(0);
 
   // the previous step's accepted capsule prefix, applied in registers with the
@@ -703,8 +711,11 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
   }
 
   // The registers hold S / gam: a token's decay then folds into gam and the
-  // update is one fused multiply-add per element, S/gam += (u/gam) k^.
-  float gam = 1.f;
+  // update is one fused multiply-add per element, S/gam += (u/gam) k^. Each pass
+  // keeps its own gam (both see the same gates, so they agree).
+  float gam_p[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) gam_p[q] = 1.f;
   // One token group; the first is called outside the loop, so that the compiler's
   // flush of the memory counter at the entry of a loop that reads the state comes
   // only after that group's staging.
@@ -712,11 +723,11 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
     const int nt = min(kStageTokens, t1 - ts);
     if constexpr (kDma) {
       // the group's raw inputs are in LDS once wave 0's direct loads land: for the
-      // first group they precede exactly NI V4 state loads, so waiting until no
-      // more than those are pending leaves the state in flight
+      // first group they precede exactly NH V4 state loads (the first pass's), so
+      // waiting until no more than those are pending leaves the state in flight
       if (ts != t0) issue_dma(ts, nt);
       if (ts == t0) {
-        constexpr int kState = NI * V4;
+        constexpr int kState = NH * V4;
         static_assert(kState < 64, "vmcnt holds 6 bits");
         __builtin_amdgcn_s_waitcnt((kState & 15) | (7 << 4) | (15 << 8) | ((kState >> 4) << 14));
       } else {
@@ -797,113 +808,137 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
       if (ts == t0) store_replayed();              // the registers hold the replayed state
     }
 
-    for (int j = 0; j < nt; ++j) {
-      const int t = ts + j;
-      float kv[E], qv[E];
+    // one pass over the group's tokens for the rows I0 .. I1 - 1 of each lane group
+    auto walk = [&](auto pc) {
+      constexpr int PASS = decltype(pc)::value, I0 = PASS * NH, I1 = I0 + NH;
+      float& gam = gam_p[PASS];
+      for (int j = 0; j < nt; ++j) {
+        const int t = ts + j;
+        float kv[E], qv[E];
 #pragma unroll
-      for (int jj = 0; jj < V4; ++jj) {
-        const float4_t kx = *reinterpret_cast<const float4_t*>(&sm.kh[j][4 * c + 4 * LPR * jj]);
-        const float4_t qx = *reinterpret_cast<const float4_t*>(&sm.qh[j][4 * c + 4 * LPR * jj]);
-        kv[4 * jj + 0] = kx.x; kv[4 * jj + 1] = kx.y; kv[4 * jj + 2] = kx.z; kv[4 * jj + 3] = kx.w;
-        qv[4 * jj + 0] = qx.x; qv[4 * jj + 1] = qx.y; qv[4 * jj + 2] = qx.z; qv[4 * jj + 3] = qx.w;
-      }
-      const float beta = sm.beta[j], kq = sm.kq[j];
-      // decay of the held state up to and including this token
-      const float gn = gam * sm.alpha[j];
-      const bool keep_scaled = gn >= kMinStateScale;   // uniform over the workgroup
-      float pk[NI], pq[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          sk = fmaf(S[i][e], kv[e], sk);
-          sq = fmaf(S[i][e], qv[e], sq);
+        for (int jj = 0; jj < V4; ++jj) {
+          const float4_t kx = *reinterpret_cast<const float4_t*>(&sm.kh[j][4 * c + 4 * LPR * jj]);
+          const float4_t qx = *reinterpret_cast<const float4_t*>(&sm.qh[j][4 * c + 4 * LPR * jj]);
+          kv[4 * jj + 0] = kx.x; kv[4 * jj + 1] = kx.y; kv[4 * jj + 2] = kx.z; kv[4 * jj + 3] = kx.w;
+          qv[4 * jj + 0] = qx.x; qv[4 * jj + 1] = qx.y; qv[4 * jj + 2] = qx.z; qv[4 * jj + 3] = qx.w;
         }
-        pk[i] = sk;
-        pq[i] = sq;
-      }
+        const float beta = sm.beta[j], kq = sm.kq[j];
+        // decay of the held state up to and including this token
+        const float gn = gam * sm.alpha[j];
+        const bool keep_scaled = gn >= kMinStateScale;   // uniform over the workgroup
+        float pk[NI], pq[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        pk[i] = group_sum<LPR>(pk[i]);
-        pq[i] = group_sum<LPR>(pq[i]);
-      }
-      const int jcap = t - t0;
-      float* caprow = nullptr;
-      if constexpr (CAPTURE) {
-        if (jcap < ncap) caprow = cap + ((size_t)r * p.capacity + jcap) * p.capsule_width;
-      }
-      // the state's scale is reset (one in-place multiply) only when the
-      // product would leave the range where 1/gam is safe
-      const float rgn = keep_scaled ? __builtin_amdgcn_rcpf(gn) : 1.f;
-      // u = beta (v - alpha S k^) with the delta correction, v without it
-      const float gk = delta ? gn : 0.f;
-      float u[NI];
+        for (int i = I0; i < I1; ++i) {
+          float sk = 0.f, sq = 0.f;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float vv = sm.v[j][row_base + i * RI + rg - block_row0];   // zero past Dv
-        u[i] = beta * (vv - gk * pk[i]);
-      }
-      // the state after the segment's last token is used only as a final state
-      // (the verify asks for none)
-      if (t + 1 < t1 || fin != nullptr) {          // uniform over the workgroup
-        if (!keep_scaled) {
-#pragma unroll
-          for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int e = 0; e < E; ++e) S[i][e] *= gn;
+          for (int e = 0; e < E; ++e) {
+            sk = fmaf(S[i][e], kv[e], sk);
+            sq = fmaf(S[i][e], qv[e], sq);
+          }
+          pk[i] = sk;
+          pq[i] = sq;
         }
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const float w = u[i] * rgn;
-#pragma unroll
-          for (int e = 0; e < E; ++e) S[i][e] = fmaf(w, kv[e], S[i][e]);
+        for (int i = I0; i < I1; ++i) {
+          pk[i] = group_sum<LPR>(pk[i]);
+          pq[i] = group_sum<LPR>(pq[i]);
         }
-      }
-      // One store per token for the NI rows of a lane group: every lane of the group
-      // holds every row's total, and lane c < NI writes row c. The stores are range
-      // checked against the head's Dv rows, so lanes c >= NI (sent past the range)
-      // and rows past Dv write nothing, without a branch per row.
-      {
-        float o_c = 0.f, u_c = 0.f;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const float o = fmaf(gn, pq[i], u[i] * kq);
-          o_c = c == i ? o : o_c;
-          u_c = c == i ? u[i] : u_c;
-        }
-        const int row_c = c < NI ? row_base + c * RI + rg : Dv;
-        const rsrc_t ro = make_rsrc(op + ((size_t)t * p.Hv + h) * Dv, Dv * (int)sizeof(IO));
-        if constexpr (sizeof(IO) == 2)
-          buf_store_h1((_Float16)o_c, ro, row_c * 2);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, o_c), ro, row_c * 4, 0, 0);
+        const int jcap = t - t0;
+        float* caprow = nullptr;
         if constexpr (CAPTURE) {
-          if (caprow != nullptr)                   // uniform over the workgroup
-            __builtin_amdgcn_raw_buffer_store_b32(
-                __builtin_bit_cast(unsigned, u_c), make_rsrc(caprow + p.Hv + p.Hk * DK + h * Dv, Dv * 4),
-                row_c * 4, 0, 0);
+          if (jcap < ncap) caprow = cap + ((size_t)r * p.capacity + jcap) * p.capsule_width;
         }
-      }
-      if constexpr (CAPTURE) {
-        if (caprow != nullptr && blk == 0 && wave == 0) {
-          if (lane == 0) caprow[h] = sm.alpha[j];
-          // the shared key is written once per key head, by its first value head
-          if (h % p.group == 0 && rg == 0) {
+        // the state's scale is reset (one in-place multiply) only when the
+        // product would leave the range where 1/gam is safe
+        const float rgn = keep_scaled ? __builtin_amdgcn_rcpf(gn) : 1.f;
+        // u = beta (v - alpha S k^) with the delta correction, v without it
+        const float gk = delta ? gn : 0.f;
+        float u[NI];
 #pragma unroll
-            for (int jj = 0; jj < V4; ++jj)
+        for (int i = I0; i < I1; ++i) {
+          const float vv = sm.v[j][row_base + i * RI + rg - block_row0];   // zero past Dv
+          u[i] = beta * (vv - gk * pk[i]);
+        }
+        // the state after the segment's last token is used only as a final state
+        // (the verify asks for none)
+        if (t + 1 < t1 || fin != nullptr) {          // uniform over the workgroup
+          if (!keep_scaled) {
 #pragma unroll
-              for (int x = 0; x < 4; ++x)
-                caprow[p.Hv + g * DK + 4 * c + 4 * LPR * jj + x] = kv[4 * jj + x];
+            for (int i = I0; i < I1; ++i)
+#pragma unroll
+              for (int e = 0; e < E; ++e) S[i][e] *= gn;
+          }
+#pragma unroll
+          for (int i = I0; i < I1; ++i) {
+            const float w = u[i] * rgn;
+#pragma unroll
+            for (int e = 0; e < E; ++e) S[i][e] = fmaf(w, kv[e], S[i][e]);
           }
         }
+        // One store per token for the NI rows of a lane group: every lane of the group
+        // holds every row's total, and lane c < NI writes row c. The stores are range
+        // checked against the head's Dv rows, so lanes c >= NI (sent past the range)
+        // and rows past Dv write nothing, without a branch per row.
+        {
+          float o_c = 0.f, u_c = 0.f;
+#pragma unroll
+          for (int i = I0; i < I1; ++i) {
+            const float o = fmaf(gn, pq[i], u[i] * kq);
+            o_c = c == i ? o : o_c;
+            u_c = c == i ? u[i] : u_c;
+          }
+          const int row_c = (c >= I0 && c < I1) ? row_base + c * RI + rg : Dv;
+          const rsrc_t ro = make_rsrc(op + ((size_t)t * p.Hv + h) * Dv, Dv * (int)sizeof(IO));
+          if constexpr (sizeof(IO) == 2)
+            buf_store_h1((_Float16)o_c, ro, row_c * 2);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, o_c), ro, row_c * 4, 0, 0);
+          if constexpr (CAPTURE) {
+            if (caprow != nullptr)                   // uniform over the workgroup
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(unsigned, u_c), make_rsrc(caprow + p.Hv + p.Hk * DK + h * Dv, Dv * 4),
+                  row_c * 4, 0, 0);
+          }
+        }
+        if constexpr (CAPTURE && PASS == 0) {
+          if (caprow != nullptr && blk == 0 && wave == 0) {
+            if (lane == 0) caprow[h] = sm.alpha[j];
+            // the shared key is written once per key head, by its first value head
+            if (h % p.group == 0 && rg == 0) {
+#pragma unroll
+              for (int jj = 0; jj < V4; ++jj)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                  caprow[p.Hv + g * DK + 4 * c + 4 * LPR * jj + x] = kv[4 * jj + x];
+            }
+          }
+        }
+        gam = keep_scaled ? gn : 1.f;
       }
-      gam = keep_scaled ? gn : 1.f;
+    };
+    if constexpr (NP == 2) {
+      if (ts == t0) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_state_rows<DK, NI, NH, NH>(init, p.q, row_base, rg, c, Dv, S, valid);
+        // wait for everything but these loads: the first pass's loop then reads
+        // no register with a load in flight, and the compiler does not drain the
+        // memory counter (the second pass's loads with it) at its entry
+        constexpr int kB = NH * V4;
+        static_assert(kB < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_s_waitcnt((kB & 15) | (7 << 4) | (15 << 8) | ((kB >> 4) << 14));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    walk(std::integral_constant<int, 0>());
+    if constexpr (NP == 2) walk(std::integral_constant<int, 1>());
     __syncthreads();   // the next group's staging overwrites the staged tokens
   };
   if (t1 > t0) group(t0);
   for (int ts = t0 + kStageTokens; ts < t1; ts += kStageTokens) group(ts);
+  if constexpr (NP == 2) {
+    // no tokens: the second half is loaded only here, for the final state
+    if (t1 == t0) load_state_rows<DK, NI, NH, NH>(init, p.q, row_base, rg, c, Dv, S, valid);
+  }
   if constexpr (REPLAY) {
     if (t1 == t0) store_replayed();                // no tokens: the replayed state as it is
   }
@@ -913,6 +948,7 @@ __device__ __forceinline__ void recurrent_body_staged(const RecurrentArgs& p, in
     for (int i = 0; i < NI; ++i) {
       if (!valid[i]) continue;
       const int row = row_base + i * RI + rg;
+      const float gam = gam_p[i / NH];
 #pragma unroll
       for (int j = 0; j < V4; ++j) {
         float4_t x = {gam * S[i][4 * j + 0], gam * S[i][4 * j + 1], gam * S[i][4 * j + 2],
