@@ -48,26 +48,26 @@ BANK_TARGET_BYTES = 512 * 2 ** 20
 # sources: a changed kernel reports null until its counters are taken again.
 MEASURED_TRAFFIC = {
     "batched_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e01ac215981079b8", "fetch_kib": 66930.5, "write_kib": 131601.8,
-        "bytes": 271809452},
+        "sha256_16": "90c96b595bdee1ba", "fetch_kib": 66933.0, "write_kib": 131598.7,
+        "bytes": 271811346},
     "decode_effective_dense": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e01ac215981079b8", "fetch_kib": 66926.1, "write_kib": 131595.1,
-        "bytes": 271793571},
+        "sha256_16": "90c96b595bdee1ba", "fetch_kib": 66928.6, "write_kib": 131592.9,
+        "bytes": 271796440},
     "decode_kmajor": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_kmajor.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "5002d5fb8d5d6360", "fetch_kib": 66936.1, "write_kib": 131593.5,
         "bytes": 271812403},
     "spec_verify_replay": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "4b6383eea84265db", "fetch_kib": 51122.8, "write_kib": 52117.5,
-        "bytes": 158049191},
+        "sha256_16": "9d6f7262a47c98f6", "fetch_kib": 51133.3, "write_kib": 52119.2,
+        "bytes": 158072430},
     "spec_step_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e01ac215981079b8", "fetch_kib": 26530.9, "write_kib": 52098.0,
-        "bytes": 107673887},
+        "sha256_16": "90c96b595bdee1ba", "fetch_kib": 26530.9, "write_kib": 52096.4,
+        "bytes": 107672220},
     "spec_step_pooled": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "4b6383eea84265db", "fetch_kib": 51125.3, "write_kib": 52114.6,
-        "bytes": 158051278},
+        "sha256_16": "9d6f7262a47c98f6", "fetch_kib": 51135.8, "write_kib": 52119.9,
+        "bytes": 158078237},
     "spec_step_pooled_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_replay.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "4b6383eea84265db", "fetch_kib": 26532.9, "write_kib": 52093.2,
-        "bytes": 107673069},
+        "sha256_16": "9d6f7262a47c98f6", "fetch_kib": 26532.9, "write_kib": 52092.6,
+        "bytes": 107672440},
     "ragged_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_chunk.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "8a28ff8159b58b10", "fetch_kib": 258792.7, "write_kib": 240761.7,
         "bytes": 776452826},
@@ -81,8 +81,8 @@ MEASURED_TRAFFIC = {
         "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
         "bytes": 14950330},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "e01ac215981079b8", "fetch_kib": 69409.1, "write_kib": 137757.2,
-        "bytes": 283187923},
+        "sha256_16": "90c96b595bdee1ba", "fetch_kib": 69403.1, "write_kib": 137757.6,
+        "bytes": 283176033},
 }
 
 
@@ -253,12 +253,22 @@ def run_decode_kmajor(args, torch, gdn):
                          "algorithmic_bytes_per_step": nbytes}}
 
 
-def _time_steps(torch, step, steps, warmup):
-    """Average ms per step of `step(i)` over `steps` calls, HIP events on the launch stream."""
+def _time_steps(torch, step, steps, warmup, min_warm_s=0.0):
+    """Average ms per step of `step(i)` over `steps` calls, HIP events on the launch stream.
+    With min_warm_s, the untimed warmup goes on (in batches of `warmup` calls) until it
+    has run at least that long: after lighter work the GPU's clocks take tens of
+    milliseconds to settle, longer than a few calls of a short workload."""
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        for i in range(warmup):
+            step(done + i)
+        done += warmup
+        torch.cuda.synchronize()
+        if warmup <= 0 or time.perf_counter() - t0 >= min_warm_s:
+            break
+    warmup = done
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
@@ -553,10 +563,11 @@ def run_prefill(args, torch, gdn, name):
         gdn.gdn_forward(q, k, v, a, b, A_log, dt_bias, cu, out, initial_state=init, final_state=fin,
                         cu_seqlens_host=host_cu, workspace=ws)
 
-    steps = max(5, args.steps // 25)
+    # timed after at least 0.2 s of the same calls, over enough calls for 20 ms or more
+    steps = max(20, args.steps // 5)
     warm = max(2, args.warmup // 10)
     _log(f"{name}: N={N} R={R} Hv={Hv} plan={'chunk' if plan == gdn.PLAN_CHUNK else 'recurrent'} steps={steps}")
-    ms = _time_steps(torch, step, steps, warm)
+    ms = _time_steps(torch, step, steps, warm, min_warm_s=0.2)
     per_call = _per_call(torch, step, 10, warm + steps)
     flops = prefill_flops(inp["lengths"], Hk, Hv, Dk)
     flops_wy3 = prefill_flops_wy3(inp["lengths"], Hk, Hv, Dk)
@@ -630,17 +641,23 @@ def run_conv(args, torch, gdn, name):
     state_bytes = R * C * (K - 1) * 4
     nbytes = conv_bytes(N, R, C, K, 2)
     if name == "conv_prefill":
-        init = _dev(inp["initial_state"], torch)
-        fin = torch.empty_like(init)
+        # x and the output are 251 MB each: with one copy, part of x is still in the
+        # 256 MB Infinity Cache from the call before (76 against 92 us per call), so
+        # the calls rotate over three copies of x, output and states
+        banks = 3
+        sets = [(x if j == 0 else x.clone(), out if j == 0 else torch.empty_like(x),
+                 _dev(inp["initial_state"], torch), torch.empty_like(_dev(inp["initial_state"], torch)))
+                for j in range(banks)]
 
         def step(i):
-            gdn.gdn_conv_forward(x, w, bias, cu, out, initial_state=init, final_state=fin,
+            xs, outs, init, fin = sets[i % banks]
+            gdn.gdn_conv_forward(xs, w, bias, cu, outs, initial_state=init, final_state=fin,
                                  cu_seqlens_host=host_cu)
 
         _log(f"{name}: N={N} R={R} C={C} K={K}")
-        ms = _time_steps(torch, step, max(20, args.steps // 5), max(5, args.warmup // 5))
-        timing = "HIP events around consecutive calls"
-        banks = 1
+        ms = _time_steps(torch, step, max(20, args.steps // 5), max(5, args.warmup // 5), min_warm_s=0.2)
+        timing = ("HIP events around consecutive calls, after at least 0.2 s of the same calls; "
+                  "x, output and states rotate over three copies")
     else:
         banks = max(2, -(-BANK_TARGET_BYTES // state_bytes))
         states = [_dev(inp["initial_state"], torch) for _ in range(banks)]
