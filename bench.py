@@ -75,11 +75,11 @@ MEASURED_TRAFFIC = {
         "sha256_16": "8a28ff8159b58b10", "fetch_kib": 669508.5, "write_kib": 715781.8,
         "bytes": 2103869140},
     "conv_prefill": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 130733.7, "write_kib": 246423.5,
-        "bytes": 520032609},
+        "sha256_16": "8efa3ae12fc932a2", "fetch_kib": 124275.1, "write_kib": 246403.3,
+        "bytes": 506786802},
     "conv_decode": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_conv.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
-        "sha256_16": "6bc37e884b8911c5", "fetch_kib": 3716.6, "write_kib": 7168.0,
-        "bytes": 14950330},
+        "sha256_16": "8efa3ae12fc932a2", "fetch_kib": 3712.1, "write_kib": 7168.0,
+        "bytes": 14941110},
     "conv_decode_fused": {"sources": ['gateddeltanet_recurrence_amd/csrc/gdn_recurrent.hip', 'gateddeltanet_recurrence_amd/csrc/gdn_common.h', 'gateddeltanet_recurrence_amd/csrc/gdn_kernels.h'],
         "sha256_16": "90c96b595bdee1ba", "fetch_kib": 69403.1, "write_kib": 137757.6,
         "bytes": 283176033},

@@ -28,7 +28,12 @@ namespace {
 
 constexpr int kConvThreads = kConvBlockThreads;
 constexpr int kConvChannelsPerBlock = 4 * kConvThreads;
-constexpr int kConvUnroll = 8;
+// Tokens whose inputs a thread loads before using any (the loop's unroll): one
+// round for a whole block of up to kConvUnrollLong tokens, so that a thread keeps
+// all of its loads in flight at once (ragged prefill, 15 tokens per block: 92 ->
+// 88 us against two rounds of 8); blocks of a few tokens (decode) take the short
+// loop, which issues fewer redundant loads past their last token.
+constexpr int kConvUnrollLong = 16, kConvUnrollShort = 4;
 
 // The output is a stream written once: nontemporal stores (ragged prefill
 // 103 -> 83..90 us). Nontemporal loads of x were slower: a block re-reads the K - 1
@@ -187,7 +192,7 @@ __device__ __forceinline__ T* state_of(T* s, int slot, int C, int c, int K) {
 // rather than one column slice of many rows, and the workgroup that continues a
 // channel group's tokens runs on the same XCD as the one before it, whose rows
 // its window re-reads.
-template <typename IO, int K>
+template <typename IO, int K, int U>
 __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
   const int groups = (p.C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock;
   const int c = 4 * ((int)(blockIdx.x % groups) * kConvThreads + threadIdx.x);
@@ -224,17 +229,17 @@ __global__ void __launch_bounds__(kConvThreads) gdn_conv_forward_k(ConvArgs p) {
       window_at<IO, K>(x, p.C, c, start, 0, state_ref(p.initial_state, state_slot(p.initial_slots, r, p.num_slots), p.C, c, K), win);
     }
     const int stop = min(t_end, max(end, t + 1));           // this request's tokens here
-    // kConvUnroll tokens' inputs are loaded before any of them is used, so a
-    // thread keeps several loads in flight instead of waiting on each in turn
-    for (; t < stop; t += kConvUnroll) {
+    // U tokens' inputs are loaded before any of them is used, so a thread keeps
+    // several loads in flight instead of waiting on each in turn
+    for (; t < stop; t += U) {
       // loads past `stop` repeat the last token's row (in bounds, unused), so
       // none of them waits behind a branch
-      float4_t xs[kConvUnroll];
+      float4_t xs[U];
 #pragma unroll
-      for (int u = 0; u < kConvUnroll; ++u)
+      for (int u = 0; u < U; ++u)
         xs[u] = Io4<IO>::load(x + (size_t)min(t + u, stop - 1) * p.C + c);
 #pragma unroll
-      for (int u = 0; u < kConvUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         if (t + u >= stop) break;
         const float xv[4] = {xs[u].x, xs[u].y, xs[u].z, xs[u].w};
         float y[4];
@@ -308,7 +313,12 @@ hipError_t launch_conv_k(const ConvArgs& p, hipStream_t stream) {
   const unsigned groups = (unsigned)conv_channel_groups(p.C);
   if (p.N > 0) {
     const unsigned blocks = (unsigned)((p.N + p.tokens_per_block - 1) / p.tokens_per_block);
-    hipLaunchKernelGGL((gdn_conv_forward_k<IO, K>), dim3(blocks * groups), dim3(kConvThreads), 0, stream, p);
+    if (p.tokens_per_block > kConvUnrollShort)
+      hipLaunchKernelGGL((gdn_conv_forward_k<IO, K, kConvUnrollLong>), dim3(blocks * groups), dim3(kConvThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((gdn_conv_forward_k<IO, K, kConvUnrollShort>), dim3(blocks * groups), dim3(kConvThreads), 0,
+                         stream, p);
   }
   if (p.final_state != nullptr && p.final_pending)
     hipLaunchKernelGGL((gdn_conv_final_k<IO, K>), dim3((unsigned)p.R * groups), dim3(kConvThreads), 0,
