@@ -1,7 +1,8 @@
 """GPU parity of the verify kernel (gdn_capsule: capsule capture, fp16 I/O,
 Dk = Dv = 128, V-major) against the float64 oracle, called through the C ABI,
 on what the speculative verify workload does not reach: segments longer than
-one staged group of tokens, final states (in place too), no initial state with
+one staged group of tokens, final states (in place too; an empty request's
+comes back bit for bit), no initial state with
 every update rule, capture counts past either end of [0, capacity], state rows
 over a wide range of magnitudes, and heads with fewer value rows (Dv = 16, 32)
 than one wave holds.
@@ -58,6 +59,11 @@ def test_verify_several_passes_with_final_state(in_place):
     ref_o, ref_s, ref_cap = oracle_forward(inp, O, capacity=cap, poison=-7.0)
     assert_parity("f16", res["output"], ref_o, res["final_state"], ref_s, "verify passes")
     _check_capsule(res["state_update"], ref_cap, inp, lengths)
+    for r, L in enumerate(lengths):
+        # no tokens: every row of the initial state comes back bit for bit (the rows
+        # a wave's second pass holds are loaded on this path only)
+        if L == 0:
+            assert np.array_equal(res["final_state"][r], np.asarray(inp["initial_state"])[r]), r
 
 
 def test_verify_zero_initial_state_and_rules():
